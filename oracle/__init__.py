@@ -1,0 +1,234 @@
+"""CPU oracle for the routed MoE layer with decoupled top-k1/k2 weights.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU
+library never imports, links or executes anything here, and this package
+never touches the GPU library.
+
+What it computes (``oracle.c`` holds the arithmetic):
+
+* router logits  l = x . Wr^T (+ br)  -- "Paper of the Week #3 - Half the
+  FLOPs Is Not Half the Time", section "Ship It - Code of the Week" (the
+  router method's linear layer);
+* fp32 softmax, ranking, and the weights of Eq. 2 of the same page, section
+  "The Receipt": w_i = p_i / sum_{j in Top-k2} p_j for i in Top-k1, with
+  k2 >= E meaning no division (the router method's ``k2 >= num_experts``
+  branch);
+* the activated experts as gated MLPs whose channels own a gate row, an up row
+  and a down column -- "Channel Selection for Mixture-of-Experts Decoding Needs
+  No Calibration Data", section 2 "Background" -- with silu on the gate, and
+  their weighted sum.
+
+Readings taken where the pages are silent (each is pinned by a test):
+
+1. softmax: m = max l; d = fl(l - m); e = exp_spec(d) (Cody-Waite reduction,
+   degree-7 Taylor, 0 below -80); S = pairwise sum of e zero-padded to a power
+   of two; p = fl(e / S);
+2. ranking is on probabilities, highest first, lower expert index first on
+   equal probability;
+3. the top-k2 mass is summed sequentially in rank order;
+4. k2 >= E gives w = p exactly; k2 > E is clamped to E;
+5. k1 <= k2 (k1 == k2 allowed); k1 > k2 is an argument error;
+6. weights stay fp32 (the logits are fp32);
+7. experts and combine are accumulated in fp64, rounded to fp32 once.
+
+The route functions (``softmax``, ``route``) are exact fp32 definitions; the
+expert functions are accumulated in fp64.  Arrays are numpy; bf16 tensors are
+passed as ``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "oracle.c"
+LIB = HERE / "liboracle.so"
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(verbose: bool = False, src: Path = SRC, out: Path = LIB) -> Path:
+    """Compile ``oracle.c`` with gcc (no fast-math, no FP contraction)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off",
+        "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+        str(src), "-o", str(out) + ".tmp", "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(str(out) + ".tmp", out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB.exists():
+        build()
+    _lib = _open(LIB)
+    return _lib
+
+
+def _open(path):
+    lib = ctypes.CDLL(str(path))
+    P = ctypes.c_void_p
+    i64, i32, cint = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.oracle_abi_version.restype = cint
+    lib.oracle_exp_spec.restype = ctypes.c_float
+    lib.oracle_exp_spec.argtypes = [ctypes.c_float]
+    lib.oracle_exp_spec_n.restype = None
+    lib.oracle_exp_spec_n.argtypes = [P, P, i64]
+    lib.oracle_softmax.restype = cint
+    lib.oracle_softmax.argtypes = [P, i64, i32, P]
+    lib.oracle_route.restype = cint
+    lib.oracle_route.argtypes = [P, i64, i32, i32, i32, P, P]
+    lib.oracle_logits.restype = cint
+    lib.oracle_logits.argtypes = [P, cint, i64, i32, P, P, i32, P, cint]
+    lib.oracle_experts.restype = cint
+    lib.oracle_experts.argtypes = [P, cint, i64, i32, P, P, P, cint, i32, i32,
+                                   i32, P, P, P, cint]
+    lib.oracle_forward.restype = cint
+    lib.oracle_forward.argtypes = [P, cint, i64, i32, P, P, i32, P, P, P, cint,
+                                   i32, i32, i32, P, P, P, P, cint]
+    return lib
+
+
+class using_library:
+    """Context manager that points this module at another build of the oracle
+    source (the mutation tests build copies with planted mistakes)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = _open(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what} failed with status {rc}")
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported dtype {a.dtype} (float32, or uint16 bf16 bits)")
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return a
+
+
+def exp_spec(d):
+    """exp_spec elementwise over a float32 array (d <= 0)."""
+    lib = _load()
+    d = _c(np.asarray(d, dtype=np.float32))
+    out = np.empty_like(d)
+    lib.oracle_exp_spec_n(_ptr(d), _ptr(out), d.size)
+    return out
+
+
+def softmax(logits):
+    lib = _load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    p = np.empty_like(logits)
+    _check(lib.oracle_softmax(_ptr(logits), T, E, _ptr(p)), "oracle_softmax")
+    return p
+
+
+def route(logits, k1: int, k2: int):
+    """(ids [T,k1] int32, w [T,k1] float32) in rank order."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k1), np.int32)
+    w = np.empty((T, k1), np.float32)
+    _check(lib.oracle_route(_ptr(logits), T, E, k1, k2, _ptr(ids), _ptr(w)),
+           "oracle_route")
+    return ids, w
+
+
+def logits(x, Wr, br=None, nthreads: int = 1):
+    lib = _load()
+    x = _c(x)
+    Wr = _c(Wr, np.float32)
+    br = None if br is None else _c(br, np.float32)
+    T, H = x.shape
+    E = Wr.shape[0]
+    out = np.empty((T, E), np.float32)
+    _check(lib.oracle_logits(_ptr(x), _dtype_code(x), T, H, _ptr(Wr), _ptr(br),
+                             E, _ptr(out), nthreads), "oracle_logits")
+    return out
+
+
+def experts(x, Wg, Wu, Wd, ids, w, nthreads: int = 1):
+    """y [T,H] float32 = sum_r w[t,r] * SwiGLU_{ids[t,r]}(x[t])."""
+    lib = _load()
+    x = _c(x)
+    Wg, Wu, Wd = _c(Wg), _c(Wu), _c(Wd)
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    T, H = x.shape
+    E, I, H2 = Wg.shape
+    assert H2 == H and Wu.shape == Wg.shape and Wd.shape == (E, H, I)
+    wt = _dtype_code(Wg)
+    assert _dtype_code(Wu) == wt and _dtype_code(Wd) == wt
+    k1 = ids.shape[1]
+    y = np.empty((T, H), np.float32)
+    _check(lib.oracle_experts(_ptr(x), _dtype_code(x), T, H, _ptr(Wg), _ptr(Wu),
+                              _ptr(Wd), wt, E, I, k1, _ptr(ids), _ptr(w), _ptr(y),
+                              nthreads), "oracle_experts")
+    return y
+
+
+def forward(x, Wr, Wg, Wu, Wd, k1: int, k2: int, br=None, nthreads: int = 1):
+    """Whole layer: returns (y, logits, ids, w)."""
+    lib = _load()
+    x = _c(x)
+    Wr = _c(Wr, np.float32)
+    br = None if br is None else _c(br, np.float32)
+    Wg, Wu, Wd = _c(Wg), _c(Wu), _c(Wd)
+    T, H = x.shape
+    E, I, _ = Wg.shape
+    wt = _dtype_code(Wg)
+    y = np.empty((T, H), np.float32)
+    lg = np.empty((T, E), np.float32)
+    ids = np.empty((T, k1), np.int32)
+    w = np.empty((T, k1), np.float32)
+    _check(lib.oracle_forward(_ptr(x), _dtype_code(x), T, H, _ptr(Wr), _ptr(br),
+                              E, _ptr(Wg), _ptr(Wu), _ptr(Wd), wt, I, k1, k2,
+                              _ptr(y), _ptr(lg), _ptr(ids), _ptr(w), nthreads),
+           "oracle_forward")
+    return y, lg, ids, w
