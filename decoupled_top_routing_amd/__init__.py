@@ -1,1 +1,173 @@
-"""placeholder"""
+"""Routed MoE layer with decoupled top-k1/k2 weights on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmoe.so`` (declared in
+``include/moe.h``).  Every step of the layer runs in the library's HIP
+kernels; this module only checks tensors, allocates outputs and workspace with
+torch, and passes pointers and the current stream.  There is no CPU fallback:
+if the library is missing or cannot be loaded, every call raises.
+
+The method: "Paper of the Week #3 - Half the FLOPs Is Not Half the Time",
+section "The Receipt", Eq. 2 -- activate the top-k1 experts, each weighted by
+its probability over the probability mass of the top-k2 experts (k2 = k1:
+standard renormalisation; k2 >= E: none).
+"""
+from __future__ import annotations
+
+import ctypes
+import threading
+from pathlib import Path
+
+import torch
+
+__all__ = ["route", "forward", "MoeError", "library_path", "load_library",
+           "F32", "BF16", "FORCE_DECODE", "FORCE_PREFILL"]
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libmoe.so"
+
+F32, BF16 = 0, 1
+FORCE_DECODE, FORCE_PREFILL = 1, 2
+ABI_VERSION = 1
+
+_STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_EWORKSPACE",
+           4: "MOE_ENOTSUP", 5: "MOE_EHIP"}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def library_path() -> Path:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libmoe.so (once); raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not LIB_PATH.exists():
+            raise MoeError(-1, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+        lib.moe_abi_version.restype = ctypes.c_int
+        lib.moe_status_str.restype = ctypes.c_char_p
+        lib.moe_status_str.argtypes = [ctypes.c_int]
+        lib.moe_last_error_str.restype = ctypes.c_char_p
+        lib.moe_route.restype = ctypes.c_int
+        lib.moe_route.argtypes = [P, i64, i32, i32, i32, P, P, P]
+        lib.moe_forward_workspace.restype = ctypes.c_size_t
+        lib.moe_forward_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
+                                    i32, P, P, P, P, u32, P, ctypes.c_size_t, P]
+        if lib.moe_abi_version() != ABI_VERSION:
+            raise MoeError(-1, f"libmoe ABI {lib.moe_abi_version()} != {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load_library()
+        raise MoeError(rc, lib.moe_last_error_str().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeError(1, f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise MoeError(1, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(4, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise MoeError(4, f"unsupported dtype {t.dtype}")
+
+
+def route(logits: torch.Tensor, k1: int, k2: int):
+    """ids [T,k1] int32 and Eq. 2 weights [T,k1] fp32 from fp32 logits [T,E]."""
+    lib = load_library()
+    _need_cuda("logits", logits, torch.float32)
+    T, E = logits.shape
+    ids = torch.empty((T, k1), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k1), dtype=torch.float32, device=logits.device)
+    _check(lib.moe_route(_ptr(logits), T, E, k1, k2, _ptr(ids), _ptr(w),
+                         _stream(logits.device)))
+    return ids, w
+
+
+# One zero-filled workspace per (device, stream), grown on demand.  The
+# library leaves its synchronisation words at zero after every call.
+_workspaces: dict = {}
+
+
+def _workspace(device, stream_ptr: int, nbytes: int) -> torch.Tensor:
+    key = (device, stream_ptr)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
+            return_route: bool = False, flags: int = 0, out=None):
+    """The whole routed MoE layer.
+
+    x [T,H] (fp32 or bf16), Wr [E,H] fp32, br [E] fp32 or None, Wgate and Wup
+    [E,I,H], Wdown [E,H,I] in the dtype of x.  Returns y [T,H] in x's dtype,
+    or (y, logits, ids, w) with ``return_route=True``.
+    """
+    lib = load_library()
+    _need_cuda("x", x)
+    act = _dtype_code(x)
+    _need_cuda("Wr", Wr, torch.float32)
+    for n, t in (("Wgate", Wgate), ("Wup", Wup), ("Wdown", Wdown)):
+        _need_cuda(n, t, x.dtype)
+    if br is not None:
+        _need_cuda("br", br, torch.float32)
+    T, H = x.shape
+    E, I, H2 = Wgate.shape
+    if H2 != H or Wup.shape != Wgate.shape or tuple(Wdown.shape) != (E, H, I) \
+            or tuple(Wr.shape) != (E, H):
+        raise MoeError(1, "shape mismatch between x, Wr, Wgate, Wup and Wdown")
+    dev = x.device
+    y = out if out is not None else torch.empty((T, H), dtype=x.dtype, device=dev)
+    lg = ids = w = None
+    if return_route:
+        lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k1), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k1), dtype=torch.float32, device=dev)
+    nbytes = lib.moe_forward_workspace(T, H, E, I, k1, act, act)
+    if nbytes == 0 and T > 0:
+        raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
+    stream = _stream(dev)
+    ws = _workspace(dev, stream.value or 0, nbytes)
+    _check(lib.moe_forward(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
+                           _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(y), _ptr(lg),
+                           _ptr(ids), _ptr(w), flags, _ptr(ws), ws.numel(), stream))
+    if return_route:
+        return y, lg, ids, w
+    return y

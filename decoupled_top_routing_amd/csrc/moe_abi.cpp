@@ -1,0 +1,185 @@
+// C ABI of libmoe.so: argument checks, workspace layout and dispatch.
+// The declarations and the contract of each entry point are in include/moe.h.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MOE_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace layout of moe_forward (each segment 256-byte aligned).
+struct Layout {
+  size_t logits, ids, w, plan, abuf, total;
+};
+
+Layout layout(int64_t T, int32_t E, int32_t I, int32_t k1) {
+  Layout L;
+  size_t o = 0;
+  const size_t n_assign = (size_t)T * (size_t)k1;
+  L.logits = o;
+  o += round256((size_t)T * E * 4);
+  L.ids = o;
+  o += round256(n_assign * 4);
+  L.w = o;
+  o += round256(n_assign * 4);
+  L.plan = o;
+  o += round256((4 + (size_t)E + (size_t)E + 1 + n_assign) * 4);
+  L.abuf = o;
+  o += round256(n_assign * (size_t)I * 4);
+  L.total = o;
+  return L;
+}
+
+// Largest T accepted: keeps every element index of every tensor well inside
+// int64 and every grid dimension inside its hardware limit.
+constexpr int64_t kMaxT = int64_t(1) << 24;
+
+int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
+  if (T < 0 || T > kMaxT) return fail(MOE_EINVAL, "T=%lld out of [0, %lld]", (long long)T, (long long)kMaxT);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "E=%d out of [1, %d]", E, MOE_MAX_EXPERTS);
+  if (k1 < 1 || k1 > E) return fail(MOE_EINVAL, "k1=%d out of [1, E=%d]", k1, E);
+  if (k2 < k1) return fail(MOE_EINVAL, "k2=%d < k1=%d", k2, k1);
+  return MOE_OK;
+}
+
+template <typename WT, typename XT>
+int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const float *br, int32_t E,
+                  const WT *Wg, const WT *Wu, const WT *Wd, int32_t I, int32_t k1, int32_t k2,
+                  XT *y, float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
+                  char *ws, const Layout &L, hipStream_t s) {
+  (void)flags;
+  float *logits = reinterpret_cast<float *>(ws + L.logits);
+  int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
+  float *w = reinterpret_cast<float *>(ws + L.w);
+  int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  float *abuf = reinterpret_cast<float *>(ws + L.abuf);
+  const int64_t n_assign = T * k1;
+  hipError_t e;
+  if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) != hipSuccess)
+    return hip_fail(e, "router kernel");
+  if ((e = moe::launch_route(logits, T, E, k1, k2, ids, w, ids_out, w_out, s)) != hipSuccess)
+    return hip_fail(e, "route kernel");
+  if ((e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
+    return hip_fail(e, "plan kernel");
+  if ((e = moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)) !=
+      hipSuccess)
+    return hip_fail(e, "gate/up kernel");
+  if ((e = moe::launch_down<WT, XT>(Wd, T, H, I, ids, k1, abuf, y, s)) != hipSuccess)
+    return hip_fail(e, "down kernel");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EALIGN: return "misaligned pointer";
+    case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ENOTSUP: return "unsupported dtype combination";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error_str(void) { return g_err; }
+
+int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1, int32_t k2, int32_t *ids,
+              float *weights, void *stream) {
+  int rc = check_route_args(T, E, k1, k2);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !weights) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
+    return fail(MOE_EALIGN, "logits, ids and weights need 4-byte alignment");
+  hipError_t e = moe::launch_route(logits, T, E, k1, k2, ids, weights, nullptr, nullptr,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "route kernel");
+  return MOE_OK;
+}
+
+size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1,
+                             int32_t act_dtype, int32_t w_dtype) {
+  (void)act_dtype;
+  (void)w_dtype;
+  if (T < 0 || T > kMaxT || E < 1 || E > MOE_MAX_EXPERTS || k1 < 1 || k1 > E || H < 8 ||
+      I < 8)
+    return 0;
+  return layout(T, E, I, k1).total;
+}
+
+int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const float *Wr,
+                const float *br, int32_t E, const void *Wgate, const void *Wup,
+                const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
+                float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_route_args(T, E, k1, k2);
+  if (rc != MOE_OK) return rc;
+  if (H < 8 || H % 8 != 0) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 8", H);
+  if (I < 8 || I % 8 != 0) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 8", I);
+  if ((int64_t)H * I > (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
+  if (flags & ~(MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_PREFILL))
+    return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & MOE_FLAG_FORCE_DECODE) && (flags & MOE_FLAG_FORCE_PREFILL))
+    return fail(MOE_EINVAL, "both path flags set");
+  const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
+  const bool b16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
+  if (!f32 && !b16)
+    return fail(MOE_ENOTSUP, "dtype pair (act=%d, w=%d) not supported", act_dtype, w_dtype);
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !Wgate || !Wup || !Wdown || !y) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wgate, 16) || !aligned(Wup, 16) ||
+      !aligned(Wdown, 16) || !aligned(y, 16))
+    return fail(MOE_EALIGN, "x, Wr, Wgate, Wup, Wdown and y need 16-byte alignment");
+  if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
+      (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
+    return fail(MOE_EALIGN, "br and the route outputs need 4-byte alignment");
+  const Layout L = layout(T, E, I, k1);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
+                L.total, workspace_bytes, workspace);
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = static_cast<char *>(workspace);
+  if (f32)
+    return forward_typed<float, float>(
+        static_cast<const float *>(x), T, H, Wr, br, E, static_cast<const float *>(Wgate),
+        static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2,
+        static_cast<float *>(y), logits_out, ids_out, w_out, flags, ws, L, s);
+  return forward_typed<moe::bf16_t, moe::bf16_t>(
+      static_cast<const moe::bf16_t *>(x), T, H, Wr, br, E,
+      static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
+      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, static_cast<moe::bf16_t *>(y),
+      logits_out, ids_out, w_out, flags, ws, L, s);
+}
+
+}  // extern "C"

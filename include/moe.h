@@ -1,0 +1,145 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the routed Mixture-of-Experts layer of a
+ * fine-grained MoE at inference, with decoupled top-k1/k2 weights, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Paper of the Week #3 - Half the FLOPs Is Not Half the Time",
+ * section "The Receipt", Eq. 2): a token runs its k1 most probable experts and
+ * weights each by its probability divided by the probability mass of its k2
+ * most probable experts,
+ *
+ *     w_i = p_i / sum_{j in Top-k2} p_j      for i in Top-k1,
+ *
+ * so k2 = k1 is standard top-k renormalisation and k2 = E is none.  The
+ * router method of the same page (section "Ship It - Code of the Week")
+ * computes the probabilities in fp32 from a linear router and keeps
+ * min(k2, E) candidates.  An expert is a gated MLP whose channel c owns one
+ * gate row, one up row and one down column ("Channel Selection for
+ * Mixture-of-Experts Decoding Needs No Calibration Data", section 2
+ * "Background"); the activation is silu on the gate times the up projection.
+ *
+ * Numerical contract of the route (softmax, ranking, Eq. 2), fp32 throughout:
+ *   m = max_e l_e;  d_e = l_e - m;  e_e = exp(d_e) evaluated as
+ *   2^n * P7(r) with n = rint(d * log2 e), r = d - n ln2 (Cody & Waite's
+ *   two-constant reduction) and P7 the degree-7 Taylor polynomial by Horner
+ *   with fused multiply-adds, and e_e = 0 for d_e < -80;
+ *   S = pairwise sum of e over the next power of two (zero padded);
+ *   p_e = e_e / S (IEEE division);  ranking by p descending, lower index
+ *   first on equal p;  M = sum of the first min(k2,E) ranked p, left to right;
+ *   w_r = p_r / M, or w_r = p_r when k2 >= E.
+ * Given identical logits the ids and weights are reproducible bit for bit.
+ *
+ * Conventions for every entry point:
+ *  - all tensors are row-major and contiguous, in device memory of the
+ *    current HIP device, owned by the caller; the library keeps no pointer
+ *    after returning and allocates no device memory;
+ *  - `stream` is a hipStream_t (NULL = the null stream); all work is enqueued
+ *    on it with no host synchronisation; outputs are overwritten;
+ *  - argument errors are returned before anything is launched; a failed launch
+ *    returns MOE_EHIP (text in moe_last_error_str()); device faults surface at
+ *    the caller's next synchronisation, as usual for HIP;
+ *  - logits must be finite (a precondition: with a non-finite logit the
+ *    outputs for that token are unspecified);
+ *  - entry points never throw and are safe to call from several host threads.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,     /* a size or k argument out of range, or a NULL pointer */
+    MOE_EALIGN = 2,     /* a pointer without the required alignment */
+    MOE_EWORKSPACE = 3, /* workspace NULL, misaligned or too small */
+    MOE_ENOTSUP = 4,    /* unsupported dtype combination */
+    MOE_EHIP = 5        /* a HIP runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* moe_forward flags: force one of the two expert paths (testing); 0 = choose
+ * by batch size. */
+#define MOE_FLAG_FORCE_DECODE 1u
+#define MOE_FLAG_FORCE_PREFILL 2u
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char *moe_status_str(int status);
+
+/* Text of the last MOE_EHIP / argument error on the calling thread. */
+const char *moe_last_error_str(void);
+
+/*
+ * moe_route -- softmax, ranking and Eq. 2 weights from given router logits
+ * (the router method of "Paper of the Week #3", section "Ship It - Code of
+ * the Week", from the softmax on; weights per Eq. 2 of section "The Receipt").
+ *
+ *   logits  [T, E] fp32, finite.                   4-byte aligned
+ *   ids     [T, k1] int32 out: expert indices in rank order
+ *   weights [T, k1] fp32 out: Eq. 2 weights in the same order
+ *   1 <= E <= 1024;  1 <= k1 <= E;  k2 >= k1 (k2 > E behaves as k2 = E).
+ *   T = 0 returns MOE_OK and launches nothing.
+ */
+int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1,
+              int32_t k2, int32_t *ids, float *weights, void *stream);
+
+/*
+ * moe_forward_workspace -- bytes of device workspace moe_forward needs for
+ * these sizes (a multiple of 256).  0 for invalid sizes.
+ */
+size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
+                             int32_t k1, int32_t act_dtype, int32_t w_dtype);
+
+/*
+ * moe_forward -- the whole routed MoE layer: router logits, route (as
+ * moe_route), the activated experts and their weighted sum,
+ *
+ *   y[t] = sum_{r<k1} w[t,r] * Wdown[e] (silu(Wgate[e] x[t]) * (Wup[e] x[t])),
+ *   e = ids[t,r],  logits[t] = Wr x[t] (+ br).
+ *
+ *   x      [T, H]    act_dtype (MOE_F32 or MOE_BF16)          16-byte aligned
+ *   Wr     [E, H]    fp32 router weight                       16-byte aligned
+ *   br     [E]       fp32 router bias, or NULL                 4-byte aligned
+ *   Wgate  [E, I, H] w_dtype: row c of expert e = gate row of channel c
+ *   Wup    [E, I, H] w_dtype: row c of expert e = up row of channel c
+ *   Wdown  [E, H, I] w_dtype: column c of expert e = down column of channel c
+ *                                                   (all three 16-byte aligned)
+ *   y      [T, H]    act_dtype out                            16-byte aligned
+ *   logits_out [T,E] fp32, ids_out [T,k1] int32, w_out [T,k1] fp32: optional
+ *          copies of the route (NULL to skip), 4-byte aligned
+ *   workspace: device memory of at least moe_forward_workspace(...) bytes,
+ *          256-byte aligned, ZERO-FILLED before its first use; the library
+ *          leaves its synchronisation words at zero after every call, so one
+ *          zero fill at allocation lasts for the workspace's lifetime.  Calls
+ *          that run concurrently need separate workspaces.
+ *   flags: 0, MOE_FLAG_FORCE_DECODE or MOE_FLAG_FORCE_PREFILL.
+ *
+ *   Supported dtype pairs (act, w): (F32, F32) and (BF16, BF16); accumulation
+ *   is fp32.  1 <= E <= 1024; H and I multiples of 8; 1 <= k1 <= E;
+ *   k2 >= k1.  T = 0 returns MOE_OK and launches nothing.
+ *   Identical inputs give bitwise identical logits, ids, weights and y.
+ */
+int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
+                const float *Wr, const float *br, int32_t E,
+                const void *Wgate, const void *Wup, const void *Wdown,
+                int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
+                float *logits_out, int32_t *ids_out, float *w_out,
+                uint32_t flags, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

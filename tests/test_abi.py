@@ -1,0 +1,106 @@
+"""The C ABI library loads and exports what include/moe.h declares, and its
+argument checks return before anything is launched (no GPU needed)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import decoupled_top_routing_amd as moe
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "moe.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_forward", "moe_forward_workspace", "moe_abi_version",
+              "moe_status_str", "moe_last_error_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+    assert lib.moe_abi_version() == moe.ABI_VERSION
+
+
+def test_status_strings():
+    lib = moe.load_library()
+    for code in range(6):
+        assert lib.moe_status_str(code)
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+def test_workspace_size():
+    lib = moe.load_library()
+    n1 = lib.moe_forward_workspace(1, 2048, 128, 768, 4, 1, 1)
+    n8 = lib.moe_forward_workspace(8, 2048, 128, 768, 4, 1, 1)
+    assert n1 > 0 and n1 % 256 == 0 and n8 > n1
+    assert lib.moe_forward_workspace(1, 2048, 2000, 768, 4, 1, 1) == 0  # E > 1024
+    assert lib.moe_forward_workspace(1, 2048, 128, 768, 0, 1, 1) == 0  # k1 = 0
+
+
+def _route(lib, T, E, k1, k2, ptr=8):
+    p = ctypes.c_void_p(ptr)
+    return lib.moe_route(p, T, E, k1, k2, p, p, None)
+
+
+@pytest.mark.parametrize("T,E,k1,k2,code", [
+    (1, 0, 1, 1, 1),          # E < 1
+    (1, 1025, 1, 1, 1),       # E > 1024
+    (1, 16, 0, 4, 1),         # k1 < 1
+    (1, 16, 17, 17, 1),       # k1 > E
+    (1, 16, 4, 3, 1),         # k2 < k1
+    (-1, 16, 2, 4, 1),        # T < 0
+])
+def test_route_rejects_bad_arguments(T, E, k1, k2, code):
+    lib = moe.load_library()
+    assert _route(lib, T, E, k1, k2) == code
+    assert lib.moe_last_error_str()
+
+
+def test_route_zero_tokens_is_a_no_op():
+    lib = moe.load_library()
+    assert _route(lib, 0, 16, 2, 4) == 0
+
+
+def test_route_null_and_misaligned_pointers():
+    lib = moe.load_library()
+    assert lib.moe_route(None, 1, 16, 2, 4, None, None, None) == 1
+    assert _route(lib, 1, 16, 2, 4, ptr=6) == 2
+
+
+def _fwd(lib, **kw):
+    a = dict(x=16, act=1, T=1, H=2048, Wr=16, br=None, E=128, Wg=16, Wu=16, Wd=16, wt=1,
+             I=768, k1=4, k2=16, y=16, lo=None, io=None, wo=None, flags=0, ws=256,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.moe_forward(v(a["x"]), a["act"], a["T"], a["H"], v(a["Wr"]), v(a["br"]),
+                           a["E"], v(a["Wg"]), v(a["Wu"]), v(a["Wd"]), a["wt"], a["I"],
+                           a["k1"], a["k2"], v(a["y"]), v(a["lo"]), v(a["io"]), v(a["wo"]),
+                           a["flags"], v(a["ws"]), a["wsb"], v(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k2=3), 1), (dict(H=100), 1), (dict(I=4), 1), (dict(E=2048), 1),
+    (dict(act=0, wt=1), 4), (dict(act=1, wt=0), 4), (dict(act=2, wt=2), 4),
+    (dict(x=24), 2), (dict(Wd=8), 2), (dict(br=2), 2),
+    (dict(ws=None), 3), (dict(ws=128), 3), (dict(wsb=1024), 3),
+    (dict(x=None), 1), (dict(flags=3), 1), (dict(flags=8), 1),
+])
+def test_forward_rejects_bad_arguments(kw, code):
+    lib = moe.load_library()
+    assert _fwd(lib, **kw) == code, lib.moe_last_error_str()
+
+
+def test_forward_zero_tokens_is_a_no_op():
+    lib = moe.load_library()
+    assert _fwd(lib, T=0, x=None, y=None, ws=None, wsb=0) == 0

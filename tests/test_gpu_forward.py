@@ -1,0 +1,132 @@
+"""moe_forward on the GPU against the CPU oracle.
+
+For each workload: (i) the GPU's logits match the oracle's within 1e-5
+normwise; (ii) the oracle's route on the GPU's own logits equals the GPU's ids
+and weights bit for bit; (iii) y matches the oracle's experts and combine on
+that route within the tolerance of the dtype; (iv) an independent oracle run
+from x picks the same experts except on near-ties, which are counted, not
+failed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decoupled_top_routing_amd as moe
+import oracle
+from decoupled_top_routing_amd import synth
+from parity import (TOL_BF16, TOL_F32, check_route_exact, host_layer, near_tie_tokens,
+                    normwise_err, to_f64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(L):
+    return {k: (None if v is None else v.to(DEV)) for k, v in L.items()}
+
+
+def run_and_check(cfg, L, Lh, k1, k2, flags=0, token_sample=None, tol=None):
+    g = to_dev(L) if L["Wg"].device.type == "cpu" else L
+    print(f"{cfg.name} T={g['x'].shape[0]} k1={k1} k2={k2} flags={flags}", flush=True)
+    y, lg, ids, w = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], k1, k2,
+                                br=g["br"], return_route=True, flags=flags)
+    torch.cuda.synchronize()
+    lg_h = lg.cpu().numpy()
+    T = lg_h.shape[0]
+    sel = np.arange(T) if token_sample is None else np.asarray(token_sample)
+    x_h = Lh["x"][sel]
+    # (i) logits
+    ref_l = oracle.logits(x_h, Lh["Wr"], Lh["br"], nthreads=8)
+    assert normwise_err(lg_h[sel], ref_l) <= 1e-5
+    # (ii) route on the GPU logits, all tokens
+    oids, ow = check_route_exact(ids, w, lg_h, k1, k2, f"{cfg.name} ({k1},{k2})")
+    # (iii) experts and combine on that route
+    y_ref = oracle.experts(x_h, Lh["Wg"], Lh["Wu"], Lh["Wd"], oids[sel], ow[sel], nthreads=8)
+    err = normwise_err(to_f64(y)[sel], y_ref)
+    tol = tol if tol is not None else (TOL_F32 if cfg.dtype == "f32" else TOL_BF16)
+    assert err <= tol, f"normwise error {err} > {tol}"
+    # (iv) independent route from the oracle's own logits
+    iids, _ = oracle.route(ref_l, k1, k2)
+    ties = near_tie_tokens(oracle.softmax(ref_l), k1)
+    differ = (np.sort(iids, 1) != np.sort(oids[sel], 1)).any(1)
+    assert not (differ & ~ties).any(), "experts differ away from a near-tie"
+    return y, err
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    L = synth.make_layer(synth.TINY)
+    return L, host_layer(L)
+
+
+@pytest.mark.parametrize("k1,k2", synth.TINY.k_pairs)
+@pytest.mark.parametrize("flags", [0, moe.FORCE_DECODE])
+def test_tiny_fp32(tiny, k1, k2, flags):
+    L, Lh = tiny
+    run_and_check(synth.TINY, L, Lh, k1, k2, flags)
+
+
+@pytest.fixture(scope="module")
+def a3b():
+    L = synth.make_layer(synth.DECODE_B8)
+    return L, host_layer(L)
+
+
+@pytest.mark.parametrize("k1,k2", synth.DECODE_B1.k_pairs)
+@pytest.mark.parametrize("T", [1, 8])
+def test_a3b_decode(a3b, k1, k2, T):
+    L, Lh = a3b
+    Lt = dict(L, x=L["x"][:T])
+    Lht = dict(Lh, x=Lh["x"][:T])
+    cfg = synth.DECODE_B1 if T == 1 else synth.DECODE_B8
+    run_and_check(cfg, Lt, Lht, k1, k2)
+
+
+def test_a3b_ragged_batches(a3b):
+    L, Lh = a3b
+    for T in (2, 3, 5, 7):
+        Lt = dict(L, x=L["x"][:T])
+        run_and_check(synth.DECODE_B8, Lt, dict(Lh, x=Lh["x"][:T]), 4, 16)
+
+
+def test_a3b_ids_do_not_depend_on_k2(a3b):
+    """P1, The Receipt: k2 changes the weights, never the experts."""
+    L, _ = a3b
+    g = to_dev(L)
+    ref = None
+    for k2 in (4, 8, 16, 64, 128):
+        _, _, ids, _ = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], 4, k2,
+                                   return_route=True)
+        if ref is None:
+            ref = ids
+        assert torch.equal(ids, ref)
+
+
+def test_forward_is_deterministic(a3b):
+    L, _ = a3b
+    g = to_dev(L)
+    a = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], 4, 16, return_route=True)
+    b = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], 4, 16, return_route=True)
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+def test_zero_tokens(a3b):
+    L, _ = a3b
+    g = to_dev(L)
+    y = moe.forward(g["x"][:0], g["Wr"], g["Wg"], g["Wu"], g["Wd"], 4, 16)
+    assert y.shape == (0, synth.DECODE_B1.H)
+
+
+@pytest.mark.parametrize("E,k1,k2,H,I,T", [
+    (1, 1, 1, 8, 8, 3),        # one expert, smallest sizes
+    (8, 8, 8, 64, 16, 5),      # every expert active: the dense mixture
+    (16, 3, 40, 136, 24, 17),  # k2 > E, ragged sizes
+    (1024, 2, 7, 64, 8, 9),    # the most experts
+])
+def test_edge_shapes_fp32(E, k1, k2, H, I, T):
+    from dataclasses import replace
+    cfg = replace(synth.TINY, name=f"edge-E{E}", T=T, H=H, E=E, I=I)
+    L = synth.make_layer(cfg)
+    run_and_check(cfg, L, host_layer(L), k1, k2)
