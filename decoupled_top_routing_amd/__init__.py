@@ -133,12 +133,15 @@ def _workspace(device, stream_ptr: int, nbytes: int) -> torch.Tensor:
 
 
 def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
-            return_route: bool = False, flags: int = 0, out=None):
+            return_route: bool = False, flags: int = 0, out=None, workspace=None):
     """The whole routed MoE layer.
 
     x [T,H] (fp32 or bf16), Wr [E,H] fp32, br [E] fp32 or None, Wgate and Wup
     [E,I,H], Wdown [E,H,I] in the dtype of x.  Returns y [T,H] in x's dtype,
-    or (y, logits, ids, w) with ``return_route=True``.
+    or (y, logits, ids, w) with ``return_route=True``.  ``out`` receives y if
+    given; ``workspace`` is an optional zero-filled uint8 device tensor of at
+    least ``moe_forward_workspace`` bytes (needed under graph capture, where
+    nothing may be allocated).
     """
     lib = load_library()
     _need_cuda("x", x)
@@ -164,7 +167,11 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
     if nbytes == 0 and T > 0:
         raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
     stream = _stream(dev)
-    ws = _workspace(dev, stream.value or 0, nbytes)
+    if workspace is not None:
+        _need_cuda("workspace", workspace, torch.uint8)
+        ws = workspace
+    else:
+        ws = _workspace(dev, stream.value or 0, nbytes)
     _check(lib.moe_forward(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
                            _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(y), _ptr(lg),
                            _ptr(ids), _ptr(w), flags, _ptr(ws), ws.numel(), stream))

@@ -98,4 +98,68 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs (v_dot2_f32_bf16):
+// the bf16 products are exact in fp32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------- DPP
+// Wave-wide reductions with DPP lane moves (no LDS round trip).  The order
+// is fixed: pairs (xor 1), quads (xor 2), half rows, rows of 16, then rows
+// 0+1 and 2+3, then the two halves; the result is read from lane 63.  For
+// a sum this is the pairwise tree over the 64 lanes.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // row_half_mirror
+constexpr int kMirror = 0x140;     // row_mirror
+constexpr int kBcast15 = 0x142;    // row_bcast:15
+constexpr int kBcast31 = 0x143;    // row_bcast:31
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t mov(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+}  // namespace dpp
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  using namespace dpp;
+  auto step = [](float a, uint32_t b) { return a + __uint_as_float(b); };
+  const uint32_t z = 0u;  // +0.0f
+  v = step(v, mov<kXor1>(z, __float_as_uint(v)));
+  v = step(v, mov<kXor2>(z, __float_as_uint(v)));
+  v = step(v, mov<kHalfMirror>(z, __float_as_uint(v)));
+  v = step(v, mov<kMirror>(z, __float_as_uint(v)));
+  v = step(v, mov<kBcast15, 0xA>(z, __float_as_uint(v)));
+  v = step(v, mov<kBcast31, 0xC>(z, __float_as_uint(v)));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  using namespace dpp;
+  const uint32_t ninf = 0xFF800000u;
+  v = fmaxf(v, __uint_as_float(mov<kXor1>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(mov<kXor2>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(mov<kHalfMirror>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(mov<kMirror>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(mov<kBcast15, 0xA>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(mov<kBcast31, 0xC>(ninf, __float_as_uint(v))));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  using namespace dpp;
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, mov<kXor1>(0u, v));
+  v = mx(v, mov<kXor2>(0u, v));
+  v = mx(v, mov<kHalfMirror>(0u, v));
+  v = mx(v, mov<kMirror>(0u, v));
+  v = mx(v, mov<kBcast15, 0xA>(0u, v));
+  v = mx(v, mov<kBcast31, 0xC>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 }  // namespace moe

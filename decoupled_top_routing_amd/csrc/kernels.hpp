@@ -10,6 +10,25 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 
+// Every workspace starts with a fixed 16 KiB region of synchronisation words
+// (an epoch word, then counters that are zero whenever no call is running).
+// Its size and place do not depend on the call's shapes, so one workspace can
+// serve calls of different shapes.
+constexpr size_t kSyncRegionBytes = 16384;
+
+// Byte offsets of the fused decode kernel's buffers in the workspace.
+struct DecodeLayout {
+  size_t sync, logits, abuf, total;
+};
+size_t fused_decode_workspace(int64_t T, int H, int E, int I, int k1, DecodeLayout *L);
+bool fused_decode_supported(int64_t T, int H, int E, int I, int k1, bool bf16);
+
+template <typename WT, typename XT>
+hipError_t launch_fused_decode(const XT *x, int64_t T, int H, const float *Wr, const float *br,
+                               int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
+                               int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+                               char *ws, hipStream_t s);
+
 hipError_t launch_route(const float *logits, int64_t T, int E, int k1, int k2, int32_t *ids,
                         float *w, int32_t *ids2, float *w2, hipStream_t s);
 

@@ -38,7 +38,7 @@ struct Layout {
 
 Layout layout(int64_t T, int32_t E, int32_t I, int32_t k1) {
   Layout L;
-  size_t o = 0;
+  size_t o = moe::kSyncRegionBytes;  // reserved: sync words of the fused path
   const size_t n_assign = (size_t)T * (size_t)k1;
   L.logits = o;
   o += round256((size_t)T * E * 4);
@@ -66,19 +66,39 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
   return MOE_OK;
 }
 
+// Small batches whose shapes the fused decode kernel covers take it (one
+// launch per layer); everything else takes the multi-kernel path.
+bool use_fused(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf16,
+               uint32_t flags) {
+  if (flags & MOE_FLAG_FORCE_PREFILL) return false;
+  return moe::fused_decode_supported(T, H, E, I, k1, bf16);
+}
+
+size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
+  moe::DecodeLayout D;
+  const size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
+  const size_t b = layout(T, E, I, k1).total;
+  return a > b ? a : b;
+}
+
 template <typename WT, typename XT>
 int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const float *br, int32_t E,
                   const WT *Wg, const WT *Wu, const WT *Wd, int32_t I, int32_t k1, int32_t k2,
                   XT *y, float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
                   char *ws, const Layout &L, hipStream_t s) {
-  (void)flags;
+  hipError_t e;
+  if (use_fused(T, H, E, I, k1, sizeof(WT) == 2, flags)) {
+    if ((e = moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
+                                              logits_out, ids_out, w_out, ws, s)) != hipSuccess)
+      return hip_fail(e, "fused decode kernel");
+    return MOE_OK;
+  }
   float *logits = reinterpret_cast<float *>(ws + L.logits);
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
   float *w = reinterpret_cast<float *>(ws + L.w);
   int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
   float *abuf = reinterpret_cast<float *>(ws + L.abuf);
   const int64_t n_assign = T * k1;
-  hipError_t e;
   if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) != hipSuccess)
     return hip_fail(e, "router kernel");
   if ((e = moe::launch_route(logits, T, E, k1, k2, ids, w, ids_out, w_out, s)) != hipSuccess)
@@ -134,7 +154,7 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   if (T < 0 || T > kMaxT || E < 1 || E > MOE_MAX_EXPERTS || k1 < 1 || k1 > E || H < 8 ||
       I < 8)
     return 0;
-  return layout(T, E, I, k1).total;
+  return workspace_bytes_for(T, H, E, I, k1);
 }
 
 int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const float *Wr,
@@ -165,9 +185,10 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
       (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
     return fail(MOE_EALIGN, "br and the route outputs need 4-byte alignment");
   const Layout L = layout(T, E, I, k1);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+  const size_t need = workspace_bytes_for(T, H, E, I, k1);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
-                L.total, workspace_bytes, workspace);
+                need, workspace_bytes, workspace);
   hipStream_t s = (hipStream_t)stream;
   char *ws = static_cast<char *>(workspace);
   if (f32)

@@ -1,0 +1,171 @@
+// Device-side route of one token: fp32 softmax with a specified exp, ranking
+// and the Eq. 2 weights ("Paper of the Week #3 - Half the FLOPs Is Not Half
+// the Time", section "The Receipt", Eq. 2; section "Ship It - Code of the
+// Week").  Used by the route kernel and by the fused decode kernel.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+namespace expc {
+// Constants of the exp below, derived from ln 2 at compile time.
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+__host__ __device__ constexpr uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__host__ __device__ constexpr float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+// log2(e) rounded to float
+constexpr float kLog2e = (float)(1.0 / kLn2);
+// ln 2 rounded to float with its 8 low significand bits cleared (16
+// significant bits, so n * hi is exact for |n| < 256) and the rounded rest.
+constexpr float kLn2Hi = bitsf(fbits((float)kLn2) & 0xFFFFFF00u);
+constexpr float kLn2Lo = (float)(kLn2 - (double)kLn2Hi);
+// 1/k!, k = 0..7, rounded to float
+constexpr float kC0 = 1.0f, kC1 = 1.0f, kC2 = (float)(1.0 / 2.0), kC3 = (float)(1.0 / 6.0),
+                kC4 = (float)(1.0 / 24.0), kC5 = (float)(1.0 / 120.0),
+                kC6 = (float)(1.0 / 720.0), kC7 = (float)(1.0 / 5040.0);
+}  // namespace expc
+
+// e^d for d <= 0 by Cody & Waite's reduction (Software Manual for the
+// Elementary Functions, 1980): n = rint(d log2 e), r = d - n ln2 with ln2
+// split in two parts, e^d = 2^n e^r, e^r by its degree-7 Taylor polynomial
+// in Horner form with fused multiply-adds.  Zero below -80, so every nonzero
+// result is a normal float.
+__device__ __forceinline__ float exp_nonpos(float d) {
+#pragma clang fp contract(off)
+  using namespace expc;
+  if (d < -80.0f) return 0.0f;
+  float t = d * kLog2e;
+  float n = __builtin_rintf(t);
+  float r = __builtin_fmaf(-n, kLn2Hi, d);
+  r = __builtin_fmaf(-n, kLn2Lo, r);
+  float q = kC7;
+  q = __builtin_fmaf(q, r, kC6);
+  q = __builtin_fmaf(q, r, kC5);
+  q = __builtin_fmaf(q, r, kC4);
+  q = __builtin_fmaf(q, r, kC3);
+  q = __builtin_fmaf(q, r, kC2);
+  q = __builtin_fmaf(q, r, kC1);
+  q = __builtin_fmaf(q, r, kC0);
+  return __builtin_ldexpf(q, (int)n);
+}
+
+// Route one token with the calling wavefront.  V = values per lane, with
+// 64 * V >= E; lane L holds experts [L*V, L*V + V) ("blocked" layout, so a
+// lower lane always holds lower indices).
+//
+//  1. m = max of the logits (exact);
+//  2. e = exp_nonpos(l - m), 0 for the padding;
+//  3. S = pairwise sum of e over 64*V slots: a lane-local adjacent-pair tree,
+//     then the pairwise tree over lanes (wave_sum_dpp).  fp32 addition is
+//     commutative, so the lane order inside a node does not matter, and zero
+//     padding of a power-of-two tree leaves its sum unchanged: S equals the
+//     pairwise sum over the next power of two >= E;
+//  4. p = e / S (IEEE division);
+//  5. R rounds of selection: each lane offers its best untaken expert (key =
+//     bits of p + 1, larger p first, lower index first within the lane), the
+//     wave takes the maximum key, and the lowest lane holding it wins; this
+//     ranks by p descending, then index ascending.  R = min(k2, E), or k1 when
+//     k2 >= E (no mass needed);
+//  6. M = p_(0) + p_(1) + ... left to right over the min(k2, E) ranked values;
+//     w_r = p_(r) / M, or p_(r) when k2 >= E.
+// Rank r is held by lane r % 64 in slot r / 64 until the end.
+// COHERENT: read the logits with device-coherent loads (they were written by
+// other workgroups of the same kernel).  ids and w may point to LDS.
+template <int V, bool COHERENT = false>
+__device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
+                            int32_t *__restrict__ ids, float *__restrict__ w,
+                            int32_t *__restrict__ ids2, float *__restrict__ w2) {
+#pragma clang fp contract(off)
+  const int lane = lane_id();
+  float ex[V];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane * V + j;
+    float lv = -INFINITY;
+    if (e < E)
+      lv = COHERENT ? __hip_atomic_load(const_cast<float *>(l + e), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT)
+                    : l[e];
+    ex[j] = lv;
+    lmax = fmaxf(lmax, ex[j]);
+  }
+  const float m = wave_max_dpp(lmax);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane * V + j;
+    ex[j] = e < E ? exp_nonpos(ex[j] - m) : 0.0f;
+  }
+  float s[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) s[j] = ex[j];
+#pragma unroll
+  for (int step = 1; step < V; step <<= 1) {
+#pragma unroll
+    for (int j = 0; j + step < V; j += 2 * step) s[j] = s[j] + s[j + step];
+  }
+  // the DPP sum is the pairwise tree over the 64 lanes (see wave_sum_dpp)
+  const float S = wave_sum_dpp(s[0]);
+
+  uint32_t key[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane * V + j;
+    key[j] = e < E ? __float_as_uint(ex[j] / S) + 1u : 0u;
+  }
+
+  const bool renorm = k2 < E;
+  const int R = renorm ? k2 : k1;
+  float M = 0.0f;
+  int32_t my_id[V];
+  float my_p[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    my_id[q] = 0;
+    my_p[q] = 0.0f;
+  }
+  for (int r = 0; r < R; ++r) {
+    uint32_t best = 0u;
+    int bj = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (key[j] > best) {
+        best = key[j];
+        bj = j;
+      }
+    }
+    const uint32_t kmax = wave_max_u32_dpp(best);
+    const uint64_t mask = __ballot(best == kmax);
+    const int win = __ffsll((unsigned long long)mask) - 1;
+    if (lane == win) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (j == bj) key[j] = 0u;
+    }
+    const int id = __builtin_amdgcn_readlane(lane * V + bj, win);
+    const float pr = __uint_as_float(kmax - 1u);
+    if (renorm) M = M + pr;
+    if (r < k1 && lane == (r & (kWave - 1))) {
+      const int q = r / kWave;
+#pragma unroll
+      for (int qq = 0; qq < V; ++qq)
+        if (qq == q) {
+          my_id[qq] = id;
+          my_p[qq] = pr;
+        }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    const int r = q * kWave + lane;
+    if (r < k1) {
+      const float wr = renorm ? my_p[q] / M : my_p[q];
+      ids[r] = my_id[q];
+      w[r] = wr;
+      if (ids2) ids2[r] = my_id[q];
+      if (w2) w2[r] = wr;
+    }
+  }
+}
+
+}  // namespace moe

@@ -59,8 +59,11 @@ def tiny():
     return L, host_layer(L)
 
 
+PATHS = [0, moe.FORCE_DECODE, moe.FORCE_PREFILL]
+
+
 @pytest.mark.parametrize("k1,k2", synth.TINY.k_pairs)
-@pytest.mark.parametrize("flags", [0, moe.FORCE_DECODE])
+@pytest.mark.parametrize("flags", PATHS)
 def test_tiny_fp32(tiny, k1, k2, flags):
     L, Lh = tiny
     run_and_check(synth.TINY, L, Lh, k1, k2, flags)
@@ -80,6 +83,39 @@ def test_a3b_decode(a3b, k1, k2, T):
     Lht = dict(Lh, x=Lh["x"][:T])
     cfg = synth.DECODE_B1 if T == 1 else synth.DECODE_B8
     run_and_check(cfg, Lt, Lht, k1, k2)
+
+
+@pytest.mark.parametrize("flags", [moe.FORCE_PREFILL])
+@pytest.mark.parametrize("k1,k2", [(8, 8), (4, 16)])
+def test_a3b_decode_general_path(a3b, k1, k2, flags):
+    L, Lh = a3b
+    run_and_check(synth.DECODE_B8, L, Lh, k1, k2, flags)
+
+
+def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
+    """One workspace serves calls of different shapes and paths in a row; the
+    synchronisation words must be back at zero after every call."""
+    L, Lh = a3b
+    tL, tLh = tiny
+    g, tg = to_dev(L), to_dev(tL)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    ref = {}
+    for rep in range(3):
+        for name, (lay, T, k1, k2, fl) in {
+                "a": (g, 1, 4, 16, 0), "b": (tg, 8, 2, 4, 0), "c": (g, 8, 8, 8, 0),
+                "d": (g, 5, 3, 16, moe.FORCE_PREFILL), "e": (tg, 3, 2, 16, 0)}.items():
+            y = moe.forward(lay["x"][:T], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
+                            br=lay["br"], flags=fl, workspace=ws)
+            torch.cuda.synchronize()
+            words = ws[:16384].view(torch.int32).cpu()
+            # word 0 is the workspace's epoch; every counter and the error
+            # word must be back at zero
+            assert int(words[1:].abs().sum()) == 0, f"sync words left set ({name})"
+            yb = y.float().cpu()
+            if rep == 0:
+                ref[name] = yb
+            else:
+                assert torch.equal(ref[name], yb), name
 
 
 def test_a3b_ragged_batches(a3b):
@@ -124,6 +160,10 @@ def test_zero_tokens(a3b):
     (8, 8, 8, 64, 16, 5),      # every expert active: the dense mixture
     (16, 3, 40, 136, 24, 17),  # k2 > E, ragged sizes
     (1024, 2, 7, 64, 8, 9),    # the most experts
+    (16, 2, 4, 256, 64, 64),   # the largest batch on the fused decode path
+    (16, 2, 4, 256, 64, 65),   # the smallest batch past it
+    (512, 10, 20, 512, 136, 40),  # many unique experts, down rows of 34 chunks
+    (33, 5, 9, 1024, 64, 13),  # router rows of 4 chunks per lane
 ])
 def test_edge_shapes_fp32(E, k1, k2, H, I, T):
     from dataclasses import replace
