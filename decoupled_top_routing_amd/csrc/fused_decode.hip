@@ -56,7 +56,7 @@ constexpr int kPF = 6;            // down rows prefetched for this many experts
 constexpr int kRPW = 1;           // down rows per wave
 constexpr int kRB = kWaves * kRPW;
 constexpr int kSub = 32;          // sub-counters of the done count
-constexpr int kStage = 3072;      // a values staged in LDS per round (floats)
+constexpr int kStage = 2048;      // a values staged in LDS per round (floats)
 // Published words are written to several copies spread over memory channels
 // (copy stride = a multiple of 4 KiB plus 1280 B), and each consumer block
 // reads the copy of its index, so that hundreds of blocks do not poll the
@@ -123,6 +123,52 @@ __device__ __forceinline__ float await_tagged(const uint64_t *p, uint32_t tag, i
   return __uint_as_float((uint32_t)w);
 }
 
+// Stage n tagged words into dst[0..n) (LDS; dst[0..2n) with two bf16 values
+// per word when PACKED), n <= MAXW * kThreads: each
+// thread first issues the loads of all its words, then re-reads only those
+// that do not carry `tag` yet, so the wait costs one round trip, not one per
+// word.  Ends with a block barrier.
+template <int MAXW, bool PACKED = false, typename AddrFn>
+__device__ void stage_tagged(float *dst, int n, AddrFn addr, uint32_t tag, int32_t *err) {
+  uint64_t w[MAXW];
+  const uint64_t done = (uint64_t)tag << 32;
+#pragma unroll
+  for (int k = 0; k < MAXW; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    w[k] = i < n ? coh_ld(addr(i)) : done;
+  }
+  uint32_t spins = 0;
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) ok &= (uint32_t)(w[k] >> 32) == tag;
+    if (ok) break;
+    if (++spins > kSpinLimit) {
+      coh_st(err, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < n && (uint32_t)(w[k] >> 32) != tag) w[k] = coh_ld(addr(i));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXW; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < n) {
+      if constexpr (PACKED) {
+        dst[2 * i] = bf16_lo((uint32_t)w[k]);
+        dst[2 * i + 1] = bf16_hi((uint32_t)w[k]);
+      } else {
+        dst[i] = __uint_as_float((uint32_t)w[k]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Thread 0 adds 1 to *ctr once the whole block is here; the old value is
 // returned to every thread of the block.
 __device__ int block_count(int32_t *ctr, int *s_old) {
@@ -165,6 +211,15 @@ __device__ void router_block(const Args &a, int rb, uint32_t tag) {
 // The route of every token and the unique experts of the batch, in LDS:
 // uniq[u] ascending, list[off[u] .. off[u+1]) = assignments (t*k1 + r) routed
 // to uniq[u], ascending.  Built identically by every block.
+struct BlockRoute {
+  uint64_t K[kThreads];
+  int32_t rank[kThreads];
+  float sp[kThreads];
+  int32_t sid[kThreads];
+  float red[kWaves];
+  float M;
+};
+
 struct Plan {
   float logits[kMaxLogits];
   int32_t ids[kMaxAssign];
@@ -175,10 +230,100 @@ struct Plan {
   uint32_t bits[kMaxExperts / 32];
   int32_t pre[kMaxExperts / 32];
   int32_t U;
+  BlockRoute br;
 };
 
 __device__ __forceinline__ int uidx_of(const Plan &P, int e) {
   return P.pre[e >> 5] + __popc(P.bits[e >> 5] & ((1u << (e & 31)) - 1u));
+}
+
+// One token (E <= 256) routed by the whole block, with the arithmetic of
+// route_token: exact max; e = exp_nonpos(l - max); S = the pairwise tree
+// (each wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
+// (p descending, index ascending) counted in parallel (element e by
+// 256 / next_pow2(E) threads, each over a slice of the keys); the mass summed
+// in rank order by one thread; w = p / M or p.
+
+__device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
+                                  int32_t *ids_out, float *w_out, BlockRoute &S) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const bool valid = tid < E;
+  const float lv = valid ? l[tid] : -INFINITY;
+  const float wm = wave_max_dpp(lv);
+  if (lane == 0) S.red[wv] = wm;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]));
+  const float ex = valid ? exp_nonpos(lv - m) : 0.0f;
+  const float ws = wave_sum_dpp(ex);
+  __syncthreads();
+  if (lane == 0) S.red[wv] = ws;
+  __syncthreads();
+  const float sum = (S.red[0] + S.red[1]) + (S.red[2] + S.red[3]);
+  const float p = ex / sum;
+  const uint32_t key = valid ? __float_as_uint(p) + 1u : 0u;
+  S.K[tid] = ((uint64_t)key << 11) | (uint64_t)(2047 - tid);
+  S.rank[tid] = 0;
+  __syncthreads();
+  int epow = 1, lg = 0;
+  while (epow < E) {
+    epow <<= 1;
+    ++lg;
+  }
+  const int split = kThreads / epow;
+  const int e = tid & (epow - 1), part = tid >> lg;
+  const int chunk = epow / split;
+  if (e < E) {
+    const uint64_t Ke = S.K[e];
+    const int j0 = part * chunk, j1 = min(E, j0 + chunk);
+    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    int j = j0;
+    for (; j + 4 <= j1; j += 4) {
+      c0 += S.K[j] > Ke ? 1 : 0;
+      c1 += S.K[j + 1] > Ke ? 1 : 0;
+      c2 += S.K[j + 2] > Ke ? 1 : 0;
+      c3 += S.K[j + 3] > Ke ? 1 : 0;
+    }
+    for (; j < j1; ++j) c0 += S.K[j] > Ke ? 1 : 0;
+    const int cnt = (c0 + c1) + (c2 + c3);
+    if (cnt) atomicAdd(&S.rank[e], cnt);
+  }
+  __syncthreads();
+  const bool renorm = k2 < E;
+  const int R = renorm ? k2 : k1;
+  if (valid) {
+    const int r = S.rank[tid];
+    if (r < R) {
+      S.sp[r] = p;
+      S.sid[r] = tid;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // left to right in rank order; the loads run ahead of the adds
+    float M = 0.0f;
+    if (renorm) {
+      int r = 0;
+      for (; r + 8 <= R; r += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = S.sp[r + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) M = M + v[q];
+      }
+      for (; r < R; ++r) M = M + S.sp[r];
+    }
+    S.M = M;
+  }
+  __syncthreads();
+  if (tid < k1) {
+    const float wr = renorm ? S.sp[tid] / S.M : S.sp[tid];
+    ids[tid] = S.sid[tid];
+    w[tid] = wr;
+    if (ids_out) ids_out[tid] = S.sid[tid];
+    if (w_out) w_out[tid] = wr;
+  }
+  __syncthreads();
 }
 
 template <int V>
@@ -188,17 +333,52 @@ __device__ void build_plan(const Args &a, Plan &P, uint32_t tag, bool write_out)
   for (int i = threadIdx.x; i < nw; i += kThreads) P.bits[i] = 0u;
   // the router's logits, as soon as each one carries this call's tag
   const uint64_t *lg = a.logits + (blockIdx.x % kRepL) * a.rep_l;
-  for (int i = threadIdx.x; i < a.T * a.E; i += kThreads)
-    P.logits[i] = await_tagged(lg + i, tag, a.sync + kError);
-  __syncthreads();
-  const int wv = threadIdx.x >> 6;
-  for (int t = wv; t < a.T; t += kWaves) {
-    const int o = t * a.k1;
-    route_token<V>(P.logits + t * a.E, a.E, a.k1, a.k2, P.ids + o, P.w + o,
-                   write_out && a.ids_out ? a.ids_out + o : nullptr,
-                   write_out && a.w_out ? a.w_out + o : nullptr);
+  stage_tagged<kMaxLogits / kThreads>(P.logits, a.T * a.E, [&](int i) { return lg + i; }, tag,
+                                      a.sync + kError);
+  if (a.T == 1 && a.E <= kThreads && a.k1 <= kThreads) {
+    route_token_block(P.logits, a.E, a.k1, a.k2, P.ids, P.w, write_out ? a.ids_out : nullptr,
+                      write_out ? a.w_out : nullptr, P.br);
+  } else {
+    const int wv = threadIdx.x >> 6;
+    for (int t = wv; t < a.T; t += kWaves) {
+      const int o = t * a.k1;
+      route_token<V>(P.logits + t * a.E, a.E, a.k1, a.k2, P.ids + o, P.w + o,
+                     write_out && a.ids_out ? a.ids_out + o : nullptr,
+                     write_out && a.w_out ? a.w_out + o : nullptr);
+    }
+    __syncthreads();
   }
-  __syncthreads();
+  if (n <= kWave) {
+    // one wave builds the plan: lane i holds assignment i
+    if (threadIdx.x < kWave) {
+      const int i = threadIdx.x;
+      const int e = i < n ? P.ids[i] : 0x7FFFFFFF;
+      int cnt_less = 0, same_before = 0;
+      for (int j = 0; j < n; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        cnt_less += ej < e;
+        same_before += (ej == e) & (j < i);
+      }
+      const uint64_t first = __ballot(i < n && same_before == 0);
+      int uniq_less = 0;
+      for (int j = 0; j < n; ++j)
+        if ((first >> j) & 1ull) uniq_less += __builtin_amdgcn_readlane(e, j) < e;
+      if (i < n) {
+        if (same_before == 0) {
+          P.uniq[uniq_less] = e;
+          P.off[uniq_less] = cnt_less;
+        }
+        P.list[cnt_less + same_before] = i;
+      }
+      if (i == 0) {
+        const int U = __popcll(first);
+        P.U = U;
+        P.off[U] = n;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int e = P.ids[i];
     atomicOr(&P.bits[e >> 5], 1u << (e & 31));
@@ -277,6 +457,7 @@ __device__ void gateup_block(const Args &a, const Plan &P, int item, uint32_t ta
       uint4 xq[NCH];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) xq[j] = ld16(xr + (j * kWave + lane) * NW);
+      float av[CPW];
 #pragma unroll
       for (int ci = 0; ci < CPW; ++ci) {
         float ag = 0.0f, au = 0.0f;
@@ -291,11 +472,26 @@ __device__ void gateup_block(const Args &a, const Plan &P, int item, uint32_t ta
           au = dot2_bf16(uq[ci][j].z, xq[j].z, au);
           au = dot2_bf16(uq[ci][j].w, xq[j].w, au);
         }
-        ag = wave_sum_dpp(ag);
-        au = wave_sum_dpp(au);
-        const int c = c0 + ci;
-        if (lane < kRepA && c < a.I)
-          coh_st(a.abuf + lane * a.rep_a + (int64_t)asg * a.I + c, tagged(tag, silu(ag) * au * wt));
+        av[ci] = silu(wave_sum_dpp(ag)) * wave_sum_dpp(au) * wt;
+      }
+      if constexpr (CPW % 2 == 0) {
+        // two channels per word, as bf16 (the down projection reads bf16
+        // weights; a 2^-9 relative rounding of a)
+#pragma unroll
+        for (int ci = 0; ci < CPW; ci += 2) {
+          const int c = c0 + ci;
+          const uint64_t word = ((uint64_t)tag << 32) | (f32_to_bf16_bits(av[ci + 1]) << 16) |
+                                f32_to_bf16_bits(av[ci]);
+          if (lane < kRepA && c < a.I)
+            coh_st(a.abuf + lane * a.rep_a + ((int64_t)asg * a.I + c) / 2, word);
+        }
+      } else {
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+          const int c = c0 + ci;
+          if (lane < kRepA && c < a.I)
+            coh_st(a.abuf + lane * a.rep_a + (int64_t)asg * a.I + c, tagged(tag, av[ci]));
+        }
       }
     } else {
       float xv[NCH][NW];
@@ -330,7 +526,7 @@ __device__ void gateup_block(const Args &a, const Plan &P, int item, uint32_t ta
 // ------------------------------------------------------------- down
 // Each wave owns kRPW rows; lane L holds 16-byte chunks L and L+64 of a row
 // (NCD = 1 or 2 chunks per lane, I*sizeof(WT)/16 <= 128).
-template <typename WT, typename XT, int NCD>
+template <typename WT, typename XT, int NCD, bool PACKED>
 __device__ void down_block(const Args &a, const Plan &P, int hb, float *s_a, float *s_y,
                            uint32_t tag) {
   constexpr int NW = Elem<WT>::kPer16B;
@@ -353,18 +549,32 @@ __device__ void down_block(const Args &a, const Plan &P, int hb, float *s_a, flo
   for (int s = 0; s < kPF; ++s)
     if (s < U) issue(s, dq[s]);
   const uint64_t *ab = a.abuf + (blockIdx.x % kRepA) * a.rep_a;
-  const int per_round = kStage / a.I;  // I <= 1024, so at least 3
+  // assignments staged per round (I <= 1024)
+  const int per_round = (PACKED ? 2 * kStage : kStage) / a.I;
   for (int ub = 0; ub < U; ub += kPF) {
     const int ue = min(U, ub + kPF);
     const int g0 = P.off[ub], g1 = P.off[ue];
     for (int r0 = g0; r0 < g1; r0 += per_round) {
       const int r1 = min(g1, r0 + per_round);
       // stage the a vectors of assignments list[r0 .. r1) as they are published
-      for (int idx = threadIdx.x; idx < (r1 - r0) * a.I; idx += kThreads) {
-        const int i = r0 + idx / a.I, c = idx - (idx / a.I) * a.I;
-        s_a[idx] = await_tagged(ab + (int64_t)P.list[i] * a.I + c, tag, a.sync + kError);
+      if constexpr (PACKED) {
+        const int half = a.I / 2;
+        stage_tagged<kStage / kThreads, true>(
+            s_a, (r1 - r0) * half,
+            [&](int idx) {
+              const int i = r0 + idx / half, c2 = idx - (idx / half) * half;
+              return ab + ((int64_t)P.list[i] * a.I) / 2 + c2;
+            },
+            tag, a.sync + kError);
+      } else {
+        stage_tagged<kStage / kThreads>(
+            s_a, (r1 - r0) * a.I,
+            [&](int idx) {
+              const int i = r0 + idx / a.I, c = idx - (idx / a.I) * a.I;
+              return ab + (int64_t)P.list[i] * a.I + c;
+            },
+            tag, a.sync + kError);
       }
-      __syncthreads();
 #pragma unroll
       for (int s = 0; s < kPF; ++s) {
         const int u = ub + s;
@@ -407,7 +617,7 @@ __device__ void down_block(const Args &a, const Plan &P, int hb, float *s_a, flo
 template <typename WT, typename XT, int V, int NCHR, int NCH, int CPW, int NCD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fused_decode_kernel(Args a) {
   __shared__ Plan P;
-  __shared__ float s_a[kStage];
+  __shared__ float s_a[2 * kStage];
   __shared__ float s_y[kMaxTok * kRB];
   __shared__ int s_old;
   const int b = blockIdx.x;
@@ -424,7 +634,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   if (is_gu) {
     if (item / a.n_cb < P.U) gateup_block<WT, XT, NCH, CPW>(a, P, item, tag);
   } else {
-    down_block<WT, XT, NCD>(a, P, item, s_a, s_y, tag);
+    down_block<WT, XT, NCD, sizeof(WT) == 2 && CPW % 2 == 0>(a, P, item, s_a, s_y, tag);
   }
   // done count over the non-router blocks (kSub sub-counters, then the top);
   // the last one advances the epoch and clears the counters

@@ -61,11 +61,12 @@ __device__ __forceinline__ float exp_nonpos(float d) {
 //     padding of a power-of-two tree leaves its sum unchanged: S equals the
 //     pairwise sum over the next power of two >= E;
 //  4. p = e / S (IEEE division);
-//  5. R rounds of selection: each lane offers its best untaken expert (key =
-//     bits of p + 1, larger p first, lower index first within the lane), the
-//     wave takes the maximum key, and the lowest lane holding it wins; this
-//     ranks by p descending, then index ascending.  R = min(k2, E), or k1 when
-//     k2 >= E (no mass needed);
+//  5. ranking by (p descending, index ascending) with key = bits of p + 1
+//     (p >= 0, so the bits order like the values; padding has key 0): for
+//     E <= 256 every expert's rank is counted directly, otherwise R rounds
+//     take the largest remaining key (lowest lane, lowest slot on ties).
+//     Only the first R = min(k2, E) ranks are read (k1 when k2 >= E: no mass
+//     needed);
 //  6. M = p_(0) + p_(1) + ... left to right over the min(k2, E) ranked values;
 //     w_r = p_(r) / M, or p_(r) when k2 >= E.
 // Rank r is held by lane r % 64 in slot r / 64 until the end.
@@ -124,27 +125,7 @@ __device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
     my_id[q] = 0;
     my_p[q] = 0.0f;
   }
-  for (int r = 0; r < R; ++r) {
-    uint32_t best = 0u;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      if (key[j] > best) {
-        best = key[j];
-        bj = j;
-      }
-    }
-    const uint32_t kmax = wave_max_u32_dpp(best);
-    const uint64_t mask = __ballot(best == kmax);
-    const int win = __ffsll((unsigned long long)mask) - 1;
-    if (lane == win) {
-#pragma unroll
-      for (int j = 0; j < V; ++j)
-        if (j == bj) key[j] = 0u;
-    }
-    const int id = __builtin_amdgcn_readlane(lane * V + bj, win);
-    const float pr = __uint_as_float(kmax - 1u);
-    if (renorm) M = M + pr;
+  auto keep = [&](int r, int id, float pr) {
     if (r < k1 && lane == (r & (kWave - 1))) {
       const int q = r / kWave;
 #pragma unroll
@@ -153,6 +134,75 @@ __device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
           my_id[qq] = id;
           my_p[qq] = pr;
         }
+    }
+  };
+  if constexpr (V <= 4) {
+    // Rank of each expert = number of experts ahead of it in the order (p
+    // descending, index ascending); keys are distinct, so the ranks are a
+    // permutation.  Each lane counts against every key, broadcast with
+    // readlane: independent instructions instead of a chain of reductions.
+    // key and index packed so one unsigned compare orders by (p desc, index
+    // asc): padding (key 0) sorts after every expert (key >= 1)
+    uint64_t K[V];
+    int rank[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      K[j] = ((uint64_t)key[j] << 11) | (uint64_t)(2047 - (lane * V + j));
+      rank[j] = 0;
+    }
+#pragma unroll 4
+    for (int L = 0; L < kWave; ++L) {
+#pragma unroll
+      for (int s2 = 0; s2 < V; ++s2) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)K[s2], L);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(K[s2] >> 32), L);
+        const uint64_t kk = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+        for (int j = 0; j < V; ++j) rank[j] += kk > K[j] ? 1 : 0;
+      }
+    }
+    // walk the ranks in order: the lane holding rank r hands over its expert
+    for (int r = 0; r < R; ++r) {
+      int sid = -1;
+      uint32_t skey = 0u;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const bool m = rank[j] == r;
+        sid = m ? lane * V + j : sid;
+        skey = m ? key[j] : skey;
+      }
+      const uint64_t mask = __ballot(sid >= 0);
+      const int win = __ffsll((unsigned long long)mask) - 1;
+      const int id = __builtin_amdgcn_readlane(sid, win);
+      const float pr = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)skey, win) - 1u);
+      if (renorm) M = M + pr;
+      keep(r, id, pr);
+    }
+  } else {
+    // R rounds: each lane offers its best untaken expert, the wave takes the
+    // largest key, and the lowest lane holding it wins.
+    for (int r = 0; r < R; ++r) {
+      uint32_t best = 0u;
+      int bj = 0;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        if (key[j] > best) {
+          best = key[j];
+          bj = j;
+        }
+      }
+      const uint32_t kmax = wave_max_u32_dpp(best);
+      const uint64_t mask = __ballot(best == kmax);
+      const int win = __ffsll((unsigned long long)mask) - 1;
+      if (lane == win) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          if (j == bj) key[j] = 0u;
+      }
+      const int id = __builtin_amdgcn_readlane(lane * V + bj, win);
+      const float pr = __uint_as_float(kmax - 1u);
+      if (renorm) M = M + pr;
+      keep(r, id, pr);
     }
   }
 #pragma unroll
