@@ -53,7 +53,10 @@ def total_bytes(cfg, T, counted):
     return counted + cfg.E * cfg.H * 4 + 2 * T * cfg.H * elt
 
 
-def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup):
+PATH_FLAGS = {"auto": 0, "f": 1, "g": 2, "p": 4}
+
+
+def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup, path="auto"):
     """Graph-capture one pass over the ring and time whole replays."""
     dev = layers[0]["Wg"].device
     L = len(layers)
@@ -69,7 +72,7 @@ def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup):
         for i, lay in enumerate(layers):
             r = moe.forward(xs[i], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
                             br=lay["br"], out=ys[i], workspace=ws,
-                            return_route=record_ids)
+                            return_route=record_ids, flags=PATH_FLAGS[path])
             if record_ids:
                 ids_list.append(r[2].cpu().numpy())
 
@@ -117,7 +120,7 @@ def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup):
     counted, uniq = counted_bytes(cfg, ids_list)
     per_rep.sort()
     return {
-        "T": T, "k1": k1, "k2": k2, "steps": n_steps,
+        "T": T, "k1": k1, "k2": k2, "path": path, "steps": n_steps,
         "us_per_layer": us,
         "us_p10": per_rep[len(per_rep) // 10], "us_p90": per_rep[(9 * len(per_rep)) // 10],
         "tokens_per_s": T / (us * 1e-6),
@@ -201,10 +204,12 @@ def main():
 
     cells = []
     for spec in args.cells.split(","):
-        b, k1, k2 = spec.split(":")
+        parts = spec.split(":")
+        b, k1, k2 = parts[:3]
+        path = parts[3] if len(parts) > 3 else "auto"
         T, k1, k2 = int(b[1:]), int(k1), int(k2)
-        c = time_cell(moe, torch, layers, cfg, T, k1, k2, args.steps, args.warmup)
-        print(f"# cell b{T} {k1}:{k2}: {c['us_per_layer']:.2f} us/layer "
+        c = time_cell(moe, torch, layers, cfg, T, k1, k2, args.steps, args.warmup, path)
+        print(f"# cell b{T} {k1}:{k2} [{path}]: {c['us_per_layer']:.2f} us/layer "
               f"({c['us_p10']:.2f}-{c['us_p90']:.2f}), {c['tokens_per_s']:.0f} tok/s, "
               f"{c['counted_GBps']:.0f} GB/s counted ({100 * c['hbm_frac_counted']:.1f}% of HBM), "
               f"U={c['unique_experts']:.1f}", file=sys.stderr, flush=True)
@@ -222,7 +227,7 @@ def main():
 
     def find(T, k1, k2):
         for c in cells:
-            if (c["T"], c["k1"], c["k2"]) == (T, k1, k2):
+            if (c["T"], c["k1"], c["k2"], c["path"]) == (T, k1, k2, "auto"):
                 return c
         return None
 

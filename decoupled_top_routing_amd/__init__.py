@@ -20,13 +20,13 @@ from pathlib import Path
 import torch
 
 __all__ = ["route", "forward", "MoeError", "library_path", "load_library",
-           "F32", "BF16", "FORCE_DECODE", "FORCE_PREFILL"]
+           "F32", "BF16", "FORCE_FUSED", "FORCE_GROUPED", "FORCE_PREFILL"]
 
 PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libmoe.so"
 
 F32, BF16 = 0, 1
-FORCE_DECODE, FORCE_PREFILL = 1, 2
+FORCE_FUSED, FORCE_GROUPED, FORCE_PREFILL = 1, 2, 4
 ABI_VERSION = 1
 
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_EWORKSPACE",

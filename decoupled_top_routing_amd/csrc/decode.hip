@@ -13,8 +13,11 @@
 //  gateup_kernel : one work item = (unique expert, block of channels): stream
 //                  the gate and up rows once, dot with every token routed to
 //                  the expert, a[t,r,c] = silu(g) * u * w[t,r];
-//  down_kernel   : one work item = (token, block of output rows): y[t,h] =
-//                  sum over the token's slots and channels of Wd[e,h,c] a[t,r,c].
+//  down_kernel   : one work item = (unique expert, block of output rows):
+//                  stream the down rows once, z[t,r,h] = Wd[e,h,:] . a[t,r,:];
+//  combine_kernel: y[t,h] = sum of z[t,r,h] over the token's slots, in order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -117,79 +120,136 @@ hipError_t launch_plan(const int32_t *ids, int64_t n_assign, int E, int32_t *pla
 }
 
 // ---------------------------------------------------------------- gate/up
-// A wave computes kCPW channels of one expert for every token routed to it.
-// Lane L reads 16-byte chunks L, L+64, ... of each row, so a wave load
-// instruction covers 1 KiB of contiguous weights.
+// One workgroup = (unique expert u, block of 4*CPW channels); each wave owns
+// CPW channels and issues the loads of all its gate and up rows (2*CPW*NCH
+// 16-byte chunks per lane) before any arithmetic, then reuses them for every
+// token routed to u: a[t,r,c] = silu(Wg[e,c,:] x_t) * (Wu[e,c,:] x_t) * w[t,r].
 constexpr int kGuWaves = 4;
-constexpr int kCPW = 2;                       // channels per wave
-constexpr int kGuCB = kGuWaves * kCPW;        // channels per workgroup
-constexpr int kTokGroup = 4;                  // tokens held in registers at once
 
-template <typename WT, typename XT>
+template <typename WT, typename XT, int NCH, int CPW>
 __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, int H,
                                                      const WT *__restrict__ Wg,
                                                      const WT *__restrict__ Wu, int I,
                                                      const int32_t *__restrict__ plan, int E,
                                                      int k1, const float *__restrict__ w,
                                                      float *__restrict__ abuf) {
-  constexpr int NW = Elem<WT>::kPer16B;  // weights per 16-byte chunk
-  const int n_cb = (I + kGuCB - 1) / kGuCB;
+  constexpr int NW = Elem<WT>::kPer16B;
+  const int n_cb = (I + kGuWaves * CPW - 1) / (kGuWaves * CPW);
   const int u = blockIdx.x / n_cb;
   const int cb = blockIdx.x - u * n_cb;
-  const int U = plan[0];
-  if (u >= U) return;
+  if (u >= plan[0]) return;
+  const int32_t *uniq = plan + 4;
+  const int32_t *off = uniq + E;
+  const int32_t *list = off + E + 1;
+  const int e = uniq[u];
+  const int lb = off[u], ln = off[u + 1] - lb;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int c0 = (cb * kGuWaves + wv) * CPW;
+  uint4 gq[CPW][NCH], uq[CPW][NCH];
+#pragma unroll
+  for (int ci = 0; ci < CPW; ++ci) {
+    const int c = min(c0 + ci, I - 1);
+    const WT *grow = Wg + ((int64_t)e * I + c) * H;
+    const WT *urow = Wu + ((int64_t)e * I + c) * H;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      gq[ci][j] = ld16_stream(grow + (j * kWave + lane) * NW);
+      uq[ci][j] = ld16_stream(urow + (j * kWave + lane) * NW);
+    }
+  }
+  for (int i = 0; i < ln; ++i) {
+    const int asg = list[lb + i];
+    const XT *xr = x + (int64_t)(asg / k1) * H;
+    const float wt = w[asg];
+    float ag[CPW], au[CPW];
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) ag[ci] = au[ci] = 0.0f;
+    if constexpr (sizeof(WT) == 2 && sizeof(XT) == 2) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const uint4 xq = ld16(xr + (j * kWave + lane) * NW);
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+          ag[ci] = dot2_bf16(gq[ci][j].x, xq.x, ag[ci]);
+          ag[ci] = dot2_bf16(gq[ci][j].y, xq.y, ag[ci]);
+          ag[ci] = dot2_bf16(gq[ci][j].z, xq.z, ag[ci]);
+          ag[ci] = dot2_bf16(gq[ci][j].w, xq.w, ag[ci]);
+          au[ci] = dot2_bf16(uq[ci][j].x, xq.x, au[ci]);
+          au[ci] = dot2_bf16(uq[ci][j].y, xq.y, au[ci]);
+          au[ci] = dot2_bf16(uq[ci][j].z, xq.z, au[ci]);
+          au[ci] = dot2_bf16(uq[ci][j].w, xq.w, au[ci]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        float xv[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) xv[k] = Elem<XT>::load1(xr + (j * kWave + lane) * NW + k);
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+          float gv[NW], uv[NW];
+          Elem<WT>::widen(gq[ci][j], gv);
+          Elem<WT>::widen(uq[ci][j], uv);
+#pragma unroll
+          for (int k = 0; k < NW; ++k) {
+            ag[ci] = __builtin_fmaf(gv[k], xv[k], ag[ci]);
+            au[ci] = __builtin_fmaf(uv[k], xv[k], au[ci]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) {
+      const float g = wave_sum_dpp(ag[ci]);
+      const float uu = wave_sum_dpp(au[ci]);
+      const int c = c0 + ci;
+      if (lane == 0 && c < I) abuf[(int64_t)asg * I + c] = silu(g) * uu * wt;
+    }
+  }
+}
+
+// Any H (a multiple of 8): one channel per wave, chunks walked in a loop.
+template <typename WT, typename XT>
+__global__ __launch_bounds__(256) void gateup_any_kernel(const XT *__restrict__ x, int H,
+                                                         const WT *__restrict__ Wg,
+                                                         const WT *__restrict__ Wu, int I,
+                                                         const int32_t *__restrict__ plan, int E,
+                                                         int k1, const float *__restrict__ w,
+                                                         float *__restrict__ abuf) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  const int n_cb = (I + kGuWaves - 1) / kGuWaves;
+  const int u = blockIdx.x / n_cb;
+  const int cb = blockIdx.x - u * n_cb;
+  if (u >= plan[0]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
   const int32_t *list = off + E + 1;
   const int e = uniq[u];
   const int lb = off[u], ln = off[u + 1] - lb;
   const int lane = lane_id();
-  const int c0 = cb * kGuCB + (threadIdx.x >> 6) * kCPW;
-  const int n_chunks = H / NW;  // H % 8 == 0
-  for (int ci = 0; ci < kCPW; ++ci) {
-    const int c = c0 + ci;
-    if (c >= I) break;
-    const WT *grow = Wg + ((int64_t)e * I + c) * H;
-    const WT *urow = Wu + ((int64_t)e * I + c) * H;
-    for (int g0 = 0; g0 < ln; g0 += kTokGroup) {
-      const int ng = min(kTokGroup, ln - g0);
-      float ag[kTokGroup], au[kTokGroup];
-      int tok[kTokGroup];
+  const int c = cb * kGuWaves + (threadIdx.x >> 6);
+  if (c >= I) return;
+  const WT *grow = Wg + ((int64_t)e * I + c) * H;
+  const WT *urow = Wu + ((int64_t)e * I + c) * H;
+  const int n_chunks = H / NW;
+  for (int i = 0; i < ln; ++i) {
+    const int asg = list[lb + i];
+    const XT *xr = x + (int64_t)(asg / k1) * H;
+    float ag = 0.0f, au = 0.0f;
+    for (int ch = lane; ch < n_chunks; ch += kWave) {
+      float gv[NW], uv[NW];
+      Elem<WT>::widen(ld16(grow + ch * NW), gv);
+      Elem<WT>::widen(ld16(urow + ch * NW), uv);
 #pragma unroll
-      for (int i = 0; i < kTokGroup; ++i) {
-        ag[i] = 0.0f;
-        au[i] = 0.0f;
-        tok[i] = i < ng ? list[lb + g0 + i] / k1 : 0;
-      }
-      for (int ch = lane; ch < n_chunks; ch += kWave) {
-        float gv[NW], uv[NW];
-        Elem<WT>::widen(ld16_stream(grow + (int64_t)ch * NW), gv);
-        Elem<WT>::widen(ld16_stream(urow + (int64_t)ch * NW), uv);
-#pragma unroll
-        for (int i = 0; i < kTokGroup; ++i) {
-          if (i < ng) {
-            const XT *xr = x + (int64_t)tok[i] * H + (int64_t)ch * NW;
-#pragma unroll
-            for (int k = 0; k < NW; ++k) {
-              const float xv = Elem<XT>::load1(xr + k);
-              ag[i] = __builtin_fmaf(gv[k], xv, ag[i]);
-              au[i] = __builtin_fmaf(uv[k], xv, au[i]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kTokGroup; ++i) {
-        if (i < ng) {
-          const float g = wave_sum(ag[i]);
-          const float uu = wave_sum(au[i]);
-          if (lane == 0) {
-            const int a = list[lb + g0 + i];
-            abuf[(int64_t)a * I + c] = silu(g) * uu * w[a];
-          }
-        }
+      for (int k = 0; k < NW; ++k) {
+        const float xv = Elem<XT>::load1(xr + ch * NW + k);
+        ag = __builtin_fmaf(gv[k], xv, ag);
+        au = __builtin_fmaf(uv[k], xv, au);
       }
     }
+    const float g = wave_sum_dpp(ag), uu = wave_sum_dpp(au);
+    if (lane == 0) abuf[(int64_t)asg * I + c] = silu(g) * uu * w[asg];
   }
 }
 
@@ -198,56 +258,171 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
                          float *abuf, hipStream_t s) {
   const int64_t umax = n_assign < E ? n_assign : E;
-  const int n_cb = (I + kGuCB - 1) / kGuCB;
-  const dim3 grid((unsigned)(umax * n_cb)), block(256);
-  gateup_kernel<WT, XT><<<grid, block, 0, s>>>(x, H, Wg, Wu, I, plan, E, k1, w, abuf);
+  const int nch = (H * (int)sizeof(WT)) % (16 * kWave) == 0 ? (int)(H * sizeof(WT) / 16 / kWave) : 0;
+  auto go = [&](auto nch_c, auto cpw_c) {
+    constexpr int NCH = decltype(nch_c)::value, CPW = decltype(cpw_c)::value;
+    const int n_cb = (I + kGuWaves * CPW - 1) / (kGuWaves * CPW);
+    gateup_kernel<WT, XT, NCH, CPW><<<dim3((unsigned)(umax * n_cb)), dim3(256), 0, s>>>(
+        x, H, Wg, Wu, I, plan, E, k1, w, abuf);
+  };
+  using std::integral_constant;
+  switch (nch) {
+    case 1: go(integral_constant<int, 1>{}, integral_constant<int, 8>{}); break;
+    case 2: go(integral_constant<int, 2>{}, integral_constant<int, 4>{}); break;
+    case 4: go(integral_constant<int, 4>{}, integral_constant<int, 2>{}); break;
+    case 8: go(integral_constant<int, 8>{}, integral_constant<int, 1>{}); break;
+    default: {
+      const int n_cb = (I + kGuWaves - 1) / kGuWaves;
+      gateup_any_kernel<WT, XT><<<dim3((unsigned)(umax * n_cb)), dim3(256), 0, s>>>(
+          x, H, Wg, Wu, I, plan, E, k1, w, abuf);
+    }
+  }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- down
-// A wave computes kRPW output rows of one token, summing over the token's
-// k1 slots; lane L reads 16-byte chunks L, L+64, ... of each down row.
+// One workgroup = (unique expert u, block of 4*RPW rows of Wd[e]); each wave
+// loads its RPW rows (NCD 16-byte chunks per lane per row) up front, then for
+// every assignment routed to u writes z[asg, h] = Wd[e,h,:] . a[asg,:].
 constexpr int kDnWaves = 4;
 constexpr int kRPW = 2;
 constexpr int kDnRB = kDnWaves * kRPW;
 
-template <typename WT, typename XT>
+template <typename WT, int NCD>
 __global__ __launch_bounds__(256) void down_kernel(const WT *__restrict__ Wd, int H, int I,
-                                                   const int32_t *__restrict__ ids, int k1,
+                                                   const int32_t *__restrict__ plan, int E,
                                                    const float *__restrict__ abuf,
-                                                   XT *__restrict__ y) {
+                                                   float *__restrict__ zbuf) {
   constexpr int NW = Elem<WT>::kPer16B;
   const int n_hb = (H + kDnRB - 1) / kDnRB;
-  const int64_t t = blockIdx.x / n_hb;
-  const int hb = (int)(blockIdx.x - t * n_hb);
-  const int lane = lane_id();
-  const int h0 = hb * kDnRB + (threadIdx.x >> 6) * kRPW;
-  const int n_chunks = I / NW;
-  for (int hi = 0; hi < kRPW; ++hi) {
-    const int h = h0 + hi;
-    if (h >= H) break;
-    float acc = 0.0f;
-    for (int r = 0; r < k1; ++r) {
-      const int e = ids[t * k1 + r];
-      const WT *drow = Wd + ((int64_t)e * H + h) * I;
-      const float *arow = abuf + (t * k1 + r) * (int64_t)I;
-      for (int ch = lane; ch < n_chunks; ch += kWave) {
-        float dv[NW];
-        Elem<WT>::widen(ld16_stream(drow + (int64_t)ch * NW), dv);
+  const int u = blockIdx.x / n_hb;
+  const int hb = blockIdx.x - u * n_hb;
+  if (u >= plan[0]) return;
+  const int32_t *uniq = plan + 4;
+  const int32_t *off = uniq + E;
+  const int32_t *list = off + E + 1;
+  const int e = uniq[u];
+  const int lb = off[u], ln = off[u + 1] - lb;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int nch = I / NW;
+  const int h0 = hb * kDnRB + wv * kRPW;
+  uint4 dq[kRPW][NCD];
 #pragma unroll
-        for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], arow[ch * NW + k], acc);
+  for (int ri = 0; ri < kRPW; ++ri) {
+    const WT *drow = Wd + ((int64_t)e * H + min(h0 + ri, H - 1)) * I;
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      const int ch = j * kWave + lane;
+      dq[ri][j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int i = 0; i < ln; ++i) {
+    const int asg = list[lb + i];
+    const float *arow = abuf + (int64_t)asg * I;
+    float av[NCD][NW];
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      const int ch = j * kWave + lane;
+      if (ch < nch) {
+        const uint4 q0 = ld16(arow + ch * NW);
+        Elem<float>::widen(q0, av[j]);
+        if constexpr (NW == 8) Elem<float>::widen(ld16(arow + ch * NW + 4), av[j] + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) av[j][k] = 0.0f;
       }
     }
-    const float sum = wave_sum(acc);
-    if (lane == 0) Elem<XT>::store1(y + t * H + h, sum);
+#pragma unroll
+    for (int ri = 0; ri < kRPW; ++ri) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCD; ++j) {
+        float dv[NW];
+        Elem<WT>::widen(dq[ri][j], dv);
+#pragma unroll
+        for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[j][k], acc);
+      }
+      acc = wave_sum_dpp(acc);
+      const int h = h0 + ri;
+      if (lane == 0 && h < H) zbuf[(int64_t)asg * H + h] = acc;
+    }
   }
 }
 
-template <typename WT, typename XT>
-hipError_t launch_down(const WT *Wd, int64_t T, int H, int I, const int32_t *ids, int k1,
-                       const float *abuf, XT *y, hipStream_t s) {
-  const dim3 grid((unsigned)(((H + kDnRB - 1) / kDnRB) * T)), block(256);
-  down_kernel<WT, XT><<<grid, block, 0, s>>>(Wd, H, I, ids, k1, abuf, y);
+// Any I: one row per wave, chunks walked in a loop.
+template <typename WT>
+__global__ __launch_bounds__(256) void down_any_kernel(const WT *__restrict__ Wd, int H, int I,
+                                                       const int32_t *__restrict__ plan, int E,
+                                                       const float *__restrict__ abuf,
+                                                       float *__restrict__ zbuf) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  const int n_hb = (H + kDnWaves - 1) / kDnWaves;
+  const int u = blockIdx.x / n_hb;
+  const int hb = blockIdx.x - u * n_hb;
+  if (u >= plan[0]) return;
+  const int32_t *uniq = plan + 4;
+  const int32_t *off = uniq + E;
+  const int32_t *list = off + E + 1;
+  const int e = uniq[u];
+  const int lb = off[u], ln = off[u + 1] - lb;
+  const int lane = lane_id();
+  const int h = hb * kDnWaves + (threadIdx.x >> 6);
+  if (h >= H) return;
+  const WT *drow = Wd + ((int64_t)e * H + h) * I;
+  const int nch = I / NW;
+  for (int i = 0; i < ln; ++i) {
+    const int asg = list[lb + i];
+    const float *arow = abuf + (int64_t)asg * I;
+    float acc = 0.0f;
+    for (int ch = lane; ch < nch; ch += kWave) {
+      float dv[NW];
+      Elem<WT>::widen(ld16(drow + ch * NW), dv);
+#pragma unroll
+      for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], arow[ch * NW + k], acc);
+    }
+    acc = wave_sum_dpp(acc);
+    if (lane == 0) zbuf[(int64_t)asg * H + h] = acc;
+  }
+}
+
+template <typename WT>
+hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
+                       const float *abuf, float *zbuf, hipStream_t s) {
+  const int64_t umax = n_assign < E ? n_assign : E;
+  const int n_hb = (H + kDnRB - 1) / kDnRB;
+  const int ncd = (int)((I * sizeof(WT) / 16 + kWave - 1) / kWave);
+  const dim3 grid((unsigned)(umax * n_hb)), block(256);
+  switch (ncd) {
+    case 1: down_kernel<WT, 1><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
+    case 2: down_kernel<WT, 2><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
+    case 3: down_kernel<WT, 3><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
+    case 4: down_kernel<WT, 4><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
+    default: {
+      const int n_hb1 = (H + kDnWaves - 1) / kDnWaves;
+      down_any_kernel<WT><<<dim3((unsigned)(umax * n_hb1)), block, 0, s>>>(Wd, H, I, plan, E, abuf,
+                                                                           zbuf);
+    }
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine
+// y[t,h] = sum over the token's k1 slots of z[t*k1 + r, h], in slot order.
+template <typename XT>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ zbuf, int64_t T,
+                                                      int H, int k1, XT *__restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * H) return;
+  const int64_t t = i / H, h = i - t * H;
+  float s = 0.0f;
+  for (int r = 0; r < k1; ++r) s = s + zbuf[(t * k1 + r) * H + h];
+  Elem<XT>::store1(y + i, s);
+}
+
+template <typename XT>
+hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hipStream_t s) {
+  const int64_t n = T * H;
+  combine_kernel<XT><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(zbuf, T, H, k1, y);
   return hipGetLastError();
 }
 
@@ -255,8 +430,9 @@ hipError_t launch_down(const WT *Wd, int64_t T, int H, int I, const int32_t *ids
   template hipError_t launch_gateup<WT, XT>(const XT *, int, const WT *, const WT *, int, \
                                             const int32_t *, int, int64_t, int,           \
                                             const float *, float *, hipStream_t);         \
-  template hipError_t launch_down<WT, XT>(const WT *, int64_t, int, int, const int32_t *, \
-                                          int, const float *, XT *, hipStream_t);
+  template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t, \
+                                      const float *, float *, hipStream_t);               \
+  template hipError_t launch_combine<XT>(const float *, int64_t, int, int, XT *, hipStream_t);
 MOE_INST_DECODE(float, float)
 MOE_INST_DECODE(bf16_t, bf16_t)
 

@@ -35,9 +35,9 @@
 // every tag is the current one, so the data's arrival is the signal.  There
 // are no fences (on gfx950 an agent-scope fence writes back or invalidates a
 // whole XCD's L2, which takes microseconds) and no hot counters (same-address
-// atomics serialize at about 10 ns each).  The tag is the workspace's epoch
-// + 1; the last block to finish (a two-level count) advances the epoch, so
-// stale words from earlier calls never match.  Every wait is bounded: a
+// atomics serialize at about 10 ns each).  The tag is a NaN pattern made
+// from the workspace's epoch (call_tag); the last block to finish (a
+// two-level count) advances the epoch, so stale words never match.  Every wait is bounded: a
 // timeout sets the error word and the block moves on, so the kernel always
 // terminates.
 #include "common.hpp"
@@ -102,6 +102,15 @@ __device__ __forceinline__ T coh_ld(const T *p) {
 }
 __device__ __forceinline__ int atomic_inc(int32_t *p) {
   return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tag of a call: a quiet-NaN bit pattern carrying 22 bits of the
+// workspace's epoch.  Other paths of the library write finite floats and
+// small integers into the same workspace bytes; neither can ever equal a
+// tag, so a stale word is never mistaken for a published one (and a fresh,
+// zero-filled workspace holds no tag either).
+__device__ __forceinline__ uint32_t call_tag(uint32_t epoch) {
+  return 0x7FC00000u | ((epoch + 1u) & 0x003FFFFFu);
 }
 
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
@@ -623,7 +632,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int b = blockIdx.x;
   int32_t *sync = a.sync;
   const uint32_t epoch = (uint32_t)coh_ld(sync + kEpoch);
-  const uint32_t tag = epoch + 1u;
+  const uint32_t tag = call_tag(epoch);
   if (b < a.n_r) {
     router_block<XT, NCHR>(a, b, tag);
     return;
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       for (int k = threadIdx.x; k < kSub; k += kThreads) coh_st(sync + kDoneSub0 + k * kLine, 0);
       if (threadIdx.x == 0) {
         coh_st(sync + kDoneTop, 0);
-        coh_st(sync + kEpoch, (int32_t)tag);
+        coh_st(sync + kEpoch, (int32_t)(epoch + 1u));
       }
     }
   }

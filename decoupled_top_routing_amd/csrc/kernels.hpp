@@ -44,8 +44,12 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
                          float *abuf, hipStream_t s);
 
-template <typename WT, typename XT>
-hipError_t launch_down(const WT *Wd, int64_t T, int H, int I, const int32_t *ids, int k1,
-                       const float *abuf, XT *y, hipStream_t s);
+template <typename WT>
+hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
+                       const float *abuf, float *zbuf, hipStream_t s);
+
+template <typename XT>
+hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hipStream_t s);
+
 
 }  // namespace moe

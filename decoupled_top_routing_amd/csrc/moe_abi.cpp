@@ -33,10 +33,10 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace layout of moe_forward (each segment 256-byte aligned).
 struct Layout {
-  size_t logits, ids, w, plan, abuf, total;
+  size_t logits, ids, w, plan, abuf, zbuf, total;
 };
 
-Layout layout(int64_t T, int32_t E, int32_t I, int32_t k1) {
+Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   Layout L;
   size_t o = moe::kSyncRegionBytes;  // reserved: sync words of the fused path
   const size_t n_assign = (size_t)T * (size_t)k1;
@@ -50,6 +50,8 @@ Layout layout(int64_t T, int32_t E, int32_t I, int32_t k1) {
   o += round256((4 + (size_t)E + (size_t)E + 1 + n_assign) * 4);
   L.abuf = o;
   o += round256(n_assign * (size_t)I * 4);
+  L.zbuf = o;
+  o += round256(n_assign * (size_t)H * 4);
   L.total = o;
   return L;
 }
@@ -66,28 +68,43 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
   return MOE_OK;
 }
 
-// Small batches whose shapes the fused decode kernel covers take it (one
-// launch per layer); everything else takes the multi-kernel path.
-bool use_fused(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf16,
-               uint32_t flags) {
-  if (flags & MOE_FLAG_FORCE_PREFILL) return false;
-  return moe::fused_decode_supported(T, H, E, I, k1, bf16);
+enum class Path { Fused, Grouped, Prefill };
+
+// Batches of one token whose shapes the fused kernel covers take it (one
+// launch per layer); other batches take the grouped multi-kernel path.
+int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf16,
+                uint32_t flags, Path *path) {
+  const bool fused_ok = moe::fused_decode_supported(T, H, E, I, k1, bf16);
+  if (flags & MOE_FLAG_FORCE_FUSED) {
+    if (!fused_ok) return fail(MOE_ENOTSUP, "the fused path does not take these shapes");
+    *path = Path::Fused;
+    return MOE_OK;
+  }
+  if (flags & MOE_FLAG_FORCE_PREFILL) {
+    return fail(MOE_ENOTSUP, "the prefill path is not built");
+  }
+  if (flags & MOE_FLAG_FORCE_GROUPED) {
+    *path = Path::Grouped;
+    return MOE_OK;
+  }
+  *path = (fused_ok && T == 1) ? Path::Fused : Path::Grouped;
+  return MOE_OK;
 }
 
 size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   moe::DecodeLayout D;
   const size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
-  const size_t b = layout(T, E, I, k1).total;
+  const size_t b = layout(T, H, E, I, k1).total;
   return a > b ? a : b;
 }
 
 template <typename WT, typename XT>
 int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const float *br, int32_t E,
                   const WT *Wg, const WT *Wu, const WT *Wd, int32_t I, int32_t k1, int32_t k2,
-                  XT *y, float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
+                  XT *y, float *logits_out, int32_t *ids_out, float *w_out, Path path,
                   char *ws, const Layout &L, hipStream_t s) {
   hipError_t e;
-  if (use_fused(T, H, E, I, k1, sizeof(WT) == 2, flags)) {
+  if (path == Path::Fused) {
     if ((e = moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
                                               logits_out, ids_out, w_out, ws, s)) != hipSuccess)
       return hip_fail(e, "fused decode kernel");
@@ -98,6 +115,7 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   float *w = reinterpret_cast<float *>(ws + L.w);
   int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
   float *abuf = reinterpret_cast<float *>(ws + L.abuf);
+  float *zbuf = reinterpret_cast<float *>(ws + L.zbuf);
   const int64_t n_assign = T * k1;
   if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) != hipSuccess)
     return hip_fail(e, "router kernel");
@@ -108,8 +126,10 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   if ((e = moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)) !=
       hipSuccess)
     return hip_fail(e, "gate/up kernel");
-  if ((e = moe::launch_down<WT, XT>(Wd, T, H, I, ids, k1, abuf, y, s)) != hipSuccess)
+  if ((e = moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s)) != hipSuccess)
     return hip_fail(e, "down kernel");
+  if ((e = moe::launch_combine<XT>(zbuf, T, H, k1, y, s)) != hipSuccess)
+    return hip_fail(e, "combine kernel");
   return MOE_OK;
 }
 
@@ -168,10 +188,9 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
   if (I < 8 || I % 8 != 0) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 8", I);
   if ((int64_t)H * I > (int64_t(1) << 31))
     return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
-  if (flags & ~(MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_PREFILL))
-    return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
-  if ((flags & MOE_FLAG_FORCE_DECODE) && (flags & MOE_FLAG_FORCE_PREFILL))
-    return fail(MOE_EINVAL, "both path flags set");
+  const uint32_t all = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
+  if (flags & ~all) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if (__builtin_popcount(flags) > 1) return fail(MOE_EINVAL, "more than one path flag set");
   const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
   const bool b16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
   if (!f32 && !b16)
@@ -184,23 +203,25 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
   if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
       (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
     return fail(MOE_EALIGN, "br and the route outputs need 4-byte alignment");
-  const Layout L = layout(T, E, I, k1);
+  const Layout L = layout(T, H, E, I, k1);
   const size_t need = workspace_bytes_for(T, H, E, I, k1);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                 need, workspace_bytes, workspace);
+  Path path;
+  if ((rc = choose_path(T, H, E, I, k1, b16, flags, &path)) != MOE_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   char *ws = static_cast<char *>(workspace);
   if (f32)
     return forward_typed<float, float>(
         static_cast<const float *>(x), T, H, Wr, br, E, static_cast<const float *>(Wgate),
         static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2,
-        static_cast<float *>(y), logits_out, ids_out, w_out, flags, ws, L, s);
+        static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, s);
   return forward_typed<moe::bf16_t, moe::bf16_t>(
       static_cast<const moe::bf16_t *>(x), T, H, Wr, br, E,
       static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
       static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, static_cast<moe::bf16_t *>(y),
-      logits_out, ids_out, w_out, flags, ws, L, s);
+      logits_out, ids_out, w_out, path, ws, L, s);
 }
 
 }  // extern "C"

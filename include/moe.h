@@ -66,10 +66,17 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* moe_forward flags: force one of the two expert paths (testing); 0 = choose
- * by batch size. */
-#define MOE_FLAG_FORCE_DECODE 1u
-#define MOE_FLAG_FORCE_PREFILL 2u
+/* moe_forward flags: force one of the execution paths (0 = choose by batch
+ * size and shape).  All paths compute the same layer; they differ in kernels:
+ *   FUSED   one launch per layer (router, route, experts), batches <= 8 tokens;
+ *   GROUPED router, route, per-expert plan, gate/up, down and combine kernels
+ *           (grouped GEMVs that read each activated expert once);
+ *   PREFILL the same steps with the expert projections as bf16 MFMA grouped
+ *           GEMMs (large batches).
+ * A forced path that cannot take the call's shapes returns MOE_ENOTSUP. */
+#define MOE_FLAG_FORCE_FUSED 1u
+#define MOE_FLAG_FORCE_GROUPED 2u
+#define MOE_FLAG_FORCE_PREFILL 4u
 
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -123,7 +130,7 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *          leaves its synchronisation words at zero after every call, so one
  *          zero fill at allocation lasts for the workspace's lifetime.  Calls
  *          that run concurrently need separate workspaces.
- *   flags: 0, MOE_FLAG_FORCE_DECODE or MOE_FLAG_FORCE_PREFILL.
+ *   flags: 0 or one MOE_FLAG_FORCE_* value.
  *
  *   Supported dtype pairs (act, w): (F32, F32) and (BF16, BF16); accumulation
  *   is fp32.  1 <= E <= 1024; H and I multiples of 8; 1 <= k1 <= E;

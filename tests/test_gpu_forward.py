@@ -59,7 +59,7 @@ def tiny():
     return L, host_layer(L)
 
 
-PATHS = [0, moe.FORCE_DECODE, moe.FORCE_PREFILL]
+PATHS = [0, moe.FORCE_FUSED, moe.FORCE_GROUPED]
 
 
 @pytest.mark.parametrize("k1,k2", synth.TINY.k_pairs)
@@ -85,11 +85,12 @@ def test_a3b_decode(a3b, k1, k2, T):
     run_and_check(cfg, Lt, Lht, k1, k2)
 
 
-@pytest.mark.parametrize("flags", [moe.FORCE_PREFILL])
+@pytest.mark.parametrize("flags", [moe.FORCE_FUSED, moe.FORCE_GROUPED])
 @pytest.mark.parametrize("k1,k2", [(8, 8), (4, 16)])
-def test_a3b_decode_general_path(a3b, k1, k2, flags):
+@pytest.mark.parametrize("T", [1, 8])
+def test_a3b_decode_each_path(a3b, k1, k2, flags, T):
     L, Lh = a3b
-    run_and_check(synth.DECODE_B8, L, Lh, k1, k2, flags)
+    run_and_check(synth.DECODE_B8, dict(L, x=L["x"][:T]), dict(Lh, x=Lh["x"][:T]), k1, k2, flags)
 
 
 def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
@@ -103,7 +104,7 @@ def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
     for rep in range(3):
         for name, (lay, T, k1, k2, fl) in {
                 "a": (g, 1, 4, 16, 0), "b": (tg, 8, 2, 4, 0), "c": (g, 8, 8, 8, 0),
-                "d": (g, 5, 3, 16, moe.FORCE_PREFILL), "e": (tg, 3, 2, 16, 0)}.items():
+                "d": (g, 5, 3, 16, moe.FORCE_GROUPED), "e": (tg, 3, 2, 16, 0)}.items():
             y = moe.forward(lay["x"][:T], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
                             br=lay["br"], flags=fl, workspace=ws)
             torch.cuda.synchronize()
