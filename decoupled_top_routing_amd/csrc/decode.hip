@@ -406,6 +406,79 @@ hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- down, T = 1
+// One token: each wave owns one output row and sums over every unique
+// expert directly, y[h] = sum_u Wd[e_u,h,:] . a[u,:] (ascending expert order,
+// per-lane partial sums, one wave reduction), so no partials and no combine.
+// The rows of the first kPF experts are loaded before any arithmetic.
+constexpr int kPF1 = 8;
+
+template <typename WT, typename XT, int NCD>
+__global__ __launch_bounds__(256) void down_one_token_kernel(const WT *__restrict__ Wd, int H,
+                                                             int I, const int32_t *__restrict__ plan,
+                                                             int E, const float *__restrict__ abuf,
+                                                             XT *__restrict__ y) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (h >= H) return;
+  const int lane = lane_id();
+  const int U = plan[0];
+  const int32_t *uniq = plan + 4;
+  const int32_t *off = uniq + E;
+  const int32_t *list = off + E + 1;
+  const int nch = I / NW;
+  uint4 dq[kPF1][NCD];
+  auto issue = [&](int u, uint4 (&dst)[NCD]) {
+    const WT *drow = Wd + ((int64_t)uniq[u] * H + h) * I;
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      const int ch = j * kWave + lane;
+      dst[j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kPF1; ++s)
+    if (s < U) issue(s, dq[s]);
+  float acc = 0.0f;
+  for (int ub = 0; ub < U; ub += kPF1) {
+#pragma unroll
+    for (int s = 0; s < kPF1; ++s) {
+      const int u = ub + s;
+      if (u < U) {
+        const float *arow = abuf + (int64_t)list[off[u]] * I;
+#pragma unroll
+        for (int j = 0; j < NCD; ++j) {
+          const int ch = j * kWave + lane;
+          if (ch < nch) {
+            float av[NW], dv[NW];
+            Elem<float>::widen(ld16(arow + ch * NW), av);
+            if constexpr (NW == 8) Elem<float>::widen(ld16(arow + ch * NW + 4), av + 4);
+            Elem<WT>::widen(dq[s][j], dv);
+#pragma unroll
+            for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[k], acc);
+          }
+        }
+        if (u + kPF1 < U) issue(u + kPF1, dq[s]);
+      }
+    }
+  }
+  acc = wave_sum_dpp(acc);
+  if (lane == 0) Elem<XT>::store1(y + h, acc);
+}
+
+template <typename WT, typename XT>
+hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan, int E,
+                                 const float *abuf, XT *y, hipStream_t s) {
+  const int ncd = (int)((I * sizeof(WT) / 16 + kWave - 1) / kWave);
+  const dim3 grid((unsigned)((H + 3) / 4)), block(256);
+  switch (ncd) {
+    case 1: down_one_token_kernel<WT, XT, 1><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, y); break;
+    case 2: down_one_token_kernel<WT, XT, 2><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, y); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- combine
 // y[t,h] = sum over the token's k1 slots of z[t*k1 + r, h], in slot order.
 template <typename XT>
@@ -432,7 +505,9 @@ hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hi
                                             const float *, float *, hipStream_t);         \
   template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t, \
                                       const float *, float *, hipStream_t);               \
-  template hipError_t launch_combine<XT>(const float *, int64_t, int, int, XT *, hipStream_t);
+  template hipError_t launch_combine<XT>(const float *, int64_t, int, int, XT *, hipStream_t); \
+  template hipError_t launch_down_one_token<WT, XT>(const WT *, int, int, const int32_t *, int, \
+                                                    const float *, XT *, hipStream_t);
 MOE_INST_DECODE(float, float)
 MOE_INST_DECODE(bf16_t, bf16_t)
 

@@ -220,14 +220,6 @@ __device__ void router_block(const Args &a, int rb, uint32_t tag) {
 // The route of every token and the unique experts of the batch, in LDS:
 // uniq[u] ascending, list[off[u] .. off[u+1]) = assignments (t*k1 + r) routed
 // to uniq[u], ascending.  Built identically by every block.
-struct BlockRoute {
-  uint64_t K[kThreads];
-  int32_t rank[kThreads];
-  float sp[kThreads];
-  int32_t sid[kThreads];
-  float red[kWaves];
-  float M;
-};
 
 struct Plan {
   float logits[kMaxLogits];
@@ -244,95 +236,6 @@ struct Plan {
 
 __device__ __forceinline__ int uidx_of(const Plan &P, int e) {
   return P.pre[e >> 5] + __popc(P.bits[e >> 5] & ((1u << (e & 31)) - 1u));
-}
-
-// One token (E <= 256) routed by the whole block, with the arithmetic of
-// route_token: exact max; e = exp_nonpos(l - max); S = the pairwise tree
-// (each wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
-// (p descending, index ascending) counted in parallel (element e by
-// 256 / next_pow2(E) threads, each over a slice of the keys); the mass summed
-// in rank order by one thread; w = p / M or p.
-
-__device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
-                                  int32_t *ids_out, float *w_out, BlockRoute &S) {
-#pragma clang fp contract(off)
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const bool valid = tid < E;
-  const float lv = valid ? l[tid] : -INFINITY;
-  const float wm = wave_max_dpp(lv);
-  if (lane == 0) S.red[wv] = wm;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]));
-  const float ex = valid ? exp_nonpos(lv - m) : 0.0f;
-  const float ws = wave_sum_dpp(ex);
-  __syncthreads();
-  if (lane == 0) S.red[wv] = ws;
-  __syncthreads();
-  const float sum = (S.red[0] + S.red[1]) + (S.red[2] + S.red[3]);
-  const float p = ex / sum;
-  const uint32_t key = valid ? __float_as_uint(p) + 1u : 0u;
-  S.K[tid] = ((uint64_t)key << 11) | (uint64_t)(2047 - tid);
-  S.rank[tid] = 0;
-  __syncthreads();
-  int epow = 1, lg = 0;
-  while (epow < E) {
-    epow <<= 1;
-    ++lg;
-  }
-  const int split = kThreads / epow;
-  const int e = tid & (epow - 1), part = tid >> lg;
-  const int chunk = epow / split;
-  if (e < E) {
-    const uint64_t Ke = S.K[e];
-    const int j0 = part * chunk, j1 = min(E, j0 + chunk);
-    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-    int j = j0;
-    for (; j + 4 <= j1; j += 4) {
-      c0 += S.K[j] > Ke ? 1 : 0;
-      c1 += S.K[j + 1] > Ke ? 1 : 0;
-      c2 += S.K[j + 2] > Ke ? 1 : 0;
-      c3 += S.K[j + 3] > Ke ? 1 : 0;
-    }
-    for (; j < j1; ++j) c0 += S.K[j] > Ke ? 1 : 0;
-    const int cnt = (c0 + c1) + (c2 + c3);
-    if (cnt) atomicAdd(&S.rank[e], cnt);
-  }
-  __syncthreads();
-  const bool renorm = k2 < E;
-  const int R = renorm ? k2 : k1;
-  if (valid) {
-    const int r = S.rank[tid];
-    if (r < R) {
-      S.sp[r] = p;
-      S.sid[r] = tid;
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // left to right in rank order; the loads run ahead of the adds
-    float M = 0.0f;
-    if (renorm) {
-      int r = 0;
-      for (; r + 8 <= R; r += 8) {
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = S.sp[r + q];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) M = M + v[q];
-      }
-      for (; r < R; ++r) M = M + S.sp[r];
-    }
-    S.M = M;
-  }
-  __syncthreads();
-  if (tid < k1) {
-    const float wr = renorm ? S.sp[tid] / S.M : S.sp[tid];
-    ids[tid] = S.sid[tid];
-    w[tid] = wr;
-    if (ids_out) ids_out[tid] = S.sid[tid];
-    if (w_out) w_out[tid] = wr;
-  }
-  __syncthreads();
 }
 
 template <int V>
@@ -682,6 +585,7 @@ static size_t fused_copy_stride(size_t bytes) { return ((bytes + 4095) & ~(size_
 
 size_t fused_decode_workspace(int64_t T, int H, int E, int I, int k1, DecodeLayout *L) {
   (void)H;
+  static_assert(fused::kSyncWords <= kRouteTicketWord, "sync words overlap the route ticket");
   static_assert(fused::kSyncWords * 4 <= kSyncRegionBytes, "sync region too small");
   L->sync = 0;
   size_t o = kSyncRegionBytes;

@@ -39,6 +39,19 @@ hipError_t launch_router(const XT *x, int64_t T, int H, const float *Wr, const f
 hipError_t launch_plan(const int32_t *ids, int64_t n_assign, int E, int32_t *plan,
                        hipStream_t s);
 
+// Route with one workgroup per token; with plan != NULL (T*k1 <= 64) the last
+// block also builds the plan.  `ticket` is a zero word of the sync region.
+hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int k2,
+                             int32_t *ids, float *w, int32_t *ids2, float *w2, int32_t *plan,
+                             int32_t *ticket, hipStream_t s);
+
+template <typename WT, typename XT>
+hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan, int E,
+                                 const float *abuf, XT *y, hipStream_t s);
+
+// word of the sync region used as the route kernel's ticket
+constexpr int kRouteTicketWord = 1024;
+
 template <typename WT, typename XT>
 hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,

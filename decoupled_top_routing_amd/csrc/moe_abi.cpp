@@ -70,8 +70,10 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
 
 enum class Path { Fused, Grouped, Prefill };
 
-// Batches of one token whose shapes the fused kernel covers take it (one
-// launch per layer); other batches take the grouped multi-kernel path.
+// The grouped multi-kernel path is the default: measured on MI355X it beats
+// the single-launch fused path at every decode batch (its gate/up and down
+// kernels sustain more bandwidth than the fused kernel's, which is limited
+// by register-bound occupancy); the fused path stays available on request.
 int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf16,
                 uint32_t flags, Path *path) {
   const bool fused_ok = moe::fused_decode_supported(T, H, E, I, k1, bf16);
@@ -87,7 +89,7 @@ int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf1
     *path = Path::Grouped;
     return MOE_OK;
   }
-  *path = (fused_ok && T == 1) ? Path::Fused : Path::Grouped;
+  *path = Path::Grouped;
   return MOE_OK;
 }
 
@@ -117,15 +119,29 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   float *abuf = reinterpret_cast<float *>(ws + L.abuf);
   float *zbuf = reinterpret_cast<float *>(ws + L.zbuf);
   const int64_t n_assign = T * k1;
+  int32_t *ticket = reinterpret_cast<int32_t *>(ws) + moe::kRouteTicketWord;
   if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) != hipSuccess)
     return hip_fail(e, "router kernel");
-  if ((e = moe::launch_route(logits, T, E, k1, k2, ids, w, ids_out, w_out, s)) != hipSuccess)
-    return hip_fail(e, "route kernel");
-  if ((e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
-    return hip_fail(e, "plan kernel");
+  if (n_assign <= 64) {
+    if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, plan, ticket,
+                                    s)) != hipSuccess)
+      return hip_fail(e, "route kernel");
+  } else {
+    if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
+                                    nullptr, s)) != hipSuccess)
+      return hip_fail(e, "route kernel");
+    if ((e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
+      return hip_fail(e, "plan kernel");
+  }
   if ((e = moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)) !=
       hipSuccess)
     return hip_fail(e, "gate/up kernel");
+  const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
+  if (T == 1 && ncd <= 2) {
+    if ((e = moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)) != hipSuccess)
+      return hip_fail(e, "down kernel");
+    return MOE_OK;
+  }
   if ((e = moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s)) != hipSuccess)
     return hip_fail(e, "down kernel");
   if ((e = moe::launch_combine<XT>(zbuf, T, H, k1, y, s)) != hipSuccess)
@@ -161,8 +177,8 @@ int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1, int32_t k2,
   if (!logits || !ids || !weights) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
     return fail(MOE_EALIGN, "logits, ids and weights need 4-byte alignment");
-  hipError_t e = moe::launch_route(logits, T, E, k1, k2, ids, weights, nullptr, nullptr,
-                                   (hipStream_t)stream);
+  hipError_t e = moe::launch_route_plan(logits, T, E, k1, k2, ids, weights, nullptr, nullptr,
+                                        nullptr, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "route kernel");
   return MOE_OK;
 }

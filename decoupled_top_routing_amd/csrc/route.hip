@@ -30,6 +30,93 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
                  ids2 ? ids2 + t * k1 : nullptr, w2 ? w2 + t * k1 : nullptr);
 }
 
+// One workgroup per token: the whole block routes it (E <= 256, k1 <= 256),
+// else its first wave does.  With `plan`, the last block to finish (ticket)
+// also builds the batch plan (T*k1 <= 64): U, the unique experts ascending,
+// and per unique expert its assignments (t*k1 + r) ascending.  The ticket
+// word is zero before and after the kernel.
+template <int V>
+__global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict__ logits,
+                                                         int64_t T, int E, int k1, int k2,
+                                                         int32_t *__restrict__ ids,
+                                                         float *__restrict__ w,
+                                                         int32_t *__restrict__ ids2,
+                                                         float *__restrict__ w2,
+                                                         int32_t *__restrict__ plan,
+                                                         int32_t *__restrict__ ticket) {
+  __shared__ float sl[kBlockThreads];
+  __shared__ BlockRoute S;
+  __shared__ int s_last;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *lrow = logits + t * E;
+  int32_t *ir = ids + t * k1;
+  float *wr = w + t * k1;
+  int32_t *ir2 = ids2 ? ids2 + t * k1 : nullptr;
+  float *wr2 = w2 ? w2 + t * k1 : nullptr;
+  if (E <= kBlockThreads && k1 <= kBlockThreads) {
+    if (tid < E) sl[tid] = lrow[tid];
+    __syncthreads();
+    route_token_block(sl, E, k1, k2, ir, wr, ir2, wr2, S);
+  } else if (tid < kWave) {
+    route_token<V>(lrow, E, k1, k2, ir, wr, ir2, wr2);
+  }
+  if (!plan) return;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(ticket, 1) == (int)T - 1;
+  __syncthreads();
+  if (!s_last || tid >= kWave) return;
+  if (tid == 0) *ticket = 0;
+  __threadfence();
+  // one wave builds the plan: lane i holds assignment i (n <= 64)
+  const int n = (int)T * k1;
+  const int i = tid;
+  const int e = i < n ? ids[i] : 0x7FFFFFFF;
+  int cnt_less = 0, same_before = 0;
+  for (int j = 0; j < n; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    cnt_less += ej < e;
+    same_before += (ej == e) & (j < i);
+  }
+  const uint64_t first = __ballot(i < n && same_before == 0);
+  int uniq_less = 0;
+  for (int j = 0; j < n; ++j)
+    if ((first >> j) & 1ull) uniq_less += __builtin_amdgcn_readlane(e, j) < e;
+  int32_t *uniq = plan + 4;
+  int32_t *off = uniq + E;
+  int32_t *list = off + E + 1;
+  if (i < n) {
+    if (same_before == 0) {
+      uniq[uniq_less] = e;
+      off[uniq_less] = cnt_less;
+    }
+    list[cnt_less + same_before] = i;
+  }
+  if (i == 0) {
+    const int U = __popcll(first);
+    plan[0] = U;
+    off[U] = n;
+  }
+}
+
+hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int k2,
+                             int32_t *ids, float *w, int32_t *ids2, float *w2, int32_t *plan,
+                             int32_t *ticket, hipStream_t s) {
+  const dim3 grid((unsigned)T), block(256);
+  if (E <= 64)
+    route_plan_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+  else if (E <= 128)
+    route_plan_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+  else if (E <= 256)
+    route_plan_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+  else if (E <= 512)
+    route_plan_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+  else
+    route_plan_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const float *logits, int64_t T, int E, int k1, int k2, int32_t *ids,
                         float *w, int32_t *ids2, float *w2, hipStream_t s) {
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
@@ -96,9 +183,55 @@ __global__ __launch_bounds__(256) void router_kernel(const XT *__restrict__ x, i
   }
 }
 
+// Small batches: one wave per expert loads its whole router row (NCHR
+// 16-byte chunks per lane, all in flight at once), then dots it with every
+// token.
+template <typename XT, int NCHR>
+__global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__ x, int64_t T,
+                                                          int H, const float *__restrict__ Wr,
+                                                          const float *__restrict__ br, int E,
+                                                          float *__restrict__ logits,
+                                                          float *__restrict__ logits2) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int lane = lane_id();
+  const float *wrow = Wr + (int64_t)e * H;
+  float wv[NCHR][4];
+#pragma unroll
+  for (int j = 0; j < NCHR; ++j) Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wv[j]);
+  const float b = br ? br[e] : 0.0f;
+  for (int64_t t = 0; t < T; ++t) {
+    const XT *xr = x + t * H;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCHR; ++j) {
+      const int h = (j * kWave + lane) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wv[j][k], Elem<XT>::load1(xr + h + k), acc);
+    }
+    const float sum = wave_sum_dpp(acc) + b;
+    if (lane == 0) {
+      logits[t * E + e] = sum;
+      if (logits2) logits2[t * E + e] = sum;
+    }
+  }
+}
+
 template <typename XT>
 hipError_t launch_router(const XT *x, int64_t T, int H, const float *Wr, const float *br, int E,
                          float *logits, float *logits2, hipStream_t s) {
+  const int nchr = (H % (4 * kWave) == 0) ? H / (4 * kWave) : 0;
+  if (T <= 64 && (nchr == 1 || nchr == 2 || nchr == 4 || nchr == 8 || nchr == 16)) {
+    const dim3 grid((unsigned)((E + 3) / 4)), block(256);
+    switch (nchr) {
+      case 1: router_rows_kernel<XT, 1><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
+      case 2: router_rows_kernel<XT, 2><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
+      case 4: router_rows_kernel<XT, 4><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
+      case 8: router_rows_kernel<XT, 8><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
+      default: router_rows_kernel<XT, 16><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(((E + 3) / 4) * ((T + 7) / 8))), block(256);
   router_kernel<XT><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2);
   return hipGetLastError();
