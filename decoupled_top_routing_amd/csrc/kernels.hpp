@@ -49,6 +49,22 @@ template <typename WT, typename XT>
 hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan, int E,
                                  const float *abuf, XT *y, hipStream_t s);
 
+// ---- prefill (bf16 MFMA) path
+bool prefill_supported(int H, int I, bool bf16);
+size_t prefill_plan_words(int64_t n, int E);
+hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const float *Wr,
+                             const float *br, int E, uint16_t *w3, float *logits, float *logits2,
+                             hipStream_t s);
+hipError_t launch_prefill_plan(const int32_t *ids, int64_t n, int E, int32_t *plan,
+                               hipStream_t s);
+hipError_t launch_gateup_mma(const uint16_t *x, int H, const uint16_t *Wg, const uint16_t *Wu,
+                             int I, const int32_t *plan, int E, int64_t n, int k1, const float *w,
+                             uint16_t *abf, hipStream_t s);
+hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I,
+                           const int32_t *plan, int E, int64_t n, uint16_t *zbf, hipStream_t s);
+hipError_t launch_combine_bf16(const uint16_t *zbf, int64_t T, int H, int k1, uint16_t *y,
+                               hipStream_t s);
+
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
 

@@ -56,6 +56,33 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   return L;
 }
 
+// Workspace layout of the prefill path.
+struct PrefillLayout {
+  size_t logits, ids, w, plan, w3, abf, zbf, total;
+};
+
+PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
+  PrefillLayout L;
+  size_t o = moe::kSyncRegionBytes;
+  const size_t n = (size_t)T * (size_t)k1;
+  L.logits = o;
+  o += round256((size_t)T * E * 4);
+  L.ids = o;
+  o += round256(n * 4);
+  L.w = o;
+  o += round256(n * 4);
+  L.plan = o;
+  o += round256(moe::prefill_plan_words((int64_t)n, E) * 4);
+  L.w3 = o;
+  o += round256((size_t)3 * E * H * 2);
+  L.abf = o;
+  o += round256(n * (size_t)I * 2);
+  L.zbf = o;
+  o += round256(n * (size_t)H * 2);
+  L.total = o;
+  return L;
+}
+
 // Largest T accepted: keeps every element index of every tensor well inside
 // int64 and every grid dimension inside its hardware limit.
 constexpr int64_t kMaxT = int64_t(1) << 24;
@@ -70,6 +97,9 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
 
 enum class Path { Fused, Grouped, Prefill };
 
+// From this batch size on the expert projections run as MFMA GEMMs.
+constexpr int64_t kPrefillMinT = 256;
+
 // The grouped multi-kernel path is the default: measured on MI355X it beats
 // the single-launch fused path at every decode batch (its gate/up and down
 // kernels sustain more bandwidth than the fused kernel's, which is limited
@@ -82,22 +112,57 @@ int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf1
     *path = Path::Fused;
     return MOE_OK;
   }
+  const bool prefill_ok = moe::prefill_supported(H, I, bf16);
   if (flags & MOE_FLAG_FORCE_PREFILL) {
-    return fail(MOE_ENOTSUP, "the prefill path is not built");
+    if (!prefill_ok) return fail(MOE_ENOTSUP, "the prefill path takes bf16, H % 128 == 0 and I % 64 == 0");
+    *path = Path::Prefill;
+    return MOE_OK;
   }
   if (flags & MOE_FLAG_FORCE_GROUPED) {
     *path = Path::Grouped;
     return MOE_OK;
   }
-  *path = Path::Grouped;
+  *path = (prefill_ok && T >= kPrefillMinT) ? Path::Prefill : Path::Grouped;
   return MOE_OK;
 }
 
 size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   moe::DecodeLayout D;
-  const size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
+  size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
   const size_t b = layout(T, H, E, I, k1).total;
-  return a > b ? a : b;
+  const size_t c = prefill_layout(T, H, E, I, k1).total;
+  if (b > a) a = b;
+  return c > a ? c : a;
+}
+
+int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, const float *br,
+                    int32_t E, const uint16_t *Wg, const uint16_t *Wu, const uint16_t *Wd,
+                    int32_t I, int32_t k1, int32_t k2, uint16_t *y, float *logits_out,
+                    int32_t *ids_out, float *w_out, char *ws, hipStream_t s) {
+  const PrefillLayout L = prefill_layout(T, H, E, I, k1);
+  float *logits = reinterpret_cast<float *>(ws + L.logits);
+  int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
+  float *w = reinterpret_cast<float *>(ws + L.w);
+  int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + L.w3);
+  uint16_t *abf = reinterpret_cast<uint16_t *>(ws + L.abf);
+  uint16_t *zbf = reinterpret_cast<uint16_t *>(ws + L.zbf);
+  const int64_t n = T * k1;
+  hipError_t e;
+  if ((e = moe::launch_router_mma(x, T, H, Wr, br, E, w3, logits, logits_out, s)) != hipSuccess)
+    return hip_fail(e, "router kernel");
+  if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr, nullptr,
+                                  s)) != hipSuccess)
+    return hip_fail(e, "route kernel");
+  if ((e = moe::launch_prefill_plan(ids, n, E, plan, s)) != hipSuccess)
+    return hip_fail(e, "plan kernel");
+  if ((e = moe::launch_gateup_mma(x, H, Wg, Wu, I, plan, E, n, k1, w, abf, s)) != hipSuccess)
+    return hip_fail(e, "gate/up kernel");
+  if ((e = moe::launch_down_mma(abf, H, Wd, I, plan, E, n, zbf, s)) != hipSuccess)
+    return hip_fail(e, "down kernel");
+  if ((e = moe::launch_combine_bf16(zbf, T, H, k1, y, s)) != hipSuccess)
+    return hip_fail(e, "combine kernel");
+  return MOE_OK;
 }
 
 template <typename WT, typename XT>
@@ -106,6 +171,14 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
                   XT *y, float *logits_out, int32_t *ids_out, float *w_out, Path path,
                   char *ws, const Layout &L, hipStream_t s) {
   hipError_t e;
+  if constexpr (sizeof(WT) == 2) {
+    if (path == Path::Prefill)
+      return forward_prefill(reinterpret_cast<const uint16_t *>(x), T, H, Wr, br, E,
+                             reinterpret_cast<const uint16_t *>(Wg),
+                             reinterpret_cast<const uint16_t *>(Wu),
+                             reinterpret_cast<const uint16_t *>(Wd), I, k1, k2,
+                             reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, s);
+  }
   if (path == Path::Fused) {
     if ((e = moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
                                               logits_out, ids_out, w_out, ws, s)) != hipSuccess)

@@ -94,7 +94,8 @@ def _fwd(lib, **kw):
     (dict(act=0, wt=1), 4), (dict(act=1, wt=0), 4), (dict(act=2, wt=2), 4),
     (dict(x=24), 2), (dict(Wd=8), 2), (dict(br=2), 2),
     (dict(ws=None), 3), (dict(ws=128), 3), (dict(wsb=1024), 3),
-    (dict(x=None), 1), (dict(flags=3), 1), (dict(flags=16), 1), (dict(flags=4), 4),
+    (dict(x=None), 1), (dict(flags=3), 1), (dict(flags=16), 1),
+    (dict(flags=4, act=0, wt=0), 4), (dict(flags=4, I=776), 4), (dict(flags=4, H=2056), 4),
 ])
 def test_forward_rejects_bad_arguments(kw, code):
     lib = moe.load_library()

@@ -14,45 +14,9 @@ import torch
 import decoupled_top_routing_amd as moe
 import oracle
 from decoupled_top_routing_amd import synth
-from parity import (TOL_BF16, TOL_F32, check_route_exact, host_layer, near_tie_tokens,
-                    normwise_err, to_f64)
+from parity import DEV, host_layer, run_and_check, to_dev
 
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
-
-
-def to_dev(L):
-    return {k: (None if v is None else v.to(DEV)) for k, v in L.items()}
-
-
-def run_and_check(cfg, L, Lh, k1, k2, flags=0, token_sample=None, tol=None):
-    g = to_dev(L) if L["Wg"].device.type == "cpu" else L
-    print(f"{cfg.name} T={g['x'].shape[0]} k1={k1} k2={k2} flags={flags}", flush=True)
-    y, lg, ids, w = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], k1, k2,
-                                br=g["br"], return_route=True, flags=flags)
-    torch.cuda.synchronize()
-    lg_h = lg.cpu().numpy()
-    T = lg_h.shape[0]
-    sel = np.arange(T) if token_sample is None else np.asarray(token_sample)
-    x_h = Lh["x"][sel]
-    # (i) logits
-    ref_l = oracle.logits(x_h, Lh["Wr"], Lh["br"], nthreads=8)
-    assert normwise_err(lg_h[sel], ref_l) <= 1e-5
-    # (ii) route on the GPU logits, all tokens
-    oids, ow = check_route_exact(ids, w, lg_h, k1, k2, f"{cfg.name} ({k1},{k2})")
-    # (iii) experts and combine on that route
-    y_ref = oracle.experts(x_h, Lh["Wg"], Lh["Wu"], Lh["Wd"], oids[sel], ow[sel], nthreads=8)
-    err = normwise_err(to_f64(y)[sel], y_ref)
-    tol = tol if tol is not None else (TOL_F32 if cfg.dtype == "f32" else TOL_BF16)
-    assert err <= tol, f"normwise error {err} > {tol}"
-    # (iv) independent route from the oracle's own logits
-    iids, _ = oracle.route(ref_l, k1, k2)
-    ties = near_tie_tokens(oracle.softmax(ref_l), k1)
-    differ = (np.sort(iids, 1) != np.sort(oids[sel], 1)).any(1)
-    assert not (differ & ~ties).any(), "experts differ away from a near-tie"
-    return y, err
-
-
 @pytest.fixture(scope="module")
 def tiny():
     L = synth.make_layer(synth.TINY)

@@ -1,0 +1,29 @@
+"""The largest layer (E=512, H=4096, I=1024, bf16), generated on the device,
+at one token and at 64 tokens.  The oracle gets only the activated experts
+of the checked tokens (one layer's experts are 12.9 GB)."""
+import numpy as np
+import pytest
+import torch
+
+from decoupled_top_routing_amd import synth
+from parity import run_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def large():
+    L = synth.make_layer(synth.LARGE, T=64, device="cuda:0")
+    Lh = {k: synth.to_numpy(L[k]) for k in ("x", "Wr", "br")}
+    yield L, Lh
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k1,k2", synth.LARGE.k_pairs)
+@pytest.mark.parametrize("T", [1, 64])
+def test_large(large, k1, k2, T):
+    L, Lh = large
+    sample = np.arange(T) if T == 1 else np.array([0, 21, 42, 63])
+    run_and_check(synth.LARGE, dict(L, x=L["x"][:T]), dict(Lh, x=Lh["x"][:T]), k1, k2,
+                  token_sample=sample)
