@@ -29,7 +29,7 @@ COMMON = [
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]
 
-SOURCES = ["route.hip", "decode.hip", "fused_decode.hip", "prefill.hip", "moe_abi.cpp"]
+SOURCES = ["route.hip", "decode.hip", "fused_decode.hip", "decode_b1.hip", "prefill.hip", "moe_abi.cpp"]
 
 
 def _compile(src: str) -> Path:

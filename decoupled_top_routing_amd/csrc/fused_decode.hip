@@ -43,13 +43,13 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_device.hpp"
+#include "sync.hpp"
 
 namespace moe {
 namespace fused {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kMaxTok = 8;        // tokens each block routes itself
 constexpr int kMaxAssign = 512;   // T * k1 held in LDS
 constexpr int kPF = 6;            // down rows prefetched for this many experts
@@ -66,9 +66,10 @@ constexpr int kRepA = 8;          // copies of the channel activations
 
 // int32 word offsets in the sync region; counters are 16 words (64 B) apart
 constexpr int kLine = 16;
-constexpr int kEpoch = 0;
+constexpr int kEpoch = kEpochWord;
 constexpr int kDoneTop = kLine;
-constexpr int kError = 2 * kLine;
+constexpr int kError = kErrorWord;
+static_assert(kErrorWord == 2 * kLine, "error word is a line of its own");
 constexpr int kDoneSub0 = 4 * kLine;  // kSub lines
 constexpr int kSyncWords = kDoneSub0 + kSub * kLine;
 constexpr int kMaxLogits = 2048;      // T * E staged in LDS
@@ -91,92 +92,6 @@ struct Args {
   int T, H, E, I, k1, k2;
   int n_r, epw, umax, n_cb, n_gu, n_hb, n_blocks;
 };
-
-template <typename T>
-__device__ __forceinline__ void coh_st(T *p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T coh_ld(const T *p) {
-  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int atomic_inc(int32_t *p) {
-  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The tag of a call: a quiet-NaN bit pattern carrying 22 bits of the
-// workspace's epoch.  Other paths of the library write finite floats and
-// small integers into the same workspace bytes; neither can ever equal a
-// tag, so a stale word is never mistaken for a published one (and a fresh,
-// zero-filled workspace holds no tag either).
-__device__ __forceinline__ uint32_t call_tag(uint32_t epoch) {
-  return 0x7FC00000u | ((epoch + 1u) & 0x003FFFFFu);
-}
-
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
-  return ((uint64_t)tag << 32) | __float_as_uint(v);
-}
-
-// Re-read a tagged word until it carries `tag` (bounded); returns its value.
-__device__ __forceinline__ float await_tagged(const uint64_t *p, uint32_t tag, int32_t *err) {
-  uint64_t w = coh_ld(p);
-  uint32_t n = 0;
-  while ((uint32_t)(w >> 32) != tag) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++n > kSpinLimit) {
-      coh_st(err, 1);
-      break;
-    }
-    w = coh_ld(p);
-  }
-  return __uint_as_float((uint32_t)w);
-}
-
-// Stage n tagged words into dst[0..n) (LDS; dst[0..2n) with two bf16 values
-// per word when PACKED), n <= MAXW * kThreads: each
-// thread first issues the loads of all its words, then re-reads only those
-// that do not carry `tag` yet, so the wait costs one round trip, not one per
-// word.  Ends with a block barrier.
-template <int MAXW, bool PACKED = false, typename AddrFn>
-__device__ void stage_tagged(float *dst, int n, AddrFn addr, uint32_t tag, int32_t *err) {
-  uint64_t w[MAXW];
-  const uint64_t done = (uint64_t)tag << 32;
-#pragma unroll
-  for (int k = 0; k < MAXW; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    w[k] = i < n ? coh_ld(addr(i)) : done;
-  }
-  uint32_t spins = 0;
-  while (true) {
-    bool ok = true;
-#pragma unroll
-    for (int k = 0; k < MAXW; ++k) ok &= (uint32_t)(w[k] >> 32) == tag;
-    if (ok) break;
-    if (++spins > kSpinLimit) {
-      coh_st(err, 1);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int k = 0; k < MAXW; ++k) {
-      const int i = threadIdx.x + k * kThreads;
-      if (i < n && (uint32_t)(w[k] >> 32) != tag) w[k] = coh_ld(addr(i));
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < MAXW; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    if (i < n) {
-      if constexpr (PACKED) {
-        dst[2 * i] = bf16_lo((uint32_t)w[k]);
-        dst[2 * i + 1] = bf16_hi((uint32_t)w[k]);
-      } else {
-        dst[i] = __uint_as_float((uint32_t)w[k]);
-      }
-    }
-  }
-  __syncthreads();
-}
 
 // Thread 0 adds 1 to *ctr once the whole block is here; the old value is
 // returned to every thread of the block.

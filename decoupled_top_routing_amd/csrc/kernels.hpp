@@ -15,6 +15,11 @@ constexpr int kMaxExperts = 1024;
 // Its size and place do not depend on the call's shapes, so one workspace can
 // serve calls of different shapes.
 constexpr size_t kSyncRegionBytes = 16384;
+// int32 words of the sync region shared by the paths that hand values over
+// between workgroups: the workspace's epoch (source of the call tags) and an
+// error word set by a wait that timed out
+constexpr int kEpochWord = 0;
+constexpr int kErrorWord = 32;
 
 // Byte offsets of the fused decode kernel's buffers in the workspace.
 struct DecodeLayout {
@@ -48,6 +53,24 @@ hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int 
 template <typename WT, typename XT>
 hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan, int E,
                                  const float *abuf, XT *y, hipStream_t s);
+
+// one token: router, route and plan (k1 <= 64) in one launch
+bool router_route_supported(int H);
+template <typename XT>
+hipError_t launch_router_route(const XT *x, int H, const float *Wr, const float *br, int E,
+                               int k1, int k2, float *logits, float *logits2, int32_t *ids,
+                               float *w, int32_t *ids2, float *w2, int32_t *plan, int32_t *ticket,
+                               hipStream_t s);
+
+// ---- one token in two launches (router + route + gate/up, then down)
+bool decode_b1_supported(int H, int I, int k1, bool bf16);
+size_t decode_b1_tagged_bytes(int E, int k1, int64_t *tp_offset, int64_t *tp_rep_words);
+template <typename WT, typename XT>
+hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
+                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
+                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+                            int32_t *sync, char *tagged, int32_t *ids, float *w, int32_t *plan,
+                            float *abuf, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);

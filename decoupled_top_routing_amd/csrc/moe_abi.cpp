@@ -33,7 +33,7 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace layout of moe_forward (each segment 256-byte aligned).
 struct Layout {
-  size_t logits, ids, w, plan, abuf, zbuf, total;
+  size_t logits, ids, w, plan, abuf, zbuf, tagged, total;
 };
 
 Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
@@ -52,6 +52,9 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   o += round256(n_assign * (size_t)I * 4);
   L.zbuf = o;
   o += round256(n_assign * (size_t)H * 4);
+  L.tagged = o;
+  int64_t tp_off = 0, tp_rep = 0;
+  o += round256(moe::decode_b1_tagged_bytes(E, k1, &tp_off, &tp_rep));
   L.total = o;
   return L;
 }
@@ -193,9 +196,23 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   float *zbuf = reinterpret_cast<float *>(ws + L.zbuf);
   const int64_t n_assign = T * k1;
   int32_t *ticket = reinterpret_cast<int32_t *>(ws) + moe::kRouteTicketWord;
-  if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) != hipSuccess)
+  if (T == 1 && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2)) {
+    if ((e = moe::launch_decode_b1<WT, XT>(
+             x, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y, logits_out, ids_out, w_out,
+             reinterpret_cast<int32_t *>(ws), ws + L.tagged, ids, w, plan, abuf, s)) != hipSuccess)
+      return hip_fail(e, "one-token kernels");
+    return MOE_OK;
+  }
+  if (T == 1 && moe::router_route_supported(H)) {
+    if ((e = moe::launch_router_route<XT>(x, H, Wr, br, E, k1, k2, logits, logits_out, ids, w,
+                                          ids_out, w_out, plan, ticket, s)) != hipSuccess)
+      return hip_fail(e, "router kernel");
+    if (n_assign > 64 && (e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
+      return hip_fail(e, "plan kernel");
+  } else if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) !=
+             hipSuccess) {
     return hip_fail(e, "router kernel");
-  if (n_assign <= 64) {
+  } else if (n_assign <= 64) {
     if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, plan, ticket,
                                     s)) != hipSuccess)
       return hip_fail(e, "route kernel");

@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_device.hpp"
+#include "sync.hpp"
 
 #pragma clang fp contract(off)
 
@@ -30,11 +31,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
                  ids2 ? ids2 + t * k1 : nullptr, w2 ? w2 + t * k1 : nullptr);
 }
 
-// One workgroup per token: the whole block routes it (E <= 256, k1 <= 256),
-// else its first wave does.  With `plan`, the last block to finish (ticket)
-// also builds the batch plan (T*k1 <= 64): U, the unique experts ascending,
-// and per unique expert its assignments (t*k1 + r) ascending.  The ticket
-// word is zero before and after the kernel.
+// One workgroup per token.  With `plan`, the last block to finish (ticket)
+// also builds the batch plan (T*k1 <= 64); the ids it reads were stored
+// device-coherently by the other blocks.  The ticket word is zero before
+// and after the kernel.
 template <int V>
 __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict__ logits,
                                                          int64_t T, int E, int k1, int k2,
@@ -45,59 +45,34 @@ __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict
                                                          int32_t *__restrict__ plan,
                                                          int32_t *__restrict__ ticket) {
   __shared__ float sl[kBlockThreads];
+  __shared__ int32_t s_ids[kMaxExperts];
+  __shared__ float s_w[kMaxExperts];
   __shared__ BlockRoute S;
   __shared__ int s_last;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const float *lrow = logits + t * E;
-  int32_t *ir = ids + t * k1;
-  float *wr = w + t * k1;
-  int32_t *ir2 = ids2 ? ids2 + t * k1 : nullptr;
-  float *wr2 = w2 ? w2 + t * k1 : nullptr;
-  if (E <= kBlockThreads && k1 <= kBlockThreads) {
+  if (E <= kBlockThreads) {
     if (tid < E) sl[tid] = lrow[tid];
     __syncthreads();
-    route_token_block(sl, E, k1, k2, ir, wr, ir2, wr2, S);
-  } else if (tid < kWave) {
-    route_token<V>(lrow, E, k1, k2, ir, wr, ir2, wr2);
+    route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S);
+  } else {
+    route_into_lds<V>(lrow, E, k1, k2, s_ids, s_w, S);
+  }
+  const int64_t o = t * k1;
+  for (int r = tid; r < k1; r += kBlockThreads) {
+    if (plan)
+      coh_st(ids + o + r, s_ids[r]);
+    else
+      ids[o + r] = s_ids[r];
+    w[o + r] = s_w[r];
+    if (ids2) ids2[o + r] = s_ids[r];
+    if (w2) w2[o + r] = s_w[r];
   }
   if (!plan) return;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ticket, 1) == (int)T - 1;
-  __syncthreads();
-  if (!s_last || tid >= kWave) return;
-  if (tid == 0) *ticket = 0;
-  __threadfence();
-  // one wave builds the plan: lane i holds assignment i (n <= 64)
+  if (!last_of(ticket, (int)T, &s_last) || tid >= kWave) return;
   const int n = (int)T * k1;
-  const int i = tid;
-  const int e = i < n ? ids[i] : 0x7FFFFFFF;
-  int cnt_less = 0, same_before = 0;
-  for (int j = 0; j < n; ++j) {
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    cnt_less += ej < e;
-    same_before += (ej == e) & (j < i);
-  }
-  const uint64_t first = __ballot(i < n && same_before == 0);
-  int uniq_less = 0;
-  for (int j = 0; j < n; ++j)
-    if ((first >> j) & 1ull) uniq_less += __builtin_amdgcn_readlane(e, j) < e;
-  int32_t *uniq = plan + 4;
-  int32_t *off = uniq + E;
-  int32_t *list = off + E + 1;
-  if (i < n) {
-    if (same_before == 0) {
-      uniq[uniq_less] = e;
-      off[uniq_less] = cnt_less;
-    }
-    list[cnt_less + same_before] = i;
-  }
-  if (i == 0) {
-    const int U = __popcll(first);
-    plan[0] = U;
-    off[U] = n;
-  }
+  wave_plan(tid < n ? coh_ld(ids + tid) : 0x7FFFFFFF, n, E, plan);
 }
 
 hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int k2,
@@ -216,6 +191,101 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__
     }
   }
 }
+
+// One token: router, route and plan in one launch.  Wave e computes logit
+// e (its router row in flight at once, NCHR 16-byte chunks per lane) and
+// stores it device-coherently; the block that takes the last ticket reads
+// every logit back, routes the token, writes ids and w and, for k1 <= 64,
+// the plan.
+template <typename XT, int NCHR, int V>
+__global__ __launch_bounds__(256) void router_route_kernel(
+    const XT *__restrict__ x, int H, const float *__restrict__ Wr, const float *__restrict__ br,
+    int E, int k1, int k2, float *__restrict__ logits, float *__restrict__ logits2,
+    int32_t *__restrict__ ids, float *__restrict__ w, int32_t *__restrict__ ids2,
+    float *__restrict__ w2, int32_t *__restrict__ plan, int32_t *__restrict__ ticket) {
+  __shared__ float sl[kMaxExperts];
+  __shared__ int32_t s_ids[kMaxExperts];
+  __shared__ float s_w[kMaxExperts];
+  __shared__ BlockRoute S;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int e = blockIdx.x * 4 + (tid >> 6);
+  if (e < E) {
+    const float *wrow = Wr + (int64_t)e * H;
+    float wv[NCHR][4];
+#pragma unroll
+    for (int j = 0; j < NCHR; ++j)
+      Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wv[j]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCHR; ++j) {
+      const int h = (j * kWave + lane) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wv[j][k], Elem<XT>::load1(x + h + k), acc);
+    }
+    const float sum = wave_sum_dpp(acc) + (br ? br[e] : 0.0f);
+    if (lane == 0) {
+      coh_st(logits + e, sum);
+      if (logits2) logits2[e] = sum;
+    }
+  }
+  if (!last_of(ticket, (int)gridDim.x, &s_last)) return;
+  for (int i = tid; i < E; i += kBlockThreads) sl[i] = coh_ld(logits + i);
+  __syncthreads();
+  route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S);
+  for (int r = tid; r < k1; r += kBlockThreads) {
+    ids[r] = s_ids[r];
+    w[r] = s_w[r];
+    if (ids2) ids2[r] = s_ids[r];
+    if (w2) w2[r] = s_w[r];
+  }
+  if (plan && k1 <= kWave && tid < kWave) wave_plan(tid < k1 ? s_ids[tid] : 0x7FFFFFFF, k1, E, plan);
+}
+
+template <typename XT, int NCHR>
+static void launch_rr_v(const XT *x, int H, const float *Wr, const float *br, int E, int k1,
+                        int k2, float *logits, float *logits2, int32_t *ids, float *w,
+                        int32_t *ids2, float *w2, int32_t *plan, int32_t *ticket, hipStream_t s) {
+  const dim3 grid((unsigned)((E + 3) / 4)), block(256);
+#define RR(V) router_route_kernel<XT, NCHR, V><<<grid, block, 0, s>>>(x, H, Wr, br, E, k1, k2, \
+                                                                      logits, logits2, ids, w, \
+                                                                      ids2, w2, plan, ticket)
+  if (E <= 64) RR(1);
+  else if (E <= 128) RR(2);
+  else if (E <= 256) RR(4);
+  else if (E <= 512) RR(8);
+  else RR(16);
+#undef RR
+}
+
+bool router_route_supported(int H) {
+  const int nchr = (H % (4 * kWave) == 0) ? H / (4 * kWave) : 0;
+  return nchr == 1 || nchr == 2 || nchr == 4 || nchr == 8 || nchr == 16;
+}
+
+template <typename XT>
+hipError_t launch_router_route(const XT *x, int H, const float *Wr, const float *br, int E,
+                               int k1, int k2, float *logits, float *logits2, int32_t *ids,
+                               float *w, int32_t *ids2, float *w2, int32_t *plan, int32_t *ticket,
+                               hipStream_t s) {
+  switch (H / (4 * kWave)) {
+    case 1: launch_rr_v<XT, 1>(x, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, plan, ticket, s); break;
+    case 2: launch_rr_v<XT, 2>(x, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, plan, ticket, s); break;
+    case 4: launch_rr_v<XT, 4>(x, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, plan, ticket, s); break;
+    case 8: launch_rr_v<XT, 8>(x, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, plan, ticket, s); break;
+    default: launch_rr_v<XT, 16>(x, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, plan, ticket, s); break;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_router_route<float>(const float *, int, const float *, const float *,
+                                               int, int, int, float *, float *, int32_t *, float *,
+                                               int32_t *, float *, int32_t *, int32_t *,
+                                               hipStream_t);
+template hipError_t launch_router_route<bf16_t>(const bf16_t *, int, const float *, const float *,
+                                                int, int, int, float *, float *, int32_t *,
+                                                float *, int32_t *, float *, int32_t *, int32_t *,
+                                                hipStream_t);
 
 template <typename XT>
 hipError_t launch_router(const XT *x, int64_t T, int H, const float *Wr, const float *br, int E,

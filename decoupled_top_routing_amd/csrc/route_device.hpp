@@ -5,6 +5,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "sync.hpp"
 
 namespace moe {
 
@@ -229,7 +230,7 @@ constexpr int kBlockWaves = kBlockThreads / kWave;
 // the mass summed in rank order by one thread; w = p / M or p.
 
 struct BlockRoute {
-  uint64_t K[kBlockThreads];
+  alignas(16) uint64_t K[kBlockThreads];
   int32_t rank[kBlockThreads];
   float sp[kBlockThreads];
   int32_t sid[kBlockThreads];
@@ -263,23 +264,29 @@ __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t
     epow <<= 1;
     ++lg;
   }
-  // element e is ranked by `split` threads, each over `chunk` keys
+  // element e is ranked by `split` threads, each over `chunk` keys of the
+  // padded key array (keys past E are below every valid key, so they never
+  // count); 8 keys per step, all loads of a step in flight together
   const int split = min(kBlockThreads / epow, epow);
   const int e = tid & (epow - 1), part = tid >> lg;
   const int chunk = epow / split;
   if (e < E && part < split) {
     const uint64_t Ke = S.K[e];
-    const int j0 = part * chunk, j1 = min(E, j0 + chunk);
-    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-    int j = j0;
-    for (; j + 4 <= j1; j += 4) {
-      c0 += S.K[j] > Ke ? 1 : 0;
-      c1 += S.K[j + 1] > Ke ? 1 : 0;
-      c2 += S.K[j + 2] > Ke ? 1 : 0;
-      c3 += S.K[j + 3] > Ke ? 1 : 0;
+    const int j0 = part * chunk;
+    int c0 = 0, c1 = 0;
+    if (chunk >= 8) {
+      for (int j = j0; j < j0 + chunk; j += 8) {
+        const ulonglong2 q0 = *reinterpret_cast<const ulonglong2 *>(&S.K[j]);
+        const ulonglong2 q1 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 2]);
+        const ulonglong2 q2 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 4]);
+        const ulonglong2 q3 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 6]);
+        c0 += (q0.x > Ke) + (q0.y > Ke) + (q1.x > Ke) + (q1.y > Ke);
+        c1 += (q2.x > Ke) + (q2.y > Ke) + (q3.x > Ke) + (q3.y > Ke);
+      }
+    } else {
+      for (int j = j0; j < j0 + chunk; ++j) c0 += S.K[j] > Ke ? 1 : 0;
     }
-    for (; j < j1; ++j) c0 += S.K[j] > Ke ? 1 : 0;
-    const int cnt = (c0 + c1) + (c2 + c3);
+    const int cnt = c0 + c1;
     if (cnt) atomicAdd(&S.rank[e], cnt);
   }
   __syncthreads();
@@ -318,6 +325,66 @@ __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t
     if (w_out) w_out[tid] = wr;
   }
   __syncthreads();
+}
+
+// Every store of this block is complete (s_waitcnt), then thread 0 takes a
+// ticket; true in the whole block that takes the last of n tickets, which
+// also puts the ticket word back to zero.
+__device__ inline bool last_of(int32_t *ticket, int n, int *s_last) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = old == n - 1;
+    if (old == n - 1) coh_st(ticket, 0);
+  }
+  __syncthreads();
+  return *s_last;
+}
+
+// The batch plan from ids [n] (n <= 64), built by one wave: U, the unique
+// experts ascending, and per unique expert its assignments (t*k1 + r)
+// ascending.  Lane i holds assignment i.
+__device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
+  const int i = lane_id();
+  int cnt_less = 0, same_before = 0;
+  for (int j = 0; j < n; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    cnt_less += ej < e;
+    same_before += (ej == e) & (j < i);
+  }
+  const uint64_t first = __ballot(i < n && same_before == 0);
+  int uniq_less = 0;
+  for (int j = 0; j < n; ++j)
+    if ((first >> j) & 1ull) uniq_less += __builtin_amdgcn_readlane(e, j) < e;
+  int32_t *uniq = plan + 4;
+  int32_t *off = uniq + E;
+  int32_t *list = off + E + 1;
+  if (i < n) {
+    if (same_before == 0) {
+      uniq[uniq_less] = e;
+      off[uniq_less] = cnt_less;
+    }
+    list[cnt_less + same_before] = i;
+  }
+  if (i == 0) {
+    const int U = __popcll(first);
+    plan[0] = U;
+    off[U] = n;
+  }
+}
+
+// Route one token into LDS (s_ids, s_w: rank order), by the whole block
+// (E <= 256, k1 <= 256) or by its first wave.
+template <int V>
+__device__ void route_into_lds(const float *l, int E, int k1, int k2, int32_t *s_ids, float *s_w,
+                               BlockRoute &S) {
+  if (E <= kBlockThreads && k1 <= kBlockThreads) {
+    route_token_block(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S);
+  } else {
+    if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr);
+    __syncthreads();
+  }
 }
 
 }  // namespace moe
