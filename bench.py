@@ -2,20 +2,26 @@
 """Benchmark of the routed MoE layer with Eq. 2 weights on one MI355X.
 
 A step is one call of the whole layer (router, route, experts, combine) on one
-batch.  The headline workload is decode at batch 1 on the H=2048, E=128,
-I=768 bf16 layer with k1:k2 = 4:16, run over a ring of 32 distinct seeded
-layers (38.7 GB) so that every layer's weights come from HBM, not from the
-256 MB Infinity Cache.  The ring is captured once in a HIP graph and replayed;
-HIP events on the capture stream time the replays.  The same ring is also
-timed at 8:8 and at batch 8, and reported in "cells".
+batch.  The headline workload is batch-1 decode on the H=2048, E=128, I=768
+bf16 layer with k1:k2 = 4:16, run over a ring of 32 distinct seeded layers
+(38.7 GB) so that every layer's weights come from HBM, not from the 256 MB
+Infinity Cache.  Each cell's ring is captured once in a HIP graph and
+replayed; HIP events on the capture stream time the replays.  The other cells
+(batch 1 and 8 at every k1:k2 pair, the 4096-token prefill, the E=512 layer
+at 1 and 64 tokens) are reported in "cells".
+
+The roofline object is for the headline's dominant kernel: every launch of
+one call is bracketed with HIP events (moe_profile_launch) in an eager pass,
+the longest is the dominant one, and its events are then recorded around that
+launch in every call of a second timed eager pass over the ring.
 
 Prints one JSON line (see the repository's benchmark contract).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import os
 import sys
 import time
 from pathlib import Path
@@ -26,46 +32,104 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
 RING = 32
+PATH_FLAGS = {"auto": 0, "f": 1, "g": 2, "p": 4}
+DEFAULT_CELLS = ",".join([
+    "C2:1:4:16", "C2:1:8:8", "C2:1:4:4", "C2:1:4:128", "C2:1:3:16", "C2:1:2:16",
+    "C3:8:4:16", "C3:8:8:8", "C3:8:4:4", "C3:8:4:128", "C3:8:3:16", "C3:8:2:16",
+    "C4:4096:4:16", "C4:4096:8:8",
+    "C5:1:10:10", "C5:1:5:5", "C5:1:5:20", "C5:64:10:10", "C5:64:5:5", "C5:64:5:20",
+])
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=6400)
+    ap.add_argument("--steps", type=int, default=6400,
+                    help="timed layer calls of the headline cell")
     ap.add_argument("--warmup", type=int, default=320)
     ap.add_argument("--ring", type=int, default=RING)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cells", default="b1:4:16,b1:8:8,b8:4:16,b8:8:8",
-                    help="cells to time; the first is the headline")
+    ap.add_argument("--cells", default=DEFAULT_CELLS,
+                    help="CONFIG:T:k1:k2[:path] list; the first is the headline")
     return ap.parse_args()
 
 
-def counted_bytes(cfg, ids_list):
-    """Activated-expert bytes per step, from the actual routes: unique experts
-    of each step's batch times 3*I*H weight elements."""
-    per_expert = 3 * cfg.I * cfg.H * (2 if cfg.dtype == "bf16" else 4)
-    uniq = [len(set(ids.flatten().tolist())) for ids in ids_list]
-    return per_expert * sum(uniq) / len(uniq), sum(uniq) / len(uniq)
+# ------------------------------------------------------------------ workloads
+def make_sets(synth, torch, names, ring):
+    """Device layers per configuration name."""
+    sets = {}
+    t0 = time.perf_counter()
+    if names & {"C2", "C3"}:
+        sets["C2"] = sets["C3"] = (synth.DECODE_B8,
+                                   [synth.make_layer(synth.DECODE_B8, layer=i, device="cuda")
+                                    for i in range(ring)])
+    if "C4" in names:
+        sets["C4"] = (synth.PREFILL, [synth.make_layer(synth.PREFILL, device="cuda")])
+    if "C5" in names:
+        cfg = synth.LARGE
+        sets["C5"] = (cfg, [synth.make_layer(cfg, layer=i, device="cuda", T=64)
+                            for i in range(cfg.layers)])
+    torch.cuda.synchronize()
+    print(f"# generated {sorted(names)} on the device in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    return sets
 
 
-def total_bytes(cfg, T, counted):
+def unique_experts(ids_list):
+    return sum(len(set(ids.flatten().tolist())) for ids in ids_list) / len(ids_list)
+
+
+def expert_bytes(cfg, U):
+    return 3 * cfg.I * cfg.H * (2 if cfg.dtype == "bf16" else 4) * U
+
+
+def layer_bytes(cfg, T, U, bias):
+    """Algorithmic bytes of one call: activated experts, router, x, y."""
     elt = 2 if cfg.dtype == "bf16" else 4
-    return counted + cfg.E * cfg.H * 4 + 2 * T * cfg.H * elt
+    return expert_bytes(cfg, U) + cfg.E * cfg.H * 4 + (cfg.E * 4 if bias else 0) + \
+        2 * T * cfg.H * elt
 
 
-PATH_FLAGS = {"auto": 0, "f": 1, "g": 2, "p": 4}
+def expert_flops(cfg, T, k1):
+    return 6.0 * T * k1 * cfg.H * cfg.I
 
 
-def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup, path="auto"):
-    """Graph-capture one pass over the ring and time whole replays."""
+def kernel_work(name, cfg, T, k1, U, bias):
+    """(algorithmic bytes, flops) of one launch of the named kernel."""
+    elt = 2 if cfg.dtype == "bf16" else 4
+    H, E, I = cfg.H, cfg.E, cfg.I
+    router = E * H * 4 + (E * 4 if bias else 0) + T * H * elt
+    gu = 2 * U * I * H * elt
+    dn = U * I * H * elt
+    n = T * k1
+    table = {
+        "b1_front": (router + gu, 2.0 * E * H + 4.0 * n * I * H),
+        "b1_down": (dn + T * H * elt, 2.0 * n * I * H),
+        "router": (router + T * E * 4, 2.0 * T * E * H),
+        "router_route": (router, 2.0 * T * E * H),
+        "gateup": (gu + T * H * elt, 4.0 * n * I * H),
+        "down": (dn, 2.0 * n * I * H),
+        "down_one_token": (dn + H * elt, 2.0 * n * I * H),
+        "fused_decode": (layer_bytes(cfg, T, U, bias), expert_flops(cfg, T, k1)),
+        "router_mma": (router + T * E * 4, 2.0 * T * E * H),
+        "gateup_mma": (gu + T * H * elt, 4.0 * n * I * H),
+        "down_mma": (dn, 2.0 * n * I * H),
+    }
+    return table.get(name, (None, None))
+
+
+# ------------------------------------------------------------------ timing
+def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
+    """Graph-capture one pass over the layers and time whole replays."""
     dev = layers[0]["Wg"].device
     L = len(layers)
     stream = torch.cuda.Stream(device=dev)
     xs = [lay["x"][:T].contiguous() for lay in layers]
     ys = [torch.empty_like(x) for x in xs]
     lib = moe.load_library()
-    nbytes = lib.moe_forward_workspace(T, cfg.H, cfg.E, cfg.I, k1, 1, 1)
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    act = 1 if cfg.dtype == "bf16" else 0
+    ws = torch.zeros(lib.moe_forward_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act),
+                     dtype=torch.uint8, device=dev)
     ids_list = []
 
     def one_pass(record_ids=False):
@@ -83,27 +147,22 @@ def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup, path="auto"):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             one_pass()
-        n_warm = max(1, warmup // L)
-        n_rep = max(1, steps // L)
-        for _ in range(n_warm):
+        for _ in range(max(1, warmup // L)):
             g.replay()
         torch.cuda.synchronize()
-        # replays must reproduce the eager outputs bit for bit
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
+        n_rep = max(1, steps // L)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
-        per_rep = []
         torch.cuda.synchronize()
-        t_wall = time.perf_counter()
         start.record(stream)
         for _ in range(n_rep):
             g.replay()
         stop.record(stream)
         stop.synchronize()
-        t_wall = time.perf_counter() - t_wall
         total_ms = start.elapsed_time(stop)
-        # a few individually timed replays for the spread
+        per_rep = []
         for _ in range(min(20, n_rep)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -115,130 +174,245 @@ def time_cell(moe, torch, layers, cfg, T, k1, k2, steps, warmup, path="auto"):
         torch.cuda.synchronize()
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
-    n_steps = n_rep * L
-    us = total_ms * 1e3 / n_steps
-    counted, uniq = counted_bytes(cfg, ids_list)
+    del g
+    us = total_ms * 1e3 / (n_rep * L)
+    U = unique_experts(ids_list)
+    bias = layers[0]["br"] is not None
     per_rep.sort()
+    counted = expert_bytes(cfg, U)
+    total = layer_bytes(cfg, T, U, bias)
+    flops = expert_flops(cfg, T, k1)
     return {
-        "T": T, "k1": k1, "k2": k2, "path": path, "steps": n_steps,
+        "T": T, "k1": k1, "k2": k2, "path": path, "layers": L, "steps": n_rep * L,
         "us_per_layer": us,
         "us_p10": per_rep[len(per_rep) // 10], "us_p90": per_rep[(9 * len(per_rep)) // 10],
         "tokens_per_s": T / (us * 1e-6),
-        "unique_experts": uniq,
+        "unique_experts": U,
         "counted_bytes": counted,
         "counted_GBps": counted / (us * 1e-6) / 1e9,
         "hbm_frac_counted": counted / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "total_bytes": total_bytes(cfg, T, counted),
-        "wall_s": t_wall,
-        "graph": g, "ws": ws, "ys": ys, "y_eager": y_eager, "ids": ids_list,
+        "total_bytes": total,
+        "hbm_frac_total": total / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "expert_tflops": flops / (us * 1e-6) / 1e12,
+        "mfma_frac": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+        "_ys": ys,
     }
 
 
-def check_parity(moe, torch, oracle, synth, layer, cfg, T, k1, k2, y_dev):
-    """Oracle check of one ring layer: route bit for bit on the GPU logits,
-    y within the bf16 tolerance (host copies of the activated experts only)."""
+def profile_launches(moe, torch, cfg, layers, T, k1, k2, path, n_calls):
+    """Per-launch HIP-event times of one call; then the longest launch timed
+    in every call of an eager pass of n_calls over the layers."""
+    stream = torch.cuda.Stream()
+    xs = [lay["x"][:T].contiguous() for lay in layers]
+    ys = [torch.empty_like(x) for x in xs]
+    lib = moe.load_library()
+    act = 1 if cfg.dtype == "bf16" else 0
+    ws = torch.zeros(lib.moe_forward_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act),
+                     dtype=torch.uint8, device=layers[0]["Wg"].device)
+
+    def call(i):
+        j = i % len(layers)
+        lay = layers[j]
+        moe.forward(xs[j], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
+                    br=lay["br"], out=ys[j], workspace=ws, flags=PATH_FLAGS[path])
+
+    launches = []
+    with torch.cuda.stream(stream):
+        for i in range(3 * len(layers)):
+            call(i)
+        for j in range(16):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            name = ""
+            for i in range(min(len(layers), 16)):
+                moe.profile_launch(j, ev[0], ev[1])
+                call(i)
+                stream.synchronize()
+                name = moe.profile_launch_name()
+                if not name:
+                    break
+                times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            if not name:
+                break
+            times.sort()
+            launches.append({"launch": j, "kernel": name,
+                             "us_median": round(times[len(times) // 2], 3)})
+        dom = max(launches, key=lambda d: d["us_median"])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_calls)]
+        torch.cuda.synchronize()
+        for i in range(n_calls):
+            moe.profile_launch(dom["launch"], evs[i][0], evs[i][1])
+            call(i)
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return launches, dom, sum(per) / len(per)
+
+
+# ------------------------------------------------------------------ checks
+def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok=32):
+    """One layer of the cell against the oracle: ids and weights equal the
+    oracle's route on the GPU's logits bit for bit; y within the bf16
+    tolerance on a token sample (host copies of the activated experts only)."""
     import numpy as np
     x = layer["x"][:T]
     y, lg, ids, w = moe.forward(x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1, k2,
-                                br=layer["br"], return_route=True)
+                                br=layer["br"], return_route=True, flags=PATH_FLAGS[path])
     torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y_dev.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), y_dev.view(torch.int16)), "timed output differs"
     lg_h = lg.cpu().numpy()
     oids, ow = oracle.route(lg_h, k1, k2)
     assert np.array_equal(oids, ids.cpu().numpy()) and \
         np.array_equal(ow.view(np.int32), w.cpu().numpy().view(np.int32)), "route differs"
-    uniq = sorted(set(oids.flatten().tolist()))
-    remap = {e: i for i, e in enumerate(uniq)}
-    sel = torch.tensor(uniq, device=x.device)
+    sel = np.unique(np.linspace(0, T - 1, min(T, n_tok)).astype(int))
+    sids = oids[sel]
+    uniq = np.unique(sids)
+    idx = torch.as_tensor(uniq, dtype=torch.long, device=x.device)
     n = synth.to_numpy
-    Wg, Wu, Wd = (n(layer[k].index_select(0, sel)) for k in ("Wg", "Wu", "Wd"))
-    rids = np.vectorize(remap.get)(oids).astype(np.int32)
-    y_ref = oracle.experts(n(x), Wg, Wu, Wd, rids, ow, nthreads=8)
-    yd = y.float().cpu().numpy().astype(np.float64)
+    Wg, Wu, Wd = (n(layer[k].index_select(0, idx)) for k in ("Wg", "Wu", "Wd"))
+    rids = np.searchsorted(uniq, sids).astype(np.int32)
+    y_ref = oracle.experts(n(x)[sel], Wg, Wu, Wd, rids, ow[sel], nthreads=8)
+    yd = y.float().cpu().numpy().astype(np.float64)[sel]
     err = float((np.abs(yd - y_ref).max(1) / np.abs(y_ref).max(1)).max())
     assert err <= 2e-2, f"normwise error {err}"
     return err
 
 
-def cpu_baseline(oracle, synth, torch, layer, cfg, k1, k2, budget_s=12.0):
+def cpu_baseline(oracle, synth, layer, k1, k2, budget_s=12.0):
     """The oracle as it stands, on host copies of one ring layer, batch 1."""
-    import numpy as np
     n = synth.to_numpy
     host = {k: n(layer[k]) for k in ("Wr", "Wg", "Wu", "Wd")}
     xs = n(layer["x"])
     done, t0 = 0, time.perf_counter()
     while True:
-        x = xs[done % xs.shape[0]:done % xs.shape[0] + 1]
-        oracle.forward(x, host["Wr"], host["Wg"], host["Wu"], host["Wd"], k1, k2, nthreads=1)
+        i = done % xs.shape[0]
+        oracle.forward(xs[i:i + 1], host["Wr"], host["Wg"], host["Wu"], host["Wd"], k1, k2,
+                       nthreads=1)
         done += 1
         el = time.perf_counter() - t0
         if el > budget_s or done >= 400:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} single-token calls (batch 1, k1:k2={k1}:{k2}) of the C oracle on "
-                      f"host copies of one {cfg.name} layer, {el:.1f} s; the oracle threads over "
-                      f"tokens, so a batch of 1 runs on one core"}
+                      f"host copies of one H=2048/E=128/I=768 bf16 layer, {el:.1f} s; the "
+                      f"oracle threads over tokens, so one token runs on one core"}
 
 
+def copy_calibration(torch, nbytes=256 << 20):
+    """A plain device copy of known size (the reference kernel for scaling the
+    FETCH_SIZE / WRITE_SIZE counters) and its bandwidth."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / 10
+    return {"bytes": nbytes, "us": ms * 1e3,
+            "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters, if the stored
+    record is for this kernel and its source is unchanged since."""
+    rec_path = ROOT / "profiles" / "traffic.json"
+    if not rec_path.exists():
+        return None
+    rec = json.loads(rec_path.read_text())
+    if rec.get("kernel") != kernel:
+        return None
+    src = ROOT / rec["source"]
+    if not src.exists() or hashlib.sha256(src.read_bytes()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+# ------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(no multi-GPU path is built)", file=sys.stderr)
+              f"(this build has no multi-GPU path)", file=sys.stderr)
         return 2
     import torch
 
     import decoupled_top_routing_amd as moe
     from decoupled_top_routing_amd import synth
 
-    dev = torch.device("cuda:0")
-    cfg = synth.DECODE_B8        # the batch-1 cells use the first token of each layer
-    t0 = time.perf_counter()
-    layers = []
-    for i in range(args.ring):
-        lay = synth.make_layer(cfg, layer=i, device="cuda")
-        layers.append(lay)
-    torch.cuda.synchronize()
-    print(f"# generated {args.ring} layers of {cfg.name} on the device in "
-          f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-
-    cells = []
+    specs = []
     for spec in args.cells.split(","):
         parts = spec.split(":")
-        b, k1, k2 = parts[:3]
-        path = parts[3] if len(parts) > 3 else "auto"
-        T, k1, k2 = int(b[1:]), int(k1), int(k2)
-        c = time_cell(moe, torch, layers, cfg, T, k1, k2, args.steps, args.warmup, path)
-        print(f"# cell b{T} {k1}:{k2} [{path}]: {c['us_per_layer']:.2f} us/layer "
+        specs.append((parts[0], int(parts[1]), int(parts[2]), int(parts[3]),
+                      parts[4] if len(parts) > 4 else "auto"))
+    sets = make_sets(synth, torch, {s[0] for s in specs}, args.ring)
+
+    cells = []
+    for idx, (name, T, k1, k2, path) in enumerate(specs):
+        cfg, layers = sets[name]
+        if name == "C4":
+            steps = 50
+        elif name == "C5":
+            steps = len(layers) * (20 if T > 1 else 40)
+        else:
+            steps = args.steps if idx == 0 else min(args.steps, 50 * len(layers))
+        c = time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps,
+                      args.warmup if idx == 0 else min(args.warmup, 4 * len(layers)))
+        c["config"] = name
+        print(f"# {name} b{T} {k1}:{k2} [{path}]: {c['us_per_layer']:.2f} us/layer "
               f"({c['us_p10']:.2f}-{c['us_p90']:.2f}), {c['tokens_per_s']:.0f} tok/s, "
               f"{c['counted_GBps']:.0f} GB/s counted ({100 * c['hbm_frac_counted']:.1f}% of HBM), "
-              f"U={c['unique_experts']:.1f}", file=sys.stderr, flush=True)
+              f"{c['expert_tflops']:.1f} TFLOP/s, U={c['unique_experts']:.1f}",
+              file=sys.stderr, flush=True)
         cells.append(c)
 
-    head = cells[0]
     import oracle
-    errs = []
-    for c in cells:
-        errs.append(check_parity(moe, torch, oracle, synth, layers[0], cfg, c["T"], c["k1"],
-                                 c["k2"], c["ys"][0]))
+    for (name, T, k1, k2, path), c in zip(specs, cells):
+        _, layers = sets[name]
+        c["parity_normwise_err"] = check_parity(moe, torch, oracle, synth, layers[0], T, k1, k2,
+                                                path, c["_ys"][0],
+                                                n_tok=4 if name == "C5" else 32)
+    print("# parity: every cell matches the oracle", file=sys.stderr, flush=True)
+
+    head = cells[0]
+    hname, hT, hk1, hk2, hpath = specs[0]
+    hcfg, hlayers = sets[hname]
+    launches, dom, dom_us = profile_launches(moe, torch, hcfg, hlayers, hT, hk1, hk2, hpath,
+                                             min(args.steps, 50 * len(hlayers)))
+    bias = hlayers[0]["br"] is not None
+    dom_bytes, _ = kernel_work(dom["kernel"], hcfg, hT, hk1, head["unique_experts"], bias)
+    print(f"# launches {launches}; dominant {dom['kernel']}: {dom_us:.2f} us per launch",
+          file=sys.stderr, flush=True)
+    calib = copy_calibration(torch)
+
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(oracle, synth, torch, layers[0], cfg, head["k1"], head["k2"])
+        cpu = cpu_baseline(oracle, synth, hlayers[0], hk1, hk2)
 
-    def find(T, k1, k2):
-        for c in cells:
-            if (c["T"], c["k1"], c["k2"], c["path"]) == (T, k1, k2, "auto"):
+    def find(cfgname, T, k1, k2):
+        for (n_, T_, a_, b_, p_), c in zip(specs, cells):
+            if (n_, T_, a_, b_, p_) == (cfgname, T, k1, k2, "auto"):
                 return c
         return None
 
     ratios = {}
-    for T in (1, 8):
-        a, b = find(T, 4, 16), find(T, 8, 8)
+    for cfgname, T in (("C2", 1), ("C3", 8)):
+        a, b = find(cfgname, T, 4, 16), find(cfgname, T, 8, 8)
         if a and b:
             ratios[f"b{T}_4:16_over_8:8"] = b["us_per_layer"] / a["us_per_layer"]
 
     us = head["us_per_layer"]
-    achieved = head["counted_bytes"] / (us * 1e-6) / 1e9
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
+    roofline = {
+        "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS if achieved else None,
+        "traffic": traffic_record(dom["kernel"]),
+        "kernel": dom["kernel"], "us_per_launch": dom_us,
+        "algorithmic_bytes_per_launch": dom_bytes,
+        "launches": launches,
+    }
     out = {
         "metric": "MoE-layer tokens/s + % HBM peak at batch 1/8, k1:k2 4:16 vs 8:8",
         "value": head["tokens_per_s"],
@@ -253,25 +427,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded Gaussian layers generated on the device",
         "config": {
-            "workload": f"decode batch {head['T']}, H={cfg.H} E={cfg.E} I={cfg.I} bf16 "
-                        f"experts, k1:k2={head['k1']}:{head['k2']}, cold ring of "
-                        f"{args.ring} layers replayed from one HIP graph",
-            "global_batch": head["T"], "ring_layers": args.ring,
+            "workload": f"decode batch {hT}, H={hcfg.H} E={hcfg.E} I={hcfg.I} bf16 experts, "
+                        f"k1:k2={hk1}:{hk2}, cold ring of {len(hlayers)} layers replayed from "
+                        f"one HIP graph",
+            "global_batch": hT, "ring_layers": len(hlayers),
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "whole layer (all kernels of one moe_forward call)",
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
+        "copy_calibration": calib,
         "cells": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()
-                   if k not in ("graph", "ws", "ys", "y_eager", "ids")} for c in cells],
+                   if not k.startswith("_")} for c in cells],
         "ratios": ratios,
-        "parity_normwise_err": errs,
     }
     print(json.dumps(out))
     return 0

@@ -69,6 +69,9 @@ def load_library():
         lib.moe_forward.restype = ctypes.c_int
         lib.moe_forward.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
                                     i32, P, P, P, P, u32, P, ctypes.c_size_t, P]
+        lib.moe_profile_launch.restype = ctypes.c_int
+        lib.moe_profile_launch.argtypes = [i32, P, P]
+        lib.moe_profile_launch_name.restype = ctypes.c_char_p
         if lib.moe_abi_version() != ABI_VERSION:
             raise MoeError(-1, f"libmoe ABI {lib.moe_abi_version()} != {ABI_VERSION}")
         _lib = lib
@@ -116,6 +119,23 @@ def route(logits: torch.Tensor, k1: int, k2: int):
     _check(lib.moe_route(_ptr(logits), T, E, k1, k2, _ptr(ids), _ptr(w),
                          _stream(logits.device)))
     return ids, w
+
+
+def profile_launch(launch: int, start, stop):
+    """Arm the next forward() on this thread to record the torch.cuda.Event
+    objects start and stop (timing enabled) right before and right after its
+    kernel launch number `launch` (moe_profile_launch)."""
+    lib = load_library()
+    for ev in (start, stop):
+        if ev.cuda_event == 0:
+            ev.record()  # creates the event; the library records it again
+    _check(lib.moe_profile_launch(launch, ctypes.c_void_p(start.cuda_event),
+                                  ctypes.c_void_p(stop.cuda_event)))
+
+
+def profile_launch_name() -> str:
+    """Kernel name of the launch bracketed by the last armed forward()."""
+    return load_library().moe_profile_launch_name().decode()
 
 
 # One zero-filled workspace per (device, stream), grown on demand.  The

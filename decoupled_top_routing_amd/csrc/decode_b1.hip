@@ -339,11 +339,11 @@ static void launch_front_v(b1::Args &a, int nchr, int nch, hipStream_t s) {
 }
 
 template <typename WT, typename XT>
-hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
-                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
-                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
-                            int32_t *sync, char *tagged, int32_t *ids, float *w, int32_t *plan,
-                            float *abuf, hipStream_t s) {
+hipError_t launch_decode_b1_front(const XT *x, int H, const float *Wr, const float *br, int E,
+                                  const WT *Wg, const WT *Wu, int I, int k1, int k2,
+                                  float *logits_out, int32_t *ids_out, float *w_out,
+                                  int32_t *sync, char *tagged, int32_t *ids, float *w,
+                                  int32_t *plan, float *abuf, hipStream_t s) {
   b1::Args a;
   int64_t tp_off = 0, tp_rep = 0;
   decode_b1_tagged_bytes(E, k1, &tp_off, &tp_rep);
@@ -377,8 +377,13 @@ hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br
   else if (E <= 256) launch_front_v<WT, XT, 4>(a, nchr, nch, s);
   else if (E <= 512) launch_front_v<WT, XT, 8>(a, nchr, nch, s);
   else launch_front_v<WT, XT, 16>(a, nchr, nch, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <typename WT, typename XT>
+hipError_t launch_decode_b1_down(const WT *Wd, int H, int I, int k1, const int32_t *plan,
+                                 const float *abuf, XT *y, int32_t *sync, hipStream_t s) {
+  constexpr int esz = sizeof(WT);
   const int ncd = (I * esz / 16 + kWave - 1) / kWave;
   const dim3 grid((unsigned)((H + b1::kWaves - 1) / b1::kWaves)), block(b1::kThreads);
   if (ncd == 1)
@@ -388,17 +393,14 @@ hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br
   return hipGetLastError();
 }
 
-template hipError_t launch_decode_b1<float, float>(const float *, int, const float *,
-                                                   const float *, int, const float *,
-                                                   const float *, const float *, int, int, int,
-                                                   float *, float *, int32_t *, float *,
-                                                   int32_t *, char *, int32_t *, float *,
-                                                   int32_t *, float *, hipStream_t);
-template hipError_t launch_decode_b1<bf16_t, bf16_t>(const bf16_t *, int, const float *,
-                                                     const float *, int, const bf16_t *,
-                                                     const bf16_t *, const bf16_t *, int, int,
-                                                     int, bf16_t *, float *, int32_t *, float *,
-                                                     int32_t *, char *, int32_t *, float *,
-                                                     int32_t *, float *, hipStream_t);
+#define MOE_INST_B1(WT, XT)                                                                    \
+  template hipError_t launch_decode_b1_front<WT, XT>(                                         \
+      const XT *, int, const float *, const float *, int, const WT *, const WT *, int, int, int, \
+      float *, int32_t *, float *, int32_t *, char *, int32_t *, float *, int32_t *, float *,    \
+      hipStream_t);                                                                            \
+  template hipError_t launch_decode_b1_down<WT, XT>(const WT *, int, int, int, const int32_t *, \
+                                                    const float *, XT *, int32_t *, hipStream_t);
+MOE_INST_B1(float, float)
+MOE_INST_B1(bf16_t, bf16_t)
 
 }  // namespace moe

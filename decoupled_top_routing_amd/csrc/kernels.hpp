@@ -66,17 +66,21 @@ hipError_t launch_router_route(const XT *x, int H, const float *Wr, const float 
 bool decode_b1_supported(int H, int I, int k1, bool bf16);
 size_t decode_b1_tagged_bytes(int E, int k1, int64_t *tp_offset, int64_t *tp_rep_words);
 template <typename WT, typename XT>
-hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
-                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
-                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
-                            int32_t *sync, char *tagged, int32_t *ids, float *w, int32_t *plan,
-                            float *abuf, hipStream_t s);
+hipError_t launch_decode_b1_front(const XT *x, int H, const float *Wr, const float *br, int E,
+                                  const WT *Wg, const WT *Wu, int I, int k1, int k2,
+                                  float *logits_out, int32_t *ids_out, float *w_out,
+                                  int32_t *sync, char *tagged, int32_t *ids, float *w,
+                                  int32_t *plan, float *abuf, hipStream_t s);
+template <typename WT, typename XT>
+hipError_t launch_decode_b1_down(const WT *Wd, int H, int I, int k1, const int32_t *plan,
+                                 const float *abuf, XT *y, int32_t *sync, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);
 size_t prefill_plan_words(int64_t n, int E);
-hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const float *Wr,
-                             const float *br, int E, uint16_t *w3, float *logits, float *logits2,
+hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipStream_t s);
+hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3,
+                             const float *br, int E, float *logits, float *logits2,
                              hipStream_t s);
 hipError_t launch_prefill_plan(const int32_t *ids, int64_t n, int E, int32_t *plan,
                                hipStream_t s);

@@ -138,10 +138,45 @@ size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k
   return c > a ? c : a;
 }
 
+// ---- launches of one moe_forward call, with the profiling aid of
+// moe_profile_launch: the armed launch is bracketed by two events.
+thread_local int g_prof_launch = -1;
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+thread_local char g_prof_name[64] = "";
+
+struct Launches {
+  hipStream_t s;
+  int n, prof;
+  hipEvent_t start, stop;
+  explicit Launches(hipStream_t st) : s(st), n(0), prof(g_prof_launch), start(g_prof_start),
+                                      stop(g_prof_stop) {
+    g_prof_launch = -1;  // one call only
+    g_prof_name[0] = 0;
+  }
+  template <typename F>
+  int operator()(const char *name, F &&launch) {
+    const bool p = n == prof && start && stop;
+    if (p && hipEventRecord(start, s) != hipSuccess) return hip_fail(hipGetLastError(), "event");
+    const hipError_t e = launch();
+    if (p) {
+      if (hipEventRecord(stop, s) != hipSuccess) return hip_fail(hipGetLastError(), "event");
+      snprintf(g_prof_name, sizeof g_prof_name, "%s", name);
+    }
+    ++n;
+    return e == hipSuccess ? MOE_OK : hip_fail(e, name);
+  }
+};
+
+#define RUN(name, expr)                               \
+  do {                                                \
+    const int rc_ = run(name, [&] { return (expr); }); \
+    if (rc_ != MOE_OK) return rc_;                    \
+  } while (0)
+
 int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, const float *br,
                     int32_t E, const uint16_t *Wg, const uint16_t *Wu, const uint16_t *Wd,
                     int32_t I, int32_t k1, int32_t k2, uint16_t *y, float *logits_out,
-                    int32_t *ids_out, float *w_out, char *ws, hipStream_t s) {
+                    int32_t *ids_out, float *w_out, char *ws, Launches &run) {
   const PrefillLayout L = prefill_layout(T, H, E, I, k1);
   float *logits = reinterpret_cast<float *>(ws + L.logits);
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
@@ -151,20 +186,15 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, co
   uint16_t *abf = reinterpret_cast<uint16_t *>(ws + L.abf);
   uint16_t *zbf = reinterpret_cast<uint16_t *>(ws + L.zbf);
   const int64_t n = T * k1;
-  hipError_t e;
-  if ((e = moe::launch_router_mma(x, T, H, Wr, br, E, w3, logits, logits_out, s)) != hipSuccess)
-    return hip_fail(e, "router kernel");
-  if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr, nullptr,
-                                  s)) != hipSuccess)
-    return hip_fail(e, "route kernel");
-  if ((e = moe::launch_prefill_plan(ids, n, E, plan, s)) != hipSuccess)
-    return hip_fail(e, "plan kernel");
-  if ((e = moe::launch_gateup_mma(x, H, Wg, Wu, I, plan, E, n, k1, w, abf, s)) != hipSuccess)
-    return hip_fail(e, "gate/up kernel");
-  if ((e = moe::launch_down_mma(abf, H, Wd, I, plan, E, n, zbf, s)) != hipSuccess)
-    return hip_fail(e, "down kernel");
-  if ((e = moe::launch_combine_bf16(zbf, T, H, k1, y, s)) != hipSuccess)
-    return hip_fail(e, "combine kernel");
+  const hipStream_t s = run.s;
+  RUN("split_router", moe::launch_split_router(Wr, E, H, w3, s));
+  RUN("router_mma", moe::launch_router_mma(x, T, H, w3, br, E, logits, logits_out, s));
+  RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
+                                      nullptr, s));
+  RUN("prefill_plan", moe::launch_prefill_plan(ids, n, E, plan, s));
+  RUN("gateup_mma", moe::launch_gateup_mma(x, H, Wg, Wu, I, plan, E, n, k1, w, abf, s));
+  RUN("down_mma", moe::launch_down_mma(abf, H, Wd, I, plan, E, n, zbf, s));
+  RUN("combine", moe::launch_combine_bf16(zbf, T, H, k1, y, s));
   return MOE_OK;
 }
 
@@ -172,20 +202,20 @@ template <typename WT, typename XT>
 int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const float *br, int32_t E,
                   const WT *Wg, const WT *Wu, const WT *Wd, int32_t I, int32_t k1, int32_t k2,
                   XT *y, float *logits_out, int32_t *ids_out, float *w_out, Path path,
-                  char *ws, const Layout &L, hipStream_t s) {
-  hipError_t e;
+                  char *ws, const Layout &L, Launches &run) {
+  const hipStream_t s = run.s;
   if constexpr (sizeof(WT) == 2) {
     if (path == Path::Prefill)
       return forward_prefill(reinterpret_cast<const uint16_t *>(x), T, H, Wr, br, E,
                              reinterpret_cast<const uint16_t *>(Wg),
                              reinterpret_cast<const uint16_t *>(Wu),
                              reinterpret_cast<const uint16_t *>(Wd), I, k1, k2,
-                             reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, s);
+                             reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, run);
   }
   if (path == Path::Fused) {
-    if ((e = moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
-                                              logits_out, ids_out, w_out, ws, s)) != hipSuccess)
-      return hip_fail(e, "fused decode kernel");
+    RUN("fused_decode", (moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1,
+                                                          k2, y, logits_out, ids_out, w_out, ws,
+                                                          s)));
     return MOE_OK;
   }
   float *logits = reinterpret_cast<float *>(ws + L.logits);
@@ -194,50 +224,43 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
   float *abuf = reinterpret_cast<float *>(ws + L.abuf);
   float *zbuf = reinterpret_cast<float *>(ws + L.zbuf);
+  int32_t *sync = reinterpret_cast<int32_t *>(ws);
   const int64_t n_assign = T * k1;
-  int32_t *ticket = reinterpret_cast<int32_t *>(ws) + moe::kRouteTicketWord;
+  int32_t *ticket = sync + moe::kRouteTicketWord;
   if (T == 1 && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2)) {
-    if ((e = moe::launch_decode_b1<WT, XT>(
-             x, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y, logits_out, ids_out, w_out,
-             reinterpret_cast<int32_t *>(ws), ws + L.tagged, ids, w, plan, abuf, s)) != hipSuccess)
-      return hip_fail(e, "one-token kernels");
+    RUN("b1_front", (moe::launch_decode_b1_front<WT, XT>(x, H, Wr, br, E, Wg, Wu, I, k1, k2,
+                                                         logits_out, ids_out, w_out, sync,
+                                                         ws + L.tagged, ids, w, plan, abuf, s)));
+    RUN("b1_down", (moe::launch_decode_b1_down<WT, XT>(Wd, H, I, k1, plan, abuf, y, sync, s)));
     return MOE_OK;
   }
   if (T == 1 && moe::router_route_supported(H)) {
-    if ((e = moe::launch_router_route<XT>(x, H, Wr, br, E, k1, k2, logits, logits_out, ids, w,
-                                          ids_out, w_out, plan, ticket, s)) != hipSuccess)
-      return hip_fail(e, "router kernel");
-    if (n_assign > 64 && (e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
-      return hip_fail(e, "plan kernel");
-  } else if ((e = moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s)) !=
-             hipSuccess) {
-    return hip_fail(e, "router kernel");
-  } else if (n_assign <= 64) {
-    if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, plan, ticket,
-                                    s)) != hipSuccess)
-      return hip_fail(e, "route kernel");
+    RUN("router_route", moe::launch_router_route<XT>(x, H, Wr, br, E, k1, k2, logits, logits_out,
+                                                     ids, w, ids_out, w_out, plan, ticket, s));
+    if (n_assign > 64) RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
   } else {
-    if ((e = moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
-                                    nullptr, s)) != hipSuccess)
-      return hip_fail(e, "route kernel");
-    if ((e = moe::launch_plan(ids, n_assign, E, plan, s)) != hipSuccess)
-      return hip_fail(e, "plan kernel");
+    RUN("router", moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s));
+    if (n_assign <= 64) {
+      RUN("route_plan", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, plan,
+                                               ticket, s));
+    } else {
+      RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
+                                          nullptr, s));
+      RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
+    }
   }
-  if ((e = moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)) !=
-      hipSuccess)
-    return hip_fail(e, "gate/up kernel");
+  RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)));
   const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
   if (T == 1 && ncd <= 2) {
-    if ((e = moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)) != hipSuccess)
-      return hip_fail(e, "down kernel");
+    RUN("down_one_token", (moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)));
     return MOE_OK;
   }
-  if ((e = moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s)) != hipSuccess)
-    return hip_fail(e, "down kernel");
-  if ((e = moe::launch_combine<XT>(zbuf, T, H, k1, y, s)) != hipSuccess)
-    return hip_fail(e, "combine kernel");
+  RUN("down", moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s));
+  RUN("combine", moe::launch_combine<XT>(zbuf, T, H, k1, y, s));
   return MOE_OK;
 }
+
+#undef RUN
 
 }  // namespace
 
@@ -316,18 +339,28 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
                 need, workspace_bytes, workspace);
   Path path;
   if ((rc = choose_path(T, H, E, I, k1, b16, flags, &path)) != MOE_OK) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  Launches run((hipStream_t)stream);
   char *ws = static_cast<char *>(workspace);
   if (f32)
     return forward_typed<float, float>(
         static_cast<const float *>(x), T, H, Wr, br, E, static_cast<const float *>(Wgate),
         static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2,
-        static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, s);
+        static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
   return forward_typed<moe::bf16_t, moe::bf16_t>(
       static_cast<const moe::bf16_t *>(x), T, H, Wr, br, E,
       static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
       static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, static_cast<moe::bf16_t *>(y),
-      logits_out, ids_out, w_out, path, ws, L, s);
+      logits_out, ids_out, w_out, path, ws, L, run);
 }
+
+int moe_profile_launch(int32_t launch, void *start, void *stop) {
+  if (launch < 0) return fail(MOE_EINVAL, "launch=%d < 0", launch);
+  g_prof_launch = launch;
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
+  return MOE_OK;
+}
+
+const char *moe_profile_launch_name(void) { return g_prof_name; }
 
 }  // extern "C"

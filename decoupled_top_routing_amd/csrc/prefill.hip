@@ -378,11 +378,15 @@ bool prefill_supported(int H, int I, bool bf16) {
 
 size_t prefill_plan_words(int64_t n, int E) { return 4 + 3 * (size_t)E + 2 + (size_t)n; }
 
-hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const float *Wr,
-                             const float *br, int E, uint16_t *w3, float *logits, float *logits2,
-                             hipStream_t s) {
+hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipStream_t s) {
   const int64_t n = (int64_t)E * H;
   pf::split_router_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(Wr, n, w3);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3,
+                             const float *br, int E, float *logits, float *logits2,
+                             hipStream_t s) {
   const int64_t tiles = ((T + pf::BM - 1) / pf::BM) * ((E + pf::BN - 1) / pf::BN);
   pf::router_mma_kernel<<<dim3((unsigned)tiles), dim3(pf::kThreads), 0, s>>>(x, T, H, w3, br, E,
                                                                              logits, logits2);

@@ -145,6 +145,20 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
                 uint32_t flags, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/*
+ * moe_profile_launch -- profiling aid; changes no output.  Arms the NEXT
+ * moe_forward call on the calling thread: it records the hipEvent_t `start`
+ * on its stream immediately before its kernel launch number `launch` (0 =
+ * the call's first launch) and `stop` immediately after it, then disarms.
+ * A call with fewer launches records nothing.  start and stop are created and
+ * owned by the caller (NULL disarms).  Returns MOE_EINVAL for launch < 0.
+ *
+ * moe_profile_launch_name -- the kernel name of the launch bracketed by the
+ * last armed call on this thread ("" if none was), e.g. "b1_front".
+ */
+int moe_profile_launch(int32_t launch, void *start, void *stop);
+const char *moe_profile_launch_name(void);
+
 #ifdef __cplusplus
 }
 #endif
