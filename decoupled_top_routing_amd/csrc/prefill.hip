@@ -13,11 +13,12 @@
 // Every product is "NT": both operands are stored K-contiguous (x and a rows
 // along H / I, weight rows along H / I), which is the layout the MFMA
 // operands want.  One tile engine serves all three GEMMs:
-//   block = 256 threads = 4 waves in a 2x2 grid, tile BM x BN = 128 x 128,
-//   K step 32 bf16; each wave owns a 64 x 64 sub-tile = 2 x 2 MFMA 32x32x16
-//   (v_mfma_f32_32x32x16_bf16) accumulators; A and B K-slices are staged in
-//   LDS (double buffered, rows padded by 16 bytes), the next slice's global
-//   loads are in flight while the current one is multiplied.
+//   block = 256 threads = 4 waves in a 2x2 grid, tile BM x BN (128 x 128 for
+//   the expert GEMMs, 64 x 64 for the router), K step 64 bf16; each wave owns
+//   a (BM/2) x (BN/2) sub-tile of MFMA 32x32x16 (v_mfma_f32_32x32x16_bf16)
+//   accumulators; A and B K-slices are staged in LDS (double buffered, rows
+//   padded by 16 bytes), the next slice's global loads are in flight while
+//   the current one is multiplied.
 // Lane layouts of v_mfma_f32_32x32x16_bf16 (checked on the device): lane l
 // holds A row l%32 and B column l%32, k = 8*(l/32) .. +7; accumulator r of
 // lane l is row (r/4)*8 + (l/32)*4 + r%4, column l%32.
@@ -28,65 +29,76 @@ namespace moe {
 namespace pf {
 
 constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BK = 64;
 constexpr int LDS_ROW = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+constexpr int GM = 128, GN = 128;  // tile of the expert GEMMs
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+template <int BM, int BN>
 struct Tile {
   uint16_t a[2][BM][LDS_ROW];
   uint16_t b[2][BN][LDS_ROW];
 };
 
-// Per thread: 2 of the 512 A chunks (16 B) and 2 of the 512 B chunks of one
-// K slice.  Chunk c: row c / 4, k offset (c % 4) * 8.
+// One K slice of A (BM x BK) and B (BN x BK) is BM*8 + BN*8 chunks of 16 B;
+// chunk i*256 + t of an operand is row i*32 + t/8, k offset (t%8)*8, so eight
+// consecutive threads read one row's 128 contiguous bytes.
+template <int BM, int BN>
 struct Loader {
-  const uint16_t *arow[2];
-  const uint16_t *brow[2];
-  int r[2], q[2];
-  uint4 ra[2], rb[2];
+  static constexpr int NA = BM / 32, NB = BN / 32;
+  const uint16_t *arow[NA];
+  const uint16_t *brow[NB];
+  uint4 ra[NA], rb[NB];
 
+  __device__ static int row(int i) { return i * 32 + (threadIdx.x >> 3); }
   __device__ void fetch(int k0) {
+    const int q = (threadIdx.x & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = ld16(arow[i] + k0 + q[i] * 8);
-      rb[i] = ld16_stream(brow[i] + k0 + q[i] * 8);
-    }
+    for (int i = 0; i < NA; ++i) ra[i] = ld16(arow[i] + k0 + q);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) rb[j] = ld16_stream(brow[j] + k0 + q);
   }
-  __device__ void store(Tile &T, int buf) {
+  __device__ void store(Tile<BM, BN> &T, int buf) {
+    const int q = (threadIdx.x & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4 *>(&T.a[buf][r[i]][q[i] * 8]) = ra[i];
-      *reinterpret_cast<uint4 *>(&T.b[buf][r[i]][q[i] * 8]) = rb[i];
-    }
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4 *>(&T.a[buf][row(i)][q]) = ra[i];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) *reinterpret_cast<uint4 *>(&T.b[buf][row(j)][q]) = rb[j];
   }
 };
 
-// acc[i][j] += A(wave rows i) * B(wave cols j)^T over one K slice in LDS.
-__device__ __forceinline__ void mma_slice(const Tile &T, int buf, int wm, int wn,
-                                          f32x16_t (&acc)[2][2]) {
+// acc[i][j] += A(wave rows i) * B(wave cols j)^T over one K slice in LDS;
+// the 2x2 waves own (BM/2) x (BN/2) sub-tiles of 32x32 MFMA blocks.
+template <int BM, int BN>
+__device__ __forceinline__ void mma_slice(const Tile<BM, BN> &T, int buf, int wm, int wn,
+                                          f32x16_t (&acc)[BM / 64][BN / 64]) {
+  constexpr int MI = BM / 64, NI = BN / 64;
   const int l = lane_id();
   const int lr = l & 31, lk = (l >> 5) * 8;
 #pragma unroll
   for (int ks = 0; ks < BK; ks += 16) {
-    bf16x8_t af[2], bf[2];
+    bf16x8_t af[MI], bf[NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      af[i] = *reinterpret_cast<const bf16x8_t *>(&T.a[buf][wm * 64 + i * 32 + lr][ks + lk]);
+    for (int i = 0; i < MI; ++i)
+      af[i] = *reinterpret_cast<const bf16x8_t *>(&T.a[buf][wm * (BM / 2) + i * 32 + lr][ks + lk]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      bf[j] = *reinterpret_cast<const bf16x8_t *>(&T.b[buf][wn * 64 + j * 32 + lr][ks + lk]);
+    for (int j = 0; j < NI; ++j)
+      bf[j] = *reinterpret_cast<const bf16x8_t *>(&T.b[buf][wn * (BN / 2) + j * 32 + lr][ks + lk]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
 }
 
-// Full K loop with double buffering.  K is a multiple of BK.
-__device__ void mma_k_loop(Tile &T, Loader &ld, int K, int wm, int wn, f32x16_t (&acc)[2][2]) {
+// Full K loop, double buffered in LDS: the next slice's global loads are in
+// flight while the current slice is multiplied.  K is a multiple of BK.
+template <int BM, int BN>
+__device__ void mma_k_loop(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm, int wn,
+                           f32x16_t (&acc)[BM / 64][BN / 64]) {
   const int nk = K / BK;
   ld.fetch(0);
   ld.store(T, 0);
@@ -94,24 +106,26 @@ __device__ void mma_k_loop(Tile &T, Loader &ld, int K, int wm, int wn, f32x16_t 
   for (int kk = 0; kk < nk; ++kk) {
     const int buf = kk & 1;
     if (kk + 1 < nk) ld.fetch((kk + 1) * BK);
-    mma_slice(T, buf, wm, wn, acc);
+    mma_slice<BM, BN>(T, buf, wm, wn, acc);
     if (kk + 1 < nk) ld.store(T, buf ^ 1);
     __syncthreads();
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
+template <int MI, int NI>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[MI][NI]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// row (within the 128-row tile) of accumulator element r of block (i, .)
+// row (within the BM-row tile) of accumulator element r of MFMA block (i, .)
+template <int BM>
 __device__ __forceinline__ int acc_row(int wm, int i, int r) {
-  return wm * 64 + i * 32 + (r >> 2) * 8 + (lane_id() >> 5) * 4 + (r & 3);
+  return wm * (BM / 2) + i * 32 + (r >> 2) * 8 + (lane_id() >> 5) * 4 + (r & 3);
 }
 
 // ------------------------------------------------------------------ plan
@@ -139,7 +153,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
   for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
   const int c = tid < E ? cnt[tid] : 0;
-  int v[3] = {c > 0 ? 1 : 0, c, (c + BM - 1) / BM};
+  int v[3] = {c > 0 ? 1 : 0, c, (c + GM - 1) / GM};
   int inc[3] = {v[0], v[1], v[2]};
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -182,20 +196,33 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
   }
 }
 
-// Locate M tile `mt` of the batch: unique expert u (binary search over
-// mt_off) and the first row of the tile within u's list.
-__device__ __forceinline__ void locate_tile(const int32_t *mt_off, int U, int mt, int *u_out,
-                                            int *row0) {
+// Work tile j of the G = (M tiles) x NT tiles of a grouped GEMM, ordered
+// (unique expert u, N tile, M tile of u): the M tiles of one expert that
+// share an N tile (the same weight rows) are consecutive.  Blocks are handed
+// to the 8 XCDs round-robin by index, so block b runs on XCD b % 8; XCD x
+// takes the contiguous range of j starting at x * ceil(G / 8), and tiles
+// that share weight rows run together on one XCD and share them through its
+// L2.  Returns false for blocks beyond G.
+__device__ bool tile_of(int b, const int32_t *mt_off, int U, int n_mt, int NT, int *u_out,
+                        int *nt_out, int *mt_out) {
+  const int G = n_mt * NT;
+  const int per = (G + 7) / 8;
+  const int slot = b >> 3, j = (b & 7) * per + slot;
+  if (slot >= per || j >= G) return false;
   int lo = 0, hi = U - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (mt_off[mid] <= mt)
+    if (mt_off[mid] * NT <= j)
       lo = mid;
     else
       hi = mid - 1;
   }
+  const int r = j - mt_off[lo] * NT;
+  const int nmt = mt_off[lo + 1] - mt_off[lo];
   *u_out = lo;
-  *row0 = (mt - mt_off[lo]) * BM;
+  *nt_out = r / nmt;
+  *mt_out = mt_off[lo] + r % nmt;
+  return true;
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -207,42 +234,41 @@ __global__ __launch_bounds__(kThreads) void gateup_mma_kernel(
     const uint16_t *__restrict__ x, int H, const uint16_t *__restrict__ Wg,
     const uint16_t *__restrict__ Wu, int I, const int32_t *__restrict__ plan, int E, int k1,
     const float *__restrict__ w, uint16_t *__restrict__ abf) {
-  __shared__ Tile T;
-  const int n_nt = I / 64;
-  const int mt = blockIdx.x / n_nt, nt = blockIdx.x - mt * n_nt;
+  __shared__ Tile<GM, GN> T;
   const int U = plan[0];
-  if (mt >= plan[1]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
   const int32_t *mt_off = off + E + 1;
   const int32_t *list = mt_off + E + 1;
-  int u, row0;
-  locate_tile(mt_off, U, mt, &u, &row0);
+  int u, nt, mt;
+  if (!tile_of(blockIdx.x, mt_off, U, plan[1], I / 64, &u, &nt, &mt)) return;
   const int e = uniq[u];
   const int lb = off[u], n_e = off[u + 1] - lb;
+  const int row0 = (mt - mt_off[u]) * GM;
   const int c0 = nt * 64;
   const int tid = threadIdx.x, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  Loader ld;
+  Loader<GM, GN> ld;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = tid * 2 + i;
-    ld.r[i] = ch >> 2;
-    ld.q[i] = ch & 3;
-    const int m = min(row0 + ld.r[i], n_e - 1);
+  for (int i = 0; i < Loader<GM, GN>::NA; ++i) {
+    const int m = min(row0 + Loader<GM, GN>::row(i), n_e - 1);
     ld.arow[i] = x + (int64_t)(list[lb + m] / k1) * H;
-    const int g = ld.r[i] >> 6, within = ld.r[i] & 63;
+  }
+#pragma unroll
+  for (int j = 0; j < Loader<GM, GN>::NB; ++j) {
+    const int rr = Loader<GM, GN>::row(j);
+    const int g = rr >> 6, within = rr & 63;
     const int cc = c0 + g * 32 + (within & 31);
-    ld.brow[i] = (within < 32 ? Wg : Wu) + ((int64_t)e * I + cc) * H;
+    ld.brow[j] = (within < 32 ? Wg : Wu) + ((int64_t)e * I + cc) * H;
   }
   f32x16_t acc[2][2];
   zero_acc(acc);
-  mma_k_loop(T, ld, H, wm, wn, acc);
+  mma_k_loop<GM, GN>(T, ld, H, wm, wn, acc);
   const int c = c0 + wn * 32 + (lane_id() & 31);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = row0 + acc_row(wm, i, r);
+      const int m = row0 + acc_row<GM>(wm, i, r);
       if (m < n_e) {
         const int asg = list[lb + m];
         const float a = silu(acc[i][0][r]) * acc[i][1][r] * w[asg];
@@ -258,39 +284,36 @@ __global__ __launch_bounds__(kThreads) void gateup_mma_kernel(
 __global__ __launch_bounds__(kThreads) void down_mma_kernel(
     const uint16_t *__restrict__ abf, int H, const uint16_t *__restrict__ Wd, int I,
     const int32_t *__restrict__ plan, int E, uint16_t *__restrict__ zbf) {
-  __shared__ Tile T;
-  const int n_nt = H / BN;
-  const int mt = blockIdx.x / n_nt, nt = blockIdx.x - mt * n_nt;
+  __shared__ Tile<GM, GN> T;
   const int U = plan[0];
-  if (mt >= plan[1]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
   const int32_t *mt_off = off + E + 1;
   const int32_t *list = mt_off + E + 1;
-  int u, row0;
-  locate_tile(mt_off, U, mt, &u, &row0);
+  int u, nt, mt;
+  if (!tile_of(blockIdx.x, mt_off, U, plan[1], H / GN, &u, &nt, &mt)) return;
   const int e = uniq[u];
   const int lb = off[u], n_e = off[u + 1] - lb;
-  const int h0 = nt * BN;
+  const int row0 = (mt - mt_off[u]) * GM;
+  const int h0 = nt * GN;
   const int tid = threadIdx.x, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  Loader ld;
+  Loader<GM, GN> ld;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = tid * 2 + i;
-    ld.r[i] = ch >> 2;
-    ld.q[i] = ch & 3;
-    const int m = min(row0 + ld.r[i], n_e - 1);
+  for (int i = 0; i < Loader<GM, GN>::NA; ++i) {
+    const int m = min(row0 + Loader<GM, GN>::row(i), n_e - 1);
     ld.arow[i] = abf + (int64_t)list[lb + m] * I;
-    ld.brow[i] = Wd + ((int64_t)e * H + h0 + ld.r[i]) * I;
   }
+#pragma unroll
+  for (int j = 0; j < Loader<GM, GN>::NB; ++j)
+    ld.brow[j] = Wd + ((int64_t)e * H + h0 + Loader<GM, GN>::row(j)) * I;
   f32x16_t acc[2][2];
   zero_acc(acc);
-  mma_k_loop(T, ld, I, wm, wn, acc);
+  mma_k_loop<GM, GN>(T, ld, I, wm, wn, acc);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = row0 + acc_row(wm, i, r);
+      const int m = row0 + acc_row<GM>(wm, i, r);
       if (m < n_e) {
         const int asg = list[lb + m];
 #pragma unroll
@@ -322,58 +345,53 @@ __global__ void split_router_kernel(const float *__restrict__ Wr, int64_t n,
   w3[2 * n + i] = (uint16_t)b3;
 }
 
-// Tile (128 tokens, 128 experts): the three terms are three K passes into
-// one accumulator.  Experts beyond E read a valid row and are not stored.
+// Tile (64 tokens, 64 experts): the three terms are three K passes into one
+// accumulator.  Experts beyond E read a valid row and are not stored.
+constexpr int RM = 64, RN = 64;
+
 __global__ __launch_bounds__(kThreads) void router_mma_kernel(
     const uint16_t *__restrict__ x, int64_t T, int H, const uint16_t *__restrict__ w3,
     const float *__restrict__ br, int E, float *__restrict__ logits,
     float *__restrict__ logits2) {
-  __shared__ Tile Tl;
-  const int n_nt = (E + BN - 1) / BN;
+  __shared__ Tile<RM, RN> Tl;
+  const int n_nt = (E + RN - 1) / RN;
   const int64_t mt = blockIdx.x / n_nt;
   const int nt = (int)(blockIdx.x - mt * n_nt);
   const int tid = threadIdx.x, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  const int64_t t0 = mt * BM;
-  const int e0 = nt * BN;
-  f32x16_t acc[2][2];
+  const int64_t t0 = mt * RM;
+  const int e0 = nt * RN;
+  f32x16_t acc[1][1];
   zero_acc(acc);
   for (int term = 0; term < 3; ++term) {
-    Loader ld;
+    Loader<RM, RN> ld;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ch = tid * 2 + i;
-      ld.r[i] = ch >> 2;
-      ld.q[i] = ch & 3;
-      const int64_t t = min<int64_t>(t0 + ld.r[i], T - 1);
+    for (int i = 0; i < Loader<RM, RN>::NA; ++i) {
+      const int64_t t = min<int64_t>(t0 + Loader<RM, RN>::row(i), T - 1);
       ld.arow[i] = x + t * H;
-      const int e = min(e0 + ld.r[i], E - 1);
-      ld.brow[i] = w3 + (int64_t)term * E * H + (int64_t)e * H;
     }
-    mma_k_loop(Tl, ld, H, wm, wn, acc);
+#pragma unroll
+    for (int j = 0; j < Loader<RM, RN>::NB; ++j) {
+      const int e = min(e0 + Loader<RM, RN>::row(j), E - 1);
+      ld.brow[j] = w3 + (int64_t)term * E * H + (int64_t)e * H;
+    }
+    mma_k_loop<RM, RN>(Tl, ld, H, wm, wn, acc);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + acc_row(wm, i, r);
-      if (t < T) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int e = e0 + wn * 64 + j * 32 + (lane_id() & 31);
-          if (e < E) {
-            const float v = acc[i][j][r] + (br ? br[e] : 0.0f);
-            logits[t * E + e] = v;
-            if (logits2) logits2[t * E + e] = v;
-          }
-        }
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int64_t t = t0 + acc_row<RM>(wm, 0, r);
+    const int e = e0 + wn * 32 + (lane_id() & 31);
+    if (t < T && e < E) {
+      const float v = acc[0][0][r] + (br ? br[e] : 0.0f);
+      logits[t * E + e] = v;
+      if (logits2) logits2[t * E + e] = v;
     }
+  }
 }
 
 }  // namespace pf
 
 bool prefill_supported(int H, int I, bool bf16) {
-  return bf16 && H % pf::BN == 0 && I % 64 == 0 && H % pf::BK == 0 && I % pf::BK == 0;
+  return bf16 && H % pf::GN == 0 && I % 64 == 0 && H % pf::BK == 0 && I % pf::BK == 0;
 }
 
 size_t prefill_plan_words(int64_t n, int E) { return 4 + 3 * (size_t)E + 2 + (size_t)n; }
@@ -387,7 +405,7 @@ hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipS
 hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3,
                              const float *br, int E, float *logits, float *logits2,
                              hipStream_t s) {
-  const int64_t tiles = ((T + pf::BM - 1) / pf::BM) * ((E + pf::BN - 1) / pf::BN);
+  const int64_t tiles = ((T + pf::RM - 1) / pf::RM) * ((E + pf::RN - 1) / pf::RN);
   pf::router_mma_kernel<<<dim3((unsigned)tiles), dim3(pf::kThreads), 0, s>>>(x, T, H, w3, br, E,
                                                                              logits, logits2);
   return hipGetLastError();
@@ -399,26 +417,27 @@ hipError_t launch_prefill_plan(const int32_t *ids, int64_t n, int E, int32_t *pl
   return hipGetLastError();
 }
 
-// upper bound of the M tiles of a batch: one partial tile per expert
+// upper bound of the M tiles of a batch: one partial tile per expert; the
+// grid is a multiple of 8 (one slot per XCD, see tile_of)
 static int64_t max_mtiles(int64_t n, int E) {
   const int64_t u = n < E ? n : E;
-  return (n + pf::BM - 1) / pf::BM + u;
+  return (n + pf::GM - 1) / pf::GM + u;
 }
+static unsigned grouped_grid(int64_t tiles) { return (unsigned)(((tiles + 7) / 8) * 8); }
 
 hipError_t launch_gateup_mma(const uint16_t *x, int H, const uint16_t *Wg, const uint16_t *Wu,
                              int I, const int32_t *plan, int E, int64_t n, int k1, const float *w,
                              uint16_t *abf, hipStream_t s) {
-  const int64_t grid = max_mtiles(n, E) * (I / 64);
-  pf::gateup_mma_kernel<<<dim3((unsigned)grid), dim3(pf::kThreads), 0, s>>>(x, H, Wg, Wu, I, plan,
-                                                                            E, k1, w, abf);
+  const unsigned grid = grouped_grid(max_mtiles(n, E) * (I / 64));
+  pf::gateup_mma_kernel<<<dim3(grid), dim3(pf::kThreads), 0, s>>>(x, H, Wg, Wu, I, plan, E, k1, w,
+                                                                  abf);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I,
                            const int32_t *plan, int E, int64_t n, uint16_t *zbf, hipStream_t s) {
-  const int64_t grid = max_mtiles(n, E) * (H / pf::BN);
-  pf::down_mma_kernel<<<dim3((unsigned)grid), dim3(pf::kThreads), 0, s>>>(abf, H, Wd, I, plan, E,
-                                                                          zbf);
+  const unsigned grid = grouped_grid(max_mtiles(n, E) * (H / pf::GN));
+  pf::down_mma_kernel<<<dim3(grid), dim3(pf::kThreads), 0, s>>>(abf, H, Wd, I, plan, E, zbf);
   return hipGetLastError();
 }
 
