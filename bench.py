@@ -324,8 +324,13 @@ def traffic_record(kernel):
     rec = json.loads(rec_path.read_text())
     if rec.get("kernel") != kernel:
         return None
-    src = ROOT / rec["source"]
-    if not src.exists() or hashlib.sha256(src.read_bytes()).hexdigest() != rec["source_sha256"]:
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        src = ROOT / name
+        if not src.exists():
+            return None
+        h.update(src.read_bytes())
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
