@@ -103,8 +103,7 @@ def kernel_work(name, cfg, T, k1, U, bias):
     dn = U * I * H * elt
     n = T * k1
     table = {
-        "b1_front": (router + gu, 2.0 * E * H + 4.0 * n * I * H),
-        "b1_down": (dn + T * H * elt, 2.0 * n * I * H),
+        "b1_layer": (layer_bytes(cfg, T, U, bias), 2.0 * E * H + expert_flops(cfg, T, k1)),
         "router": (router + T * E * 4, 2.0 * T * E * H),
         "router_route": (router, 2.0 * T * E * H),
         "gateup": (gu + T * H * elt, 4.0 * n * I * H),

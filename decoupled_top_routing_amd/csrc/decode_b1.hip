@@ -1,28 +1,40 @@
-// The routed MoE layer for ONE token (batch-1 decode) in two launches.
+// The routed MoE layer for ONE token (batch-1 decode) in one launch.
 //
 // What it computes: router logits, the fp32 softmax / top-k2 / Eq. 2 route
 // of "Paper of the Week #3 - Half the FLOPs Is Not Half the Time" (section
 // "The Receipt", Eq. 2; section "Ship It - Code of the Week"), and for each
 // activated expert the gated MLP of "Channel Selection for Mixture-of-Experts
 // Decoding Needs No Calibration Data" (section 2 "Background"), weighted and
-// summed.
+// summed in ascending expert order.
 //
-// Launch 1 (front), workgroups in block-index order:
-//   R   [0, n_r)        wave e computes logit e and publishes it as a tagged
-//                       word (sync.hpp);
-//   P   n_r             stages the E tagged logits, routes the token, writes
-//                       ids, w and the plan, and publishes (expert, weight)
-//                       of the activated experts, ascending by expert, as
-//                       tagged words in kRepP copies;
-//   GU  [n_r+1, ..)     (activated expert u, block of channels): waits for
-//                       the two words of u, streams the gate and up rows once
-//                       and writes a[u, c] = silu(g) * up * w_u.
-// A block only waits for blocks of smaller index, which the hardware
-// dispatched before it.  Launch 2 (down) computes each output row over every
-// activated expert, y[h] = sum_u Wd[e_u, h, :] . a[u, :], in ascending expert
-// order, and advances the workspace's epoch: the tags of launch 1 are made
-// from the epoch, and launch 2 starts only after every block of launch 1 has
-// finished with them.
+// Workgroups, in block-index order (a block only waits for blocks of smaller
+// index, which the hardware dispatched before it, so the kernel cannot
+// deadlock whatever the occupancy):
+//   R   [0, n_r)          wave e computes logit e and publishes it as a
+//                         tagged word (sync.hpp);
+//   P   n_r               stages the E tagged logits, routes the token, sets
+//                         the activated experts' completion counters to
+//                         (tag, 0) and publishes (expert, weight) of the
+//                         activated experts, ascending by expert, in kRepP
+//                         copies;
+//   GU  [.., +k1*n_cb)    (activated expert u, block of channels): waits for
+//                         the two words of u, streams the gate and up rows
+//                         once, stores a[u, c] = silu(g) * up * w_u
+//                         device-coherently, then adds 1 to u's counter; the
+//                         block that completes the count publishes "u
+//                         complete" in every copy;
+//   D   [.., +n_d)        (block of four output rows): marks itself started,
+//                         waits for the route, issues the down rows of the
+//                         activated experts (they stream while gate/up runs),
+//                         waits until every activated expert is complete,
+//                         stages a in LDS and writes
+//                         y[h] = sum_u Wd[e_u, h, :] . a[u, :].
+// The gate/up block that completes the last expert advances the workspace
+// epoch, the source of the call's tags, once every D block has marked itself
+// started (by then every block of the call has read the epoch).
+// The channel activations a are stored as bf16 when the weights are bf16
+// (the down projection reads bf16 weights; a relative rounding of 2^-9) and
+// as fp32 otherwise.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_device.hpp"
@@ -33,7 +45,10 @@ namespace b1 {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRepP = 16;  // copies of the published route
+constexpr int kRepP = 16;         // copies of the published route
+constexpr int kPF = 8;            // activated experts whose down rows are in flight per wave
+constexpr int kCntStride = 16;    // 64-bit words between two counters (128 B)
+constexpr int kLdsBytes = 24576;  // staged channel activations of one D block
 
 struct Args {
   const void *x;
@@ -41,22 +56,59 @@ struct Args {
   const float *br;
   const void *Wg;
   const void *Wu;
+  const void *Wd;
+  void *y;
   float *logits_out;
   int32_t *ids_out;
   float *w_out;
   int32_t *sync;
-  uint64_t *tl;     // E tagged logits
-  uint64_t *tp;     // kRepP copies of 2*k1 tagged words (expert, weight)
-  int64_t tp_rep;   // copy stride in words
-  int32_t *ids;
-  float *w;
-  int32_t *plan;
-  float *abuf;      // [k1, I]: row u = activated expert u (ascending)
-  int H, E, I, k1, k2, n_r, n_cb;
+  uint64_t *tl;       // E tagged logits
+  uint64_t *tp;       // kRepP copies of 3*k1 tagged words: (expert, weight) per
+                      // activated expert, then one "complete" word each
+  int64_t tp_rep;     // copy stride in words
+  uint64_t *cnt;      // k1 + 1 counters (tag << 32 | count), kCntStride apart:
+                      // blocks done per activated expert, then experts complete
+  uint64_t *started;  // n_d tagged words
+  void *abuf;         // [k1, I] channel activations (bf16 or fp32), row u
+  int H, E, I, k1, k2, n_r, n_cb, n_gu, n_d;
 };
 
+// LDS of a block: the route block's arrays or a D block's staged activations
+union Lds {
+  struct {
+    float sl[kMaxExperts];
+    int32_t s_ids[kMaxExperts];
+    float s_w[kMaxExperts];
+    BlockRoute S;
+  } r;
+  uint64_t a[kLdsBytes / 8];
+};
+
+// bytes of one stored channel activation
+template <typename WT>
+constexpr int kABytes = sizeof(WT) == 2 ? 2 : 4;
+
+// Wait until the tagged words p[0..n) (n <= kWave, one per lane) carry tag;
+// lane i returns word i.  Bounded; SLEEP is the pause between two re-reads.
+template <int SLEEP = 1>
+__device__ uint64_t await_lane(const uint64_t *p, int n, uint32_t tag, int32_t *err) {
+  const int lane = lane_id();
+  uint64_t w = lane < n ? coh_ld(p + lane) : ((uint64_t)tag << 32);
+  uint32_t spins = 0;
+  while (__ballot((uint32_t)(w >> 32) != tag)) {
+    if (++spins > kSpinLimit) {
+      if (lane == 0) coh_st(err, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(SLEEP);
+    if ((uint32_t)(w >> 32) != tag) w = coh_ld(p + lane);
+  }
+  return w;
+}
+
 // gate and up rows of CPW channels per wave (NCH 16-byte chunks per lane of
-// a row, all 2*CPW*NCH loads in flight before any arithmetic), dotted with x.
+// a row, all 2*CPW*NCH loads in flight before any arithmetic), dotted with x;
+// the activations are stored device-coherently.
 template <typename WT, typename XT, int NCH, int CPW>
 __device__ void gateup_rows(const Args &a, int u, int e, float wt, int c0) {
   constexpr int NW = Elem<WT>::kPer16B;
@@ -114,25 +166,120 @@ __device__ void gateup_rows(const Args &a, int u, int e, float wt, int c0) {
       }
     }
   }
+  float av[CPW];
 #pragma unroll
-  for (int ci = 0; ci < CPW; ++ci) {
-    const float g = wave_sum_dpp(ag[ci]);
-    const float up = wave_sum_dpp(au[ci]);
-    const int c = c0 + ci;
-    if (lane == 0 && c < a.I) a.abuf[(int64_t)u * a.I + c] = silu(g) * up * wt;
+  for (int ci = 0; ci < CPW; ++ci) av[ci] = silu(wave_sum_dpp(ag[ci])) * wave_sum_dpp(au[ci]) * wt;
+  if (lane != 0) return;
+  if constexpr (sizeof(WT) == 2) {
+    uint16_t *ab = static_cast<uint16_t *>(a.abuf) + (int64_t)u * a.I;
+    if constexpr (CPW % 2 == 0) {
+#pragma unroll
+      for (int ci = 0; ci < CPW; ci += 2)
+        if (c0 + ci < a.I)
+          coh_st(reinterpret_cast<uint32_t *>(ab + c0 + ci),
+                 f32_to_bf16_bits(av[ci]) | (f32_to_bf16_bits(av[ci + 1]) << 16));
+    } else {
+#pragma unroll
+      for (int ci = 0; ci < CPW; ++ci)
+        if (c0 + ci < a.I) coh_st(ab + c0 + ci, (uint16_t)f32_to_bf16_bits(av[ci]));
+    }
+  } else {
+    float *ab = static_cast<float *>(a.abuf) + (int64_t)u * a.I;
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci)
+      if (c0 + ci < a.I) coh_st(ab + c0 + ci, av[ci]);
   }
 }
 
-template <typename WT, typename XT, int NCHR, int V, int NCH, int CPW>
-__global__ __launch_bounds__(kThreads) void front_kernel(Args a) {
-  __shared__ float sl[kMaxExperts];
-  __shared__ int32_t s_ids[kMaxExperts];
-  __shared__ float s_w[kMaxExperts];
-  __shared__ BlockRoute S;
-  __shared__ int s_e;
+// One output row per wave: y[h] = sum over the activated experts, ascending,
+// of Wd[e_u, h, :] . a[u, :].
+template <typename WT, typename XT, int NCD>
+__device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int d) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  constexpr int AB = kABytes<WT>;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  int32_t *err = a.sync + kErrorWord;
+  // mark this block started (it has read the epoch)
+  if (tid == 0) coh_st(a.started + d, (uint64_t)tag << 32);
+  // the activated experts, ascending
+  if (wv == 0) {
+    const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, 2 * a.k1, tag, err);
+    if ((lane & 1) == 0 && lane < 2 * a.k1)
+      s_uniq[lane >> 1] = min(max(__float_as_int(__uint_as_float((uint32_t)w)), 0), a.E - 1);
+  }
+  __syncthreads();
+  const int h = min(d * kWaves + wv, a.H - 1);
+  const WT *Wd = static_cast<const WT *>(a.Wd);
+  const int nch = a.I / NW;
+  const int U = a.k1;
+  float acc = 0.0f;
+  for (int ub = 0; ub < U; ub += kPF) {
+    const int nu = min(kPF, U - ub);
+    uint4 dq[kPF][NCD];
+#pragma unroll
+    for (int s = 0; s < kPF; ++s) {
+      if (s < nu) {
+        const WT *drow = Wd + ((int64_t)s_uniq[ub + s] * a.H + h) * a.I;
+#pragma unroll
+        for (int j = 0; j < NCD; ++j) {
+          const int ch = j * kWave + lane;
+          dq[s][j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    if (ub == 0) {
+      // every activated expert's activations are stored
+      if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, a.k1, tag, err);
+      __syncthreads();
+    }
+    // stage this round's activations (device-coherent 8-byte loads)
+    const int nw8 = nu * a.I * AB / 8;
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(
+        static_cast<const char *>(a.abuf) + (int64_t)ub * a.I * AB);
+    for (int i = tid; i < nw8; i += kThreads) L.a[i] = coh_ld(src + i);
+    __syncthreads();
+    const char *sa = reinterpret_cast<const char *>(L.a);
+#pragma unroll
+    for (int s = 0; s < kPF; ++s) {
+      if (s < nu) {
+#pragma unroll
+        for (int j = 0; j < NCD; ++j) {
+          const int ch = j * kWave + lane;
+          if (ch < nch) {
+            if constexpr (sizeof(WT) == 2) {
+              const uint4 aq =
+                  *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB);
+              acc = dot2_bf16(dq[s][j].x, aq.x, acc);
+              acc = dot2_bf16(dq[s][j].y, aq.y, acc);
+              acc = dot2_bf16(dq[s][j].z, aq.z, acc);
+              acc = dot2_bf16(dq[s][j].w, aq.w, acc);
+            } else {
+              float dv[NW], av[NW];
+              Elem<WT>::widen(dq[s][j], dv);
+              Elem<float>::widen(
+                  *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB), av);
+#pragma unroll
+              for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[k], acc);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  acc = wave_sum_dpp(acc);
+  if (lane == 0 && d * kWaves + wv < a.H) Elem<XT>::store1(static_cast<XT *>(a.y) + h, acc);
+}
+
+template <typename WT, typename XT, int NCHR, int V, int NCH, int CPW, int NCD>
+__global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
+  __shared__ Lds L;
+  __shared__ int s_uniq[kWave];
+  __shared__ int s_e, s_last;
   __shared__ float s_wt;
   const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const uint32_t tag = call_tag((uint32_t)coh_ld(a.sync + kEpochWord));
+  const uint32_t tag_epoch = (uint32_t)coh_ld(a.sync + kEpochWord);
+  const uint32_t tag = call_tag(tag_epoch);
   int32_t *err = a.sync + kErrorWord;
   if (b < a.n_r) {
     // ---- router: one expert per wave
@@ -148,8 +295,18 @@ __global__ __launch_bounds__(kThreads) void front_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < NCHR; ++j) {
       const int h = (j * kWave + lane) * 4;
+      float xv[4];
+      if constexpr (sizeof(XT) == 2) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(x + h);
+        xv[0] = bf16_lo(q.x);
+        xv[1] = bf16_hi(q.x);
+        xv[2] = bf16_lo(q.y);
+        xv[3] = bf16_hi(q.y);
+      } else {
+        Elem<float>::widen(ld16(x + h), xv);
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wr[j][k], Elem<XT>::load1(x + h + k), acc);
+      for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wr[j][k], xv[k], acc);
     }
     const float s = wave_sum_dpp(acc) + (a.br ? a.br[e] : 0.0f);
     if (lane == 0) {
@@ -159,26 +316,30 @@ __global__ __launch_bounds__(kThreads) void front_kernel(Args a) {
     return;
   }
   if (b == a.n_r) {
-    // ---- route and plan
-    stage_tagged<kMaxExperts / kSyncThreads>(sl, a.E, [&](int i) { return a.tl + i; }, tag, err);
-    route_into_lds<V>(sl, a.E, a.k1, a.k2, s_ids, s_w, S);
+    // ---- route.  The counters (k1 per-expert ones and the count of complete
+    // experts) are set to (tag, 0) first; the staging below waits for every
+    // earlier memory operation of the block, so they are in place before the
+    // route is published.
+    if (tid <= a.k1) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
+    stage_tagged<kMaxExperts / kSyncThreads>(L.r.sl, a.E, [&](int i) { return a.tl + i; }, tag,
+                                             err);
+    route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S);
     for (int r = tid; r < a.k1; r += kThreads) {
-      a.ids[r] = s_ids[r];
-      a.w[r] = s_w[r];
-      if (a.ids_out) a.ids_out[r] = s_ids[r];
-      if (a.w_out) a.w_out[r] = s_w[r];
+      if (a.ids_out) a.ids_out[r] = L.r.s_ids[r];
+      if (a.w_out) a.w_out[r] = L.r.s_w[r];
     }
     if (tid < kWave) {
-      // lane r holds slot r; u = its expert's place among the activated ones
       const int n = a.k1;
-      const int e = lane < n ? s_ids[lane] : 0x7FFFFFFF;
+      __builtin_amdgcn_s_waitcnt(0);
+      // lane r holds slot r; u = its expert's place among the activated ones;
       // lane L writes slot L % n into copy L / n, then the next copies
+      const int e = lane < n ? L.r.s_ids[lane] : 0x7FFFFFFF;
       const int r = lane % n;
-      const int er = s_ids[r];
+      const int er = L.r.s_ids[r];
       int u = 0;
       for (int j = 0; j < n; ++j) u += __builtin_amdgcn_readlane(e, j) < er;
       const uint64_t we = tagged(tag, __int_as_float(er));
-      const uint64_t ww = tagged(tag, s_w[r]);
+      const uint64_t ww = tagged(tag, L.r.s_w[r]);
       const int per = kWave / n;
       if (lane < per * n) {
         for (int c = lane / n; c < kRepP; c += per) {
@@ -186,220 +347,183 @@ __global__ __launch_bounds__(kThreads) void front_kernel(Args a) {
           coh_st(a.tp + c * a.tp_rep + 2 * u + 1, ww);
         }
       }
-      wave_plan(e, n, a.E, a.plan);
     }
     return;
   }
-  // ---- gate/up of (activated expert u, block of channels)
-  const int item = b - a.n_r - 1;
-  const int u = item / a.n_cb, cb = item - u * a.n_cb;
-  if (tid < kWave) {
-    const uint64_t *tp = a.tp + (item % kRepP) * a.tp_rep + 2 * u;
-    uint64_t we = coh_ld(tp), ww = coh_ld(tp + 1);
-    uint32_t spins = 0;
-    while ((uint32_t)(we >> 32) != tag || (uint32_t)(ww >> 32) != tag) {
-      if (++spins > kSpinLimit) {
-        if (lane == 0) coh_st(err, 1);
-        break;
+  if (b < a.n_r + 1 + a.n_gu) {
+    // ---- gate/up of (activated expert u, block of channels)
+    const int item = b - a.n_r - 1;
+    const int u = item / a.n_cb, cb = item - u * a.n_cb;
+    if (wv == 0) {
+      const uint64_t w = await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err);
+      const uint64_t we = __shfl(w, 0), ww = __shfl(w, 1);
+      if (lane == 0) {
+        // a timed-out wait leaves any value here: keep the index in range
+        s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
+        s_wt = __uint_as_float((uint32_t)ww);
       }
-      __builtin_amdgcn_s_sleep(1);
-      if ((uint32_t)(we >> 32) != tag) we = coh_ld(tp);
-      if ((uint32_t)(ww >> 32) != tag) ww = coh_ld(tp + 1);
-    }
-    if (lane == 0) {
-      // a timed-out wait leaves any value here: keep the index in range
-      s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
-      s_wt = __uint_as_float((uint32_t)ww);
-    }
-  }
-  __syncthreads();
-  gateup_rows<WT, XT, NCH, CPW>(a, u, s_e, s_wt, (cb * kWaves + wv) * CPW);
-}
-
-// ---- launch 2: y[h] = sum_u Wd[e_u, h, :] . a[u, :]; one row per wave, in
-// rounds of kPF experts: the block loads the round's a rows (issued first,
-// so waiting for them does not wait for the down rows), then every wave
-// issues its kPF down rows, stages a in LDS and accumulates.
-constexpr int kPF = 8;
-constexpr int kMaxI = 1024;
-
-template <typename WT, typename XT, int NCD>
-__global__ __launch_bounds__(kThreads) void down_kernel(const WT *__restrict__ Wd, int H, int I,
-                                                        const int32_t *__restrict__ plan, int U,
-                                                        const float *__restrict__ abuf,
-                                                        XT *__restrict__ y,
-                                                        int32_t *__restrict__ sync) {
-  constexpr int NW = Elem<WT>::kPer16B;
-  constexpr int kA4 = kPF * kMaxI / 4 / kThreads;  // float4 of a per thread per round
-  __shared__ float s_a[kPF * kMaxI];
-  if (blockIdx.x == 0 && threadIdx.x == 0) coh_st(sync + kEpochWord, coh_ld(sync + kEpochWord) + 1);
-  const int tid = threadIdx.x, lane = lane_id();
-  const int h = min(blockIdx.x * kWaves + (tid >> 6), H - 1);
-  const int32_t *uniq = plan + 4;
-  const int nch = I / NW;
-  float acc = 0.0f;
-  for (int ub = 0; ub < U; ub += kPF) {
-    const int nu = min(kPF, U - ub);
-    const int n4 = nu * I / 4;
-    const float *ab = abuf + (int64_t)ub * I;
-    uint4 aq[kA4];
-#pragma unroll
-    for (int k = 0; k < kA4; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < n4) aq[k] = ld16(ab + 4 * i);
-    }
-    uint4 dq[kPF][NCD];
-#pragma unroll
-    for (int s = 0; s < kPF; ++s) {
-      if (s < nu) {
-        const WT *drow = Wd + ((int64_t)uniq[ub + s] * H + h) * I;
-#pragma unroll
-        for (int j = 0; j < NCD; ++j) {
-          const int ch = j * kWave + lane;
-          dq[s][j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kA4; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < n4) *reinterpret_cast<uint4 *>(&s_a[4 * i]) = aq[k];
     }
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kPF; ++s) {
-      if (s < nu) {
-        const float *arow = s_a + s * I;
-#pragma unroll
-        for (int j = 0; j < NCD; ++j) {
-          const int ch = j * kWave + lane;
-          if (ch < nch) {
-            float av[NW], dv[NW];
-            Elem<float>::widen(*reinterpret_cast<const uint4 *>(arow + ch * NW), av);
-            if constexpr (NW == 8)
-              Elem<float>::widen(*reinterpret_cast<const uint4 *>(arow + ch * NW + 4), av + 4);
-            Elem<WT>::widen(dq[s][j], dv);
-#pragma unroll
-            for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[k], acc);
+    gateup_rows<WT, XT, NCH, CPW>(a, u, s_e, s_wt, (cb * kWaves + wv) * CPW);
+    // every activation store of the block is complete, then count the block
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      s_last = 0;
+      const uint64_t old = __hip_atomic_fetch_add(a.cnt + u * kCntStride, (uint64_t)1,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == (((uint64_t)tag << 32) | (uint32_t)(a.n_cb - 1))) {
+        // the last block of expert u: every block of u counted itself after
+        // its stores were complete; publish "u complete" in every copy
+        for (int c = 0; c < kRepP; ++c) coh_st(a.tp + c * a.tp_rep + 2 * a.k1 + u, (uint64_t)tag << 32);
+        const uint64_t done = __hip_atomic_fetch_add(a.cnt + a.k1 * kCntStride, (uint64_t)1,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = done == (((uint64_t)tag << 32) | (uint32_t)(a.k1 - 1));
+      }
+    }
+    __syncthreads();
+    if (s_last) {
+      // the block completing the last expert advances the epoch once every D
+      // block has marked itself started: then no block of this call reads the
+      // epoch any more (R and P blocks read it before the route existed, every
+      // gate/up block before it counted itself)
+      for (int i = tid; i < a.n_d; i += kThreads) {
+        uint32_t spins = 0;
+        while (coh_ld(a.started + i) != ((uint64_t)tag << 32)) {
+          if (++spins > kSpinLimit) {
+            coh_st(err, 1);
+            break;
           }
+          __builtin_amdgcn_s_sleep(1);
         }
       }
+      __syncthreads();
+      if (tid == 0) coh_st(a.sync + kEpochWord, (int32_t)(tag_epoch + 1u));
     }
-    __syncthreads();
+    return;
   }
-  acc = wave_sum_dpp(acc);
-  if (lane == 0 && blockIdx.x * kWaves + (tid >> 6) < H) Elem<XT>::store1(y + h, acc);
+  down_rows<WT, XT, NCD>(a, L, s_uniq, tag, b - a.n_r - 1 - a.n_gu);
 }
 
 }  // namespace b1
 
-// Shapes the two-launch path takes: the router row and the gate/up row in
-// 1..16 / 1..8 chunks of 16 bytes per lane, the down row in at most 2 per
-// lane, k1 <= 64.
+static int b1_nch(int H, int esz) { return H * esz / (16 * kWave); }
+
+// Shapes the one-launch path takes: the router row in 1..16 and the gate/up
+// row in 1..8 chunks of 16 bytes per lane, the down row in at most 2, k1 <=
+// 32 (two published words per activated expert, one per lane), and one round
+// of activations within a D block's LDS.
 bool decode_b1_supported(int H, int I, int k1, bool bf16) {
   const int esz = bf16 ? 2 : 4;
-  if (k1 > kWave || H % (4 * kWave) != 0 || (H * esz) % (16 * kWave) != 0) return false;
-  const int nchr = H / (4 * kWave), nch = H * esz / (16 * kWave);
+  if (2 * k1 > kWave || H % (4 * kWave) != 0 || (H * esz) % (16 * kWave) != 0) return false;
+  const int nchr = H / (4 * kWave), nch = b1_nch(H, esz);
   if (!(nchr == 1 || nchr == 2 || nchr == 4 || nchr == 8 || nchr == 16)) return false;
   if (!(nch == 1 || nch == 2 || nch == 4 || nch == 8)) return false;
-  return I * esz / 16 <= 2 * kWave && I <= b1::kMaxI;
+  const int ab = bf16 ? 2 : 4;
+  const int round_bytes = (k1 < b1::kPF ? k1 : b1::kPF) * I * ab;
+  return I * esz / 16 <= 2 * kWave && round_bytes <= b1::kLdsBytes && (I * ab) % 8 == 0;
 }
 
-size_t decode_b1_tagged_bytes(int E, int k1, int64_t *tp_offset, int64_t *tp_rep_words) {
-  const size_t tl = ((size_t)E * 8 + 255) & ~(size_t)255;
-  const size_t rep = ((((size_t)2 * k1 * 8 + 4095) & ~(size_t)4095) + 1280);
-  *tp_offset = (int64_t)tl;
-  *tp_rep_words = (int64_t)(rep / 8);
-  return tl + b1::kRepP * rep;
+B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16) {
+  B1Layout L;
+  auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  size_t o = 0;
+  L.tl = o;
+  o += r256((size_t)E * 8);
+  L.tp = o;
+  L.tp_rep_words = (int64_t)(((((size_t)3 * k1 * 8 + 4095) & ~(size_t)4095) + 1280) / 8);
+  o += r256(b1::kRepP * (size_t)L.tp_rep_words * 8);
+  L.cnt = o;
+  o += r256((size_t)(k1 + 1) * b1::kCntStride * 8);
+  L.started = o;
+  o += r256((size_t)((H + b1::kWaves - 1) / b1::kWaves) * 8);
+  L.abuf = o;
+  o += r256((size_t)k1 * I * (bf16 ? 2 : 4));
+  L.total = o;
+  return L;
 }
 
 template <typename WT, typename XT, int NCHR, int V>
-static void launch_front_nch(b1::Args &a, int nch, hipStream_t s) {
-  // 4 gate/up row pairs... 16 chunk loads per lane in flight
+static void launch_nch(b1::Args &a, int nch, int ncd, hipStream_t s) {
   auto go = [&](auto kern, int cpw) {
     a.n_cb = (a.I + b1::kWaves * cpw - 1) / (b1::kWaves * cpw);
-    const int grid = a.n_r + 1 + a.k1 * a.n_cb;
+    a.n_gu = a.k1 * a.n_cb;
+    const int grid = a.n_r + 1 + a.n_gu + a.n_d;
     kern<<<dim3((unsigned)grid), dim3(b1::kThreads), 0, s>>>(a);
   };
-  if (nch == 1) go(b1::front_kernel<WT, XT, NCHR, V, 1, 8>, 8);
-  else if (nch == 2) go(b1::front_kernel<WT, XT, NCHR, V, 2, 4>, 4);
-  else if (nch == 4) go(b1::front_kernel<WT, XT, NCHR, V, 4, 2>, 2);
-  else go(b1::front_kernel<WT, XT, NCHR, V, 8, 1>, 1);
+#define B1_GO(NCH, CPW)                                        \
+  do {                                                         \
+    if (ncd == 1)                                              \
+      go(b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 1>, CPW); \
+    else                                                       \
+      go(b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 2>, CPW); \
+  } while (0)
+  if (nch == 1) B1_GO(1, 8);
+  else if (nch == 2) B1_GO(2, 4);
+  else if (nch == 4) B1_GO(4, 2);
+  else B1_GO(8, 1);
+#undef B1_GO
 }
 
 template <typename WT, typename XT, int V>
-static void launch_front_v(b1::Args &a, int nchr, int nch, hipStream_t s) {
+static void launch_v(b1::Args &a, int nchr, int nch, int ncd, hipStream_t s) {
   switch (nchr) {
-    case 1: launch_front_nch<WT, XT, 1, V>(a, nch, s); break;
-    case 2: launch_front_nch<WT, XT, 2, V>(a, nch, s); break;
-    case 4: launch_front_nch<WT, XT, 4, V>(a, nch, s); break;
-    case 8: launch_front_nch<WT, XT, 8, V>(a, nch, s); break;
-    default: launch_front_nch<WT, XT, 16, V>(a, nch, s); break;
+    case 1: launch_nch<WT, XT, 1, V>(a, nch, ncd, s); break;
+    case 2: launch_nch<WT, XT, 2, V>(a, nch, ncd, s); break;
+    case 4: launch_nch<WT, XT, 4, V>(a, nch, ncd, s); break;
+    case 8: launch_nch<WT, XT, 8, V>(a, nch, ncd, s); break;
+    default: launch_nch<WT, XT, 16, V>(a, nch, ncd, s); break;
   }
 }
 
 template <typename WT, typename XT>
-hipError_t launch_decode_b1_front(const XT *x, int H, const float *Wr, const float *br, int E,
-                                  const WT *Wg, const WT *Wu, int I, int k1, int k2,
-                                  float *logits_out, int32_t *ids_out, float *w_out,
-                                  int32_t *sync, char *tagged, int32_t *ids, float *w,
-                                  int32_t *plan, float *abuf, hipStream_t s) {
+hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
+                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
+                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+                            int32_t *sync, char *region, hipStream_t s) {
+  constexpr int esz = sizeof(WT);
+  const B1Layout Lb = decode_b1_layout(H, E, I, k1, esz == 2);
   b1::Args a;
-  int64_t tp_off = 0, tp_rep = 0;
-  decode_b1_tagged_bytes(E, k1, &tp_off, &tp_rep);
   a.x = x;
   a.Wr = Wr;
   a.br = br;
   a.Wg = Wg;
   a.Wu = Wu;
+  a.Wd = Wd;
+  a.y = y;
   a.logits_out = logits_out;
   a.ids_out = ids_out;
   a.w_out = w_out;
   a.sync = sync;
-  a.tl = reinterpret_cast<uint64_t *>(tagged);
-  a.tp = reinterpret_cast<uint64_t *>(tagged + tp_off);
-  a.tp_rep = tp_rep;
-  a.ids = ids;
-  a.w = w;
-  a.plan = plan;
-  a.abuf = abuf;
+  a.tl = reinterpret_cast<uint64_t *>(region + Lb.tl);
+  a.tp = reinterpret_cast<uint64_t *>(region + Lb.tp);
+  a.tp_rep = Lb.tp_rep_words;
+  a.cnt = reinterpret_cast<uint64_t *>(region + Lb.cnt);
+  a.started = reinterpret_cast<uint64_t *>(region + Lb.started);
+  a.abuf = region + Lb.abuf;
   a.H = H;
   a.E = E;
   a.I = I;
   a.k1 = k1;
   a.k2 = k2;
   a.n_r = (E + b1::kWaves - 1) / b1::kWaves;
-  a.n_cb = 0;
-  constexpr int esz = sizeof(WT);
-  const int nchr = H / (4 * kWave), nch = H * esz / (16 * kWave);
-  if (E <= 64) launch_front_v<WT, XT, 1>(a, nchr, nch, s);
-  else if (E <= 128) launch_front_v<WT, XT, 2>(a, nchr, nch, s);
-  else if (E <= 256) launch_front_v<WT, XT, 4>(a, nchr, nch, s);
-  else if (E <= 512) launch_front_v<WT, XT, 8>(a, nchr, nch, s);
-  else launch_front_v<WT, XT, 16>(a, nchr, nch, s);
-  return hipGetLastError();
-}
-
-template <typename WT, typename XT>
-hipError_t launch_decode_b1_down(const WT *Wd, int H, int I, int k1, const int32_t *plan,
-                                 const float *abuf, XT *y, int32_t *sync, hipStream_t s) {
-  constexpr int esz = sizeof(WT);
+  a.n_d = (H + b1::kWaves - 1) / b1::kWaves;
+  a.n_cb = a.n_gu = 0;
+  const int nchr = H / (4 * kWave), nch = b1_nch(H, esz);
   const int ncd = (I * esz / 16 + kWave - 1) / kWave;
-  const dim3 grid((unsigned)((H + b1::kWaves - 1) / b1::kWaves)), block(b1::kThreads);
-  if (ncd == 1)
-    b1::down_kernel<WT, XT, 1><<<grid, block, 0, s>>>(Wd, H, I, plan, k1, abuf, y, sync);
-  else
-    b1::down_kernel<WT, XT, 2><<<grid, block, 0, s>>>(Wd, H, I, plan, k1, abuf, y, sync);
+  if (E <= 64) launch_v<WT, XT, 1>(a, nchr, nch, ncd, s);
+  else if (E <= 128) launch_v<WT, XT, 2>(a, nchr, nch, ncd, s);
+  else if (E <= 256) launch_v<WT, XT, 4>(a, nchr, nch, ncd, s);
+  else if (E <= 512) launch_v<WT, XT, 8>(a, nchr, nch, ncd, s);
+  else launch_v<WT, XT, 16>(a, nchr, nch, ncd, s);
   return hipGetLastError();
 }
 
-#define MOE_INST_B1(WT, XT)                                                                    \
-  template hipError_t launch_decode_b1_front<WT, XT>(                                         \
-      const XT *, int, const float *, const float *, int, const WT *, const WT *, int, int, int, \
-      float *, int32_t *, float *, int32_t *, char *, int32_t *, float *, int32_t *, float *,    \
-      hipStream_t);                                                                            \
-  template hipError_t launch_decode_b1_down<WT, XT>(const WT *, int, int, int, const int32_t *, \
-                                                    const float *, XT *, int32_t *, hipStream_t);
+#define MOE_INST_B1(WT, XT)                                                                 \
+  template hipError_t launch_decode_b1<WT, XT>(const XT *, int, const float *, const float *, \
+                                               int, const WT *, const WT *, const WT *, int,  \
+                                               int, int, XT *, float *, int32_t *, float *,   \
+                                               int32_t *, char *, hipStream_t);
 MOE_INST_B1(float, float)
 MOE_INST_B1(bf16_t, bf16_t)
 

@@ -62,18 +62,18 @@ hipError_t launch_router_route(const XT *x, int H, const float *Wr, const float 
                                float *w, int32_t *ids2, float *w2, int32_t *plan, int32_t *ticket,
                                hipStream_t s);
 
-// ---- one token in two launches (router + route + gate/up, then down)
+// ---- one token in one launch (router, route, gate/up and down)
+struct B1Layout {
+  size_t tl, tp, cnt, started, abuf, total;  // byte offsets in the path's region
+  int64_t tp_rep_words;
+};
 bool decode_b1_supported(int H, int I, int k1, bool bf16);
-size_t decode_b1_tagged_bytes(int E, int k1, int64_t *tp_offset, int64_t *tp_rep_words);
+B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16);
 template <typename WT, typename XT>
-hipError_t launch_decode_b1_front(const XT *x, int H, const float *Wr, const float *br, int E,
-                                  const WT *Wg, const WT *Wu, int I, int k1, int k2,
-                                  float *logits_out, int32_t *ids_out, float *w_out,
-                                  int32_t *sync, char *tagged, int32_t *ids, float *w,
-                                  int32_t *plan, float *abuf, hipStream_t s);
-template <typename WT, typename XT>
-hipError_t launch_decode_b1_down(const WT *Wd, int H, int I, int k1, const int32_t *plan,
-                                 const float *abuf, XT *y, int32_t *sync, hipStream_t s);
+hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
+                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
+                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+                            int32_t *sync, char *region, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);

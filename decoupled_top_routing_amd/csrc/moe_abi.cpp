@@ -53,8 +53,8 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   L.zbuf = o;
   o += round256(n_assign * (size_t)H * 4);
   L.tagged = o;
-  int64_t tp_off = 0, tp_rep = 0;
-  o += round256(moe::decode_b1_tagged_bytes(E, k1, &tp_off, &tp_rep));
+  o += round256(moe::decode_b1_layout(H, E, I, k1, true).total);
+  o += round256(moe::decode_b1_layout(H, E, I, k1, false).total);
   L.total = o;
   return L;
 }
@@ -228,10 +228,9 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   const int64_t n_assign = T * k1;
   int32_t *ticket = sync + moe::kRouteTicketWord;
   if (T == 1 && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2)) {
-    RUN("b1_front", (moe::launch_decode_b1_front<WT, XT>(x, H, Wr, br, E, Wg, Wu, I, k1, k2,
-                                                         logits_out, ids_out, w_out, sync,
-                                                         ws + L.tagged, ids, w, plan, abuf, s)));
-    RUN("b1_down", (moe::launch_decode_b1_down<WT, XT>(Wd, H, I, k1, plan, abuf, y, sync, s)));
+    RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
+                                                   logits_out, ids_out, w_out, sync,
+                                                   ws + L.tagged, s)));
     return MOE_OK;
   }
   if (T == 1 && moe::router_route_supported(H)) {
