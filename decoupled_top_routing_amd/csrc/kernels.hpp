@@ -79,9 +79,10 @@ hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br
 bool prefill_supported(int H, int I, bool bf16);
 size_t prefill_plan_words(int64_t n, int E);
 hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipStream_t s);
-hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3,
-                             const float *br, int E, float *logits, float *logits2,
-                             hipStream_t s);
+hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3, int E,
+                             float *part, hipStream_t s);
+hipError_t launch_router_sum(const float *part, int64_t T, int E, const float *br, float *logits,
+                             float *logits2, hipStream_t s);
 hipError_t launch_prefill_plan(const int32_t *ids, int64_t n, int E, int32_t *plan,
                                hipStream_t s);
 hipError_t launch_gateup_mma(const uint16_t *x, int H, const uint16_t *Wg, const uint16_t *Wu,

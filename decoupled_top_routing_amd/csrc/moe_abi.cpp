@@ -61,7 +61,7 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
 
 // Workspace layout of the prefill path.
 struct PrefillLayout {
-  size_t logits, ids, w, plan, w3, abf, zbf, total;
+  size_t logits, ids, w, plan, w3, part, abf, zbf, total;
 };
 
 PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
@@ -78,6 +78,8 @@ PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   o += round256(moe::prefill_plan_words((int64_t)n, E) * 4);
   L.w3 = o;
   o += round256((size_t)3 * E * H * 2);
+  L.part = o;
+  o += round256((size_t)3 * T * E * 4);
   L.abf = o;
   o += round256(n * (size_t)I * 2);
   L.zbf = o;
@@ -188,7 +190,9 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, co
   const int64_t n = T * k1;
   const hipStream_t s = run.s;
   RUN("split_router", moe::launch_split_router(Wr, E, H, w3, s));
-  RUN("router_mma", moe::launch_router_mma(x, T, H, w3, br, E, logits, logits_out, s));
+  float *part = reinterpret_cast<float *>(ws + L.part);
+  RUN("router_mma", moe::launch_router_mma(x, T, H, w3, E, part, s));
+  RUN("router_sum", moe::launch_router_sum(part, T, E, br, logits, logits_out, s));
   RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
                                       nullptr, s));
   RUN("prefill_plan", moe::launch_prefill_plan(ids, n, E, plan, s));

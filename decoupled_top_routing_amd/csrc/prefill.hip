@@ -328,8 +328,8 @@ __global__ __launch_bounds__(kThreads) void down_mma_kernel(
 // fp32 router weights as three bf16 terms, Wr = W1 + W2 + W3 with
 // W1 = bf16(Wr), W2 = bf16(Wr - W1), W3 = bf16(Wr - W1 - W2): 24 significant
 // bits, i.e. the fp32 value (up to the last bit's rounding).  x is bf16, so
-// every product is exact in fp32 and logits = x W1^T + x W2^T + x W3^T with
-// fp32 accumulation.
+// every product is exact in fp32 and logits = (x W1^T + x W2^T) + x W3^T,
+// each term accumulated in fp32.
 __global__ void split_router_kernel(const float *__restrict__ Wr, int64_t n,
                                     uint16_t *__restrict__ w3) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -345,47 +345,62 @@ __global__ void split_router_kernel(const float *__restrict__ Wr, int64_t n,
   w3[2 * n + i] = (uint16_t)b3;
 }
 
-// Tile (64 tokens, 64 experts): the three terms are three K passes into one
-// accumulator.  Experts beyond E read a valid row and are not stored.
+// Tile (64 tokens, 64 experts) of one term: part[term, t, e] = x[t] . W_term[e]
+// (fp32 accumulation).  The three terms run as separate workgroups (three
+// times the parallelism) and router_sum_kernel adds them in a fixed order.
+// Experts beyond E read a valid row and are not stored.
 constexpr int RM = 64, RN = 64;
 
-__global__ __launch_bounds__(kThreads) void router_mma_kernel(
-    const uint16_t *__restrict__ x, int64_t T, int H, const uint16_t *__restrict__ w3,
-    const float *__restrict__ br, int E, float *__restrict__ logits,
-    float *__restrict__ logits2) {
+__global__ __launch_bounds__(kThreads) void router_mma_kernel(const uint16_t *__restrict__ x,
+                                                              int64_t T, int H,
+                                                              const uint16_t *__restrict__ w3,
+                                                              int E, float *__restrict__ part) {
   __shared__ Tile<RM, RN> Tl;
   const int n_nt = (E + RN - 1) / RN;
-  const int64_t mt = blockIdx.x / n_nt;
-  const int nt = (int)(blockIdx.x - mt * n_nt);
+  const int64_t n_tiles = ((T + RM - 1) / RM) * n_nt;
+  const int term = (int)(blockIdx.x / n_tiles);
+  const int64_t tile = blockIdx.x - term * n_tiles;
+  const int64_t mt = tile / n_nt;
+  const int nt = (int)(tile - mt * n_nt);
   const int tid = threadIdx.x, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int64_t t0 = mt * RM;
   const int e0 = nt * RN;
   f32x16_t acc[1][1];
   zero_acc(acc);
-  for (int term = 0; term < 3; ++term) {
-    Loader<RM, RN> ld;
+  Loader<RM, RN> ld;
 #pragma unroll
-    for (int i = 0; i < Loader<RM, RN>::NA; ++i) {
-      const int64_t t = min<int64_t>(t0 + Loader<RM, RN>::row(i), T - 1);
-      ld.arow[i] = x + t * H;
-    }
-#pragma unroll
-    for (int j = 0; j < Loader<RM, RN>::NB; ++j) {
-      const int e = min(e0 + Loader<RM, RN>::row(j), E - 1);
-      ld.brow[j] = w3 + (int64_t)term * E * H + (int64_t)e * H;
-    }
-    mma_k_loop<RM, RN>(Tl, ld, H, wm, wn, acc);
+  for (int i = 0; i < Loader<RM, RN>::NA; ++i) {
+    const int64_t t = min<int64_t>(t0 + Loader<RM, RN>::row(i), T - 1);
+    ld.arow[i] = x + t * H;
   }
+#pragma unroll
+  for (int j = 0; j < Loader<RM, RN>::NB; ++j) {
+    const int e = min(e0 + Loader<RM, RN>::row(j), E - 1);
+    ld.brow[j] = w3 + (int64_t)term * E * H + (int64_t)e * H;
+  }
+  mma_k_loop<RM, RN>(Tl, ld, H, wm, wn, acc);
+  float *pt = part + (int64_t)term * T * E;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t t = t0 + acc_row<RM>(wm, 0, r);
     const int e = e0 + wn * 32 + (lane_id() & 31);
-    if (t < T && e < E) {
-      const float v = acc[0][0][r] + (br ? br[e] : 0.0f);
-      logits[t * E + e] = v;
-      if (logits2) logits2[t * E + e] = v;
-    }
+    if (t < T && e < E) pt[t * E + e] = acc[0][0][r];
   }
+}
+
+// logits = (part0 + part1) + part2 (+ br)
+__global__ __launch_bounds__(256) void router_sum_kernel(const float *__restrict__ part,
+                                                         int64_t T, int E,
+                                                         const float *__restrict__ br,
+                                                         float *__restrict__ logits,
+                                                         float *__restrict__ logits2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = T * E;
+  if (i >= n) return;
+  float v = (part[i] + part[n + i]) + part[2 * n + i];
+  if (br) v = v + br[i % E];
+  logits[i] = v;
+  if (logits2) logits2[i] = v;
 }
 
 }  // namespace pf
@@ -402,12 +417,19 @@ hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3,
-                             const float *br, int E, float *logits, float *logits2,
-                             hipStream_t s) {
+hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3, int E,
+                             float *part, hipStream_t s) {
   const int64_t tiles = ((T + pf::RM - 1) / pf::RM) * ((E + pf::RN - 1) / pf::RN);
-  pf::router_mma_kernel<<<dim3((unsigned)tiles), dim3(pf::kThreads), 0, s>>>(x, T, H, w3, br, E,
-                                                                             logits, logits2);
+  pf::router_mma_kernel<<<dim3((unsigned)(3 * tiles)), dim3(pf::kThreads), 0, s>>>(x, T, H, w3, E,
+                                                                                   part);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_sum(const float *part, int64_t T, int E, const float *br, float *logits,
+                             float *logits2, hipStream_t s) {
+  const int64_t n = T * E;
+  pf::router_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(part, T, E, br,
+                                                                                logits, logits2);
   return hipGetLastError();
 }
 
