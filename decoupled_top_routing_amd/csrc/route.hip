@@ -158,16 +158,34 @@ __global__ __launch_bounds__(256) void router_kernel(const XT *__restrict__ x, i
   }
 }
 
-// Small batches: one wave per expert loads its whole router row (NCHR
-// 16-byte chunks per lane, all in flight at once), then dots it with every
-// token.
+// Small batches: one wave per (expert, group of kRowsTok tokens) loads the
+// expert's whole router row (NCHR 16-byte chunks per lane, all in flight at
+// once), then dots it with the group's tokens, four at a time (x read 4
+// elements per load).
+template <typename XT>
+__device__ __forceinline__ void load4(const XT *p, float (&v)[4]) {
+  if constexpr (sizeof(XT) == 2) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(p);
+    v[0] = bf16_lo(q.x);
+    v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y);
+    v[3] = bf16_hi(q.y);
+  } else {
+    Elem<float>::widen(ld16(p), v);
+  }
+}
+
+constexpr int kRowsTok = 16;
+
 template <typename XT, int NCHR>
 __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__ x, int64_t T,
                                                           int H, const float *__restrict__ Wr,
                                                           const float *__restrict__ br, int E,
                                                           float *__restrict__ logits,
                                                           float *__restrict__ logits2) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n_eb = (E + 3) / 4;
+  const int tg = blockIdx.x / n_eb;
+  const int e = (blockIdx.x - tg * n_eb) * 4 + (threadIdx.x >> 6);
   if (e >= E) return;
   const int lane = lane_id();
   const float *wrow = Wr + (int64_t)e * H;
@@ -175,19 +193,29 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__
 #pragma unroll
   for (int j = 0; j < NCHR; ++j) Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wv[j]);
   const float b = br ? br[e] : 0.0f;
-  for (int64_t t = 0; t < T; ++t) {
-    const XT *xr = x + t * H;
-    float acc = 0.0f;
+  const int64_t t_end = min<int64_t>(T, (int64_t)(tg + 1) * kRowsTok);
+  for (int64_t t0 = (int64_t)tg * kRowsTok; t0 < t_end; t0 += 4) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < NCHR; ++j) {
-      const int h = (j * kWave + lane) * 4;
+    for (int q = 0; q < 4; ++q) {
+      const int64_t t = min<int64_t>(t0 + q, t_end - 1);
+      const XT *xr = x + t * H;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wv[j][k], Elem<XT>::load1(xr + h + k), acc);
+      for (int j = 0; j < NCHR; ++j) {
+        float xv[4];
+        load4(xr + (j * kWave + lane) * 4, xv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[q] = __builtin_fmaf(wv[j][k], xv[k], acc[q]);
+      }
     }
-    const float sum = wave_sum_dpp(acc) + b;
-    if (lane == 0) {
-      logits[t * E + e] = sum;
-      if (logits2) logits2[t * E + e] = sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sum = wave_sum_dpp(acc[q]) + b;
+      const int64_t t = t0 + q;
+      if (lane == 0 && t < t_end) {
+        logits[t * E + e] = sum;
+        if (logits2) logits2[t * E + e] = sum;
+      }
     }
   }
 }
@@ -292,7 +320,7 @@ hipError_t launch_router(const XT *x, int64_t T, int H, const float *Wr, const f
                          float *logits, float *logits2, hipStream_t s) {
   const int nchr = (H % (4 * kWave) == 0) ? H / (4 * kWave) : 0;
   if (T <= 64 && (nchr == 1 || nchr == 2 || nchr == 4 || nchr == 8 || nchr == 16)) {
-    const dim3 grid((unsigned)((E + 3) / 4)), block(256);
+    const dim3 grid((unsigned)(((E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok))), block(256);
     switch (nchr) {
       case 1: router_rows_kernel<XT, 1><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
       case 2: router_rows_kernel<XT, 2><<<grid, block, 0, s>>>(x, T, H, Wr, br, E, logits, logits2); break;
