@@ -288,7 +288,7 @@ def cpu_baseline(oracle, synth, layer, k1, k2, budget_s=12.0):
                        nthreads=1)
         done += 1
         el = time.perf_counter() - t0
-        if el > budget_s or done >= 400:
+        if el > budget_s or done >= 4000:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} single-token calls (batch 1, k1:k2={k1}:{k2}) of the C oracle on "
