@@ -37,6 +37,10 @@ DEFAULT_CELLS = ",".join([
     "C2:1:4:16", "C2:1:8:8", "C2:1:4:4", "C2:1:4:128", "C2:1:3:16", "C2:1:2:16",
     "C3:8:4:16", "C3:8:8:8", "C3:8:4:4", "C3:8:4:128", "C3:8:3:16", "C3:8:2:16",
     "C4:4096:4:16", "C4:4096:8:8",
+    # batch sweep of the decode layer (the ring's layers, more tokens)
+    "C3:2:4:16", "C3:2:8:8", "C3:4:4:16", "C3:4:8:8", "C3:16:4:16", "C3:16:8:8",
+    "C3:32:4:16", "C3:32:8:8", "C3:64:4:16", "C3:64:8:8", "C3:128:4:16", "C3:128:8:8",
+    "C3:256:4:16", "C3:256:8:8",
     "C5:1:10:10", "C5:1:5:5", "C5:1:5:20", "C5:64:10:10", "C5:64:5:5", "C5:64:5:20",
 ])
 
@@ -60,8 +64,10 @@ def make_sets(synth, torch, names, ring):
     sets = {}
     t0 = time.perf_counter()
     if names & {"C2", "C3"}:
+        # x holds 256 tokens; a cell of T tokens uses the first T
         sets["C2"] = sets["C3"] = (synth.DECODE_B8,
-                                   [synth.make_layer(synth.DECODE_B8, layer=i, device="cuda")
+                                   [synth.make_layer(synth.DECODE_B8, layer=i, device="cuda",
+                                                     T=256)
                                     for i in range(ring)])
     if "C4" in names:
         sets["C4"] = (synth.PREFILL, [synth.make_layer(synth.PREFILL, device="cuda")])
@@ -402,7 +408,8 @@ def main():
         return None
 
     ratios = {}
-    for cfgname, T in (("C2", 1), ("C3", 8)):
+    for cfgname, T in (("C2", 1), ("C3", 2), ("C3", 4), ("C3", 8), ("C3", 16), ("C3", 32),
+                       ("C3", 64), ("C3", 128), ("C3", 256)):
         a, b = find(cfgname, T, 4, 16), find(cfgname, T, 8, 8)
         if a and b:
             ratios[f"b{T}_4:16_over_8:8"] = b["us_per_layer"] / a["us_per_layer"]

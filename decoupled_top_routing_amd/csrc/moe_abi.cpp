@@ -102,8 +102,12 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
 
 enum class Path { Fused, Grouped, Prefill };
 
-// From this batch size on the expert projections run as MFMA GEMMs.
-constexpr int64_t kPrefillMinT = 256;
+// The expert projections run as MFMA GEMMs from kPrefillMinAssign
+// assignments (T * k1) on, when the experts get two rows each on average;
+// below that the grouped GEMV path reads the same weights faster (measured:
+// the H=2048/E=128/I=768 layer crosses over between 384 and 512 assignments,
+// and the E=512 layer at 640 assignments stays faster on the GEMV path).
+constexpr int64_t kPrefillMinAssign = 512;
 
 // The grouped multi-kernel path is the default: measured on MI355X it beats
 // the single-launch fused path at every decode batch (its gate/up and down
@@ -127,7 +131,9 @@ int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf1
     *path = Path::Grouped;
     return MOE_OK;
   }
-  *path = (prefill_ok && T >= kPrefillMinT) ? Path::Prefill : Path::Grouped;
+  const int64_t n = T * k1;
+  *path = (prefill_ok && n >= kPrefillMinAssign && n >= 2 * (int64_t)E) ? Path::Prefill
+                                                                        : Path::Grouped;
   return MOE_OK;
 }
 

@@ -72,7 +72,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *   GROUPED router, route, per-expert plan, gate/up, down and combine kernels
  *           (grouped GEMVs that read each activated expert once);
  *   PREFILL the same steps with the expert projections as bf16 MFMA grouped
- *           GEMMs (large batches).
+ *           GEMMs (chosen from 512 assignments T*k1 on, when the activated
+ *           experts average two rows or more).
  * A forced path that cannot take the call's shapes returns MOE_ENOTSUP. */
 #define MOE_FLAG_FORCE_FUSED 1u
 #define MOE_FLAG_FORCE_GROUPED 2u
