@@ -32,6 +32,12 @@ Readings taken where the pages are silent (each is pinned by a test):
 6. weights stay fp32 (the logits are fp32);
 7. experts and combine are accumulated in fp64, rounded to fp32 once.
 
+The bf16 router (``logits_bf16``, ``route_bf16w``, ``forward_bf16_router``)
+is the same router method run on a bf16 model, as the page's code does it:
+the linear layer in bf16 (the exact dot product rounded once to bf16, to
+nearest with ties to even), the softmax upcast to fp32, and the weights cast
+back to bf16 (same rounding) before they scale the experts.
+
 The route functions (``softmax``, ``route``) are exact fp32 definitions; the
 expert functions are accumulated in fp64.  Arrays are numpy; bf16 tensors are
 passed as ``uint16`` bit patterns.
@@ -100,6 +106,15 @@ def _open(path):
     lib.oracle_forward.restype = cint
     lib.oracle_forward.argtypes = [P, cint, i64, i32, P, P, i32, P, P, P, cint,
                                    i32, i32, i32, P, P, P, P, cint]
+    lib.oracle_round_bf16_n.restype = None
+    lib.oracle_round_bf16_n.argtypes = [P, P, i64]
+    lib.oracle_logits_bf16.restype = cint
+    lib.oracle_logits_bf16.argtypes = [P, i64, i32, P, i32, P, cint]
+    lib.oracle_route_bf16w.restype = cint
+    lib.oracle_route_bf16w.argtypes = [P, i64, i32, i32, i32, P, P]
+    lib.oracle_forward_bf16_router.restype = cint
+    lib.oracle_forward_bf16_router.argtypes = [P, i64, i32, P, i32, P, P, P, i32,
+                                               i32, i32, P, P, P, P, cint]
     return lib
 
 
@@ -231,4 +246,57 @@ def forward(x, Wr, Wg, Wu, Wd, k1: int, k2: int, br=None, nthreads: int = 1):
                               E, _ptr(Wg), _ptr(Wu), _ptr(Wd), wt, I, k1, k2,
                               _ptr(y), _ptr(lg), _ptr(ids), _ptr(w), nthreads),
            "oracle_forward")
+    return y, lg, ids, w
+
+
+def round_bf16(d):
+    """float64 array -> float32 array of the nearest bf16 values (ties to even)."""
+    lib = _load()
+    d = _c(np.asarray(d, dtype=np.float64))
+    out = np.empty(d.shape, np.float32)
+    lib.oracle_round_bf16_n(_ptr(d), _ptr(out), d.size)
+    return out
+
+
+def logits_bf16(x, Wr, nthreads: int = 1):
+    """bf16 router logits [T,E] (float32 holding bf16 values); x [T,H] and
+    Wr [E,H] as uint16 bf16 bits."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    Wr = _c(Wr, np.uint16)
+    T, H = x.shape
+    E = Wr.shape[0]
+    out = np.empty((T, E), np.float32)
+    _check(lib.oracle_logits_bf16(_ptr(x), T, H, _ptr(Wr), E, _ptr(out), nthreads),
+           "oracle_logits_bf16")
+    return out
+
+
+def route_bf16w(logits, k1: int, k2: int):
+    """``route``, with each weight then cast to bf16 (returned as float32)."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k1), np.int32)
+    w = np.empty((T, k1), np.float32)
+    _check(lib.oracle_route_bf16w(_ptr(logits), T, E, k1, k2, _ptr(ids), _ptr(w)),
+           "oracle_route_bf16w")
+    return ids, w
+
+
+def forward_bf16_router(x, Wr, Wg, Wu, Wd, k1: int, k2: int, nthreads: int = 1):
+    """Whole layer with the bf16 router; every tensor uint16 bf16 bits.
+    Returns (y, logits, ids, w)."""
+    lib = _load()
+    x, Wr = _c(x, np.uint16), _c(Wr, np.uint16)
+    Wg, Wu, Wd = _c(Wg, np.uint16), _c(Wu, np.uint16), _c(Wd, np.uint16)
+    T, H = x.shape
+    E, I, _ = Wg.shape
+    y = np.empty((T, H), np.float32)
+    lg = np.empty((T, E), np.float32)
+    ids = np.empty((T, k1), np.int32)
+    w = np.empty((T, k1), np.float32)
+    _check(lib.oracle_forward_bf16_router(_ptr(x), T, H, _ptr(Wr), E, _ptr(Wg), _ptr(Wu),
+                                          _ptr(Wd), I, k1, k2, _ptr(y), _ptr(lg), _ptr(ids),
+                                          _ptr(w), nthreads), "oracle_forward_bf16_router")
     return y, lg, ids, w

@@ -369,3 +369,92 @@ int oracle_forward(const void *x, int act, int64_t T, int32_t H,
     return oracle_experts(x, act, T, H, Wg, Wu, Wd, wt, E, I, k1, ids, w, y,
                           nthreads);
 }
+
+/* ================================================================== */
+/* The bf16 router of the P1 router method as it runs on a bf16 model */
+/* (P1 Code of the Week): the linear layer is computed in the model's */
+/* dtype, so the logits are bf16; the softmax upcasts them to fp32    */
+/* (dtype=float); the returned weights are cast back to the logits'   */
+/* dtype.  Readings: the bf16 logit is the exact dot product rounded  */
+/* once to bf16 (round to nearest, ties to even, the usual cast); the */
+/* cast of the weights rounds the fp32 Eq. 2 weight the same way; the */
+/* experts are then scaled by that bf16 weight.                       */
+/* ================================================================== */
+
+/* d rounded to the nearest bfloat16 value, ties to even.  bf16 keeps 8
+ * significant bits, so d = m * 2^q with m an integer of at most 8 bits and
+ * q = exponent(d) - 8; below the smallest normal (2^-126) the spacing stays
+ * 2^-133.  nearbyint rounds in the default mode: to nearest, ties to even. */
+static float round_bf16(double d)
+{
+    if (d == 0.0 || !isfinite(d))
+        return (float)d;
+    int ex;
+    (void)frexp(d, &ex); /* |d| = f * 2^ex with f in [0.5, 1) */
+    int q = ex - 8;
+    if (q < -133)
+        q = -133;
+    double m = nearbyint(ldexp(d, -q));
+    return (float)ldexp(m, q);
+}
+
+void oracle_round_bf16_n(const double *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = round_bf16(in[i]);
+}
+
+/* bf16 logits: l[t,e] = bf16(sum_h x[t,h] * Wr[e,h]), the products of bf16
+ * values exact in fp64, the sum in fp64, one rounding to bf16. */
+int oracle_logits_bf16(const uint16_t *x, int64_t T, int32_t H,
+                       const uint16_t *Wr, int32_t E, float *logits,
+                       int nthreads)
+{
+    if (T < 0 || H < 1 || E < 1)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                s += (double)bf16_to_f32(x[t * H + h]) *
+                     (double)bf16_to_f32(Wr[(int64_t)e * H + h]);
+            logits[t * E + e] = round_bf16(s);
+        }
+    }
+    return OR_OK;
+}
+
+/* The route of oracle_route, then each weight cast to bf16. */
+int oracle_route_bf16w(const float *logits, int64_t T, int32_t E, int32_t k1,
+                       int32_t k2, int32_t *ids, float *w)
+{
+    int rc = oracle_route(logits, T, E, k1, k2, ids, w);
+    if (rc != OR_OK)
+        return rc;
+    for (int64_t i = 0; i < T * k1; ++i)
+        w[i] = round_bf16((double)w[i]);
+    return OR_OK;
+}
+
+/* The whole layer with the bf16 router: bf16 x, Wr and expert weights. */
+int oracle_forward_bf16_router(const uint16_t *x, int64_t T, int32_t H,
+                               const uint16_t *Wr, int32_t E,
+                               const uint16_t *Wg, const uint16_t *Wu,
+                               const uint16_t *Wd, int32_t I, int32_t k1,
+                               int32_t k2, float *y, float *logits,
+                               int32_t *ids, float *w, int nthreads)
+{
+    int rc = oracle_logits_bf16(x, T, H, Wr, E, logits, nthreads);
+    if (rc != OR_OK)
+        return rc;
+    rc = oracle_route_bf16w(logits, T, E, k1, k2, ids, w);
+    if (rc != OR_OK)
+        return rc;
+    return oracle_experts(x, OR_BF16, T, H, Wg, Wu, Wd, OR_BF16, E, I, k1, ids,
+                          w, y, nthreads);
+}

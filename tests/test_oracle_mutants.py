@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_bf16_router_pins as hf_pins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -40,6 +41,16 @@ MUTANTS = {
         ("s += (double)br[e];", "s += 0.0;"),
     "gate and up read the same row":
         ("u += load_elem(Wu, wt, row + h) * xv[h];", "u += load_elem(Wg, wt, row + h) * xv[h];"),
+    "bf16 rounding truncates":
+        ("double m = nearbyint(ldexp(d, -q));", "double m = trunc(ldexp(d, -q));"),
+    "bf16 rounding sends ties away from zero":
+        ("double m = nearbyint(ldexp(d, -q));", "double m = round(ldexp(d, -q));"),
+    "bf16 rounding keeps one bit too many":
+        ("int q = ex - 8;", "int q = ex - 9;"),
+    "bf16 logits left in fp32":
+        ("logits[t * E + e] = round_bf16(s);", "logits[t * E + e] = (float)s;"),
+    "bf16 router weights not cast":
+        ("w[i] = round_bf16((double)w[i]);", "w[i] = w[i];"),
 }
 
 PIN_CHECKS = [
@@ -56,6 +67,9 @@ PIN_CHECKS = [
     lambda: pins.test_each_expert_matches_numpy_fp64(False),
     pins.test_single_expert_case,
     pins.test_router_bias_is_added,
+    hf_pins.test_round_bf16_matches_torch_cast_from_fp32,
+    hf_pins.test_bf16_logits_are_the_exact_dot_product_rounded_once,
+    lambda: hf_pins.test_bf16_router_at_k1_eq_k2_is_stock_bitwise(128, 8),
 ]
 
 
