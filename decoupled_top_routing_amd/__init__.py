@@ -20,13 +20,14 @@ from pathlib import Path
 import torch
 
 __all__ = ["route", "forward", "MoeError", "library_path", "load_library",
-           "F32", "BF16", "FORCE_FUSED", "FORCE_GROUPED", "FORCE_PREFILL"]
+           "F32", "BF16", "FORCE_FUSED", "FORCE_GROUPED", "FORCE_PREFILL", "ROUTER_BF16"]
 
 PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libmoe.so"
 
 F32, BF16 = 0, 1
 FORCE_FUSED, FORCE_GROUPED, FORCE_PREFILL = 1, 2, 4
+ROUTER_BF16 = 8
 ABI_VERSION = 1
 
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_EWORKSPACE",
@@ -158,7 +159,11 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
 
     x [T,H] (fp32 or bf16), Wr [E,H] fp32, br [E] fp32 or None, Wgate and Wup
     [E,I,H], Wdown [E,H,I] in the dtype of x.  Returns y [T,H] in x's dtype,
-    or (y, logits, ids, w) with ``return_route=True``.  ``out`` receives y if
+    or (y, logits, ids, w) with ``return_route=True``.
+
+    A bf16 ``Wr`` selects the bf16 router (``ROUTER_BF16``, the page's router
+    method on a bf16 model): bf16 logits, fp32 softmax and Eq. 2, weights
+    rounded to bf16; it takes bf16 x and expert weights and no ``br``.  ``out`` receives y if
     given; ``workspace`` is an optional zero-filled uint8 device tensor of at
     least ``moe_forward_workspace`` bytes (needed under graph capture, where
     nothing may be allocated).
@@ -166,7 +171,9 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
     lib = load_library()
     _need_cuda("x", x)
     act = _dtype_code(x)
-    _need_cuda("Wr", Wr, torch.float32)
+    if Wr.dtype == torch.bfloat16:
+        flags |= ROUTER_BF16
+    _need_cuda("Wr", Wr, torch.bfloat16 if flags & ROUTER_BF16 else torch.float32)
     for n, t in (("Wgate", Wgate), ("Wup", Wup), ("Wdown", Wdown)):
         _need_cuda(n, t, x.dtype)
     if br is not None:

@@ -19,6 +19,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// f rounded to the nearest bf16 value (ties to even), kept as fp32.
+__device__ __forceinline__ float round_bf16(float f) {
+  return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+
 // Storage types: weights and activations are either float or bf16 (stored
 // as uint16_t bit patterns).
 struct bf16_t {

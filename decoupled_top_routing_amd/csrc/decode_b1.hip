@@ -32,6 +32,8 @@
 // The gate/up block that completes the last expert advances the workspace
 // epoch, the source of the call's tags, once every D block has marked itself
 // started (by then every block of the call has read the epoch).
+// With the bf16 router (the router method on a bf16 model) Wr is bf16, the
+// R blocks round each logit to bf16 and P rounds each weight to bf16.
 // The channel activations a are stored as bf16 when the weights are bf16
 // (the down projection reads bf16 weights; a relative rounding of 2^-9) and
 // as fp32 otherwise.
@@ -52,7 +54,7 @@ constexpr int kLdsBytes = 24576;  // staged channel activations of one D block
 
 struct Args {
   const void *x;
-  const float *Wr;
+  const void *Wr;     // fp32, or bf16 with router_bf16
   const float *br;
   const void *Wg;
   const void *Wu;
@@ -71,6 +73,7 @@ struct Args {
   uint64_t *started;  // n_d tagged words
   void *abuf;         // [k1, I] channel activations (bf16 or fp32), row u
   int H, E, I, k1, k2, n_r, n_cb, n_gu, n_d;
+  bool router_bf16;   // bf16 router: bf16 Wr, logits and weights rounded to bf16
 };
 
 // LDS of a block: the route block's arrays or a D block's staged activations
@@ -286,11 +289,23 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     const int e = b * kWaves + wv;
     if (e >= a.E) return;
     const XT *x = static_cast<const XT *>(a.x);
-    const float *wrow = a.Wr + (int64_t)e * a.H;
     float wr[NCHR][4];
+    if (a.router_bf16) {
+      const uint16_t *wrow = static_cast<const uint16_t *>(a.Wr) + (int64_t)e * a.H;
 #pragma unroll
-    for (int j = 0; j < NCHR; ++j)
-      Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wr[j]);
+      for (int j = 0; j < NCHR; ++j) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(wrow + (j * kWave + lane) * 4);
+        wr[j][0] = bf16_lo(q.x);
+        wr[j][1] = bf16_hi(q.x);
+        wr[j][2] = bf16_lo(q.y);
+        wr[j][3] = bf16_hi(q.y);
+      }
+    } else {
+      const float *wrow = static_cast<const float *>(a.Wr) + (int64_t)e * a.H;
+#pragma unroll
+      for (int j = 0; j < NCHR; ++j)
+        Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wr[j]);
+    }
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCHR; ++j) {
@@ -308,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wr[j][k], xv[k], acc);
     }
-    const float s = wave_sum_dpp(acc) + (a.br ? a.br[e] : 0.0f);
+    float s = wave_sum_dpp(acc) + (a.br ? a.br[e] : 0.0f);
+    if (a.router_bf16) s = round_bf16(s);
     if (lane == 0) {
       coh_st(a.tl + e, tagged(tag, s));
       if (a.logits_out) a.logits_out[e] = s;
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     if (tid <= a.k1) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
     stage_tagged<kMaxExperts / kSyncThreads>(L.r.sl, a.E, [&](int i) { return a.tl + i; }, tag,
                                              err);
-    route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S);
+    route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S, a.router_bf16);
     for (int r = tid; r < a.k1; r += kThreads) {
       if (a.ids_out) a.ids_out[r] = L.r.s_ids[r];
       if (a.w_out) a.w_out[r] = L.r.s_w[r];
@@ -477,15 +493,16 @@ static void launch_v(b1::Args &a, int nchr, int nch, int ncd, hipStream_t s) {
 }
 
 template <typename WT, typename XT>
-hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
-                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
-                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16, const float *br,
+                            int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
+                            int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
                             int32_t *sync, char *region, hipStream_t s) {
   constexpr int esz = sizeof(WT);
   const B1Layout Lb = decode_b1_layout(H, E, I, k1, esz == 2);
   b1::Args a;
   a.x = x;
   a.Wr = Wr;
+  a.router_bf16 = router_bf16;
   a.br = br;
   a.Wg = Wg;
   a.Wu = Wu;
@@ -520,10 +537,11 @@ hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br
 }
 
 #define MOE_INST_B1(WT, XT)                                                                 \
-  template hipError_t launch_decode_b1<WT, XT>(const XT *, int, const float *, const float *, \
-                                               int, const WT *, const WT *, const WT *, int,  \
-                                               int, int, XT *, float *, int32_t *, float *,   \
-                                               int32_t *, char *, hipStream_t);
+  template hipError_t launch_decode_b1<WT, XT>(const XT *, int, const void *, bool,           \
+                                               const float *, int, const WT *, const WT *,    \
+                                               const WT *, int, int, int, XT *, float *,      \
+                                               int32_t *, float *, int32_t *, char *,         \
+                                               hipStream_t);
 MOE_INST_B1(float, float)
 MOE_INST_B1(bf16_t, bf16_t)
 

@@ -46,9 +46,14 @@ hipError_t launch_plan(const int32_t *ids, int64_t n_assign, int E, int32_t *pla
 
 // Route with one workgroup per token; with plan != NULL (T*k1 <= 64) the last
 // block also builds the plan.  `ticket` is a zero word of the sync region.
+// wbf16 rounds the weights to bf16.
 hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int k2,
                              int32_t *ids, float *w, int32_t *ids2, float *w2, int32_t *plan,
-                             int32_t *ticket, hipStream_t s);
+                             int32_t *ticket, bool wbf16, hipStream_t s);
+
+// bf16 router: bf16 x and Wr, logits rounded to bf16 (stored as fp32)
+hipError_t launch_router_bf16(const bf16_t *x, int64_t T, int H, const bf16_t *Wr, int E,
+                              float *logits, float *logits2, hipStream_t s);
 
 template <typename WT, typename XT>
 hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan, int E,
@@ -70,17 +75,20 @@ struct B1Layout {
 bool decode_b1_supported(int H, int I, int k1, bool bf16);
 B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16);
 template <typename WT, typename XT>
-hipError_t launch_decode_b1(const XT *x, int H, const float *Wr, const float *br, int E,
-                            const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1, int k2,
-                            XT *y, float *logits_out, int32_t *ids_out, float *w_out,
+hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16, const float *br,
+                            int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
+                            int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
                             int32_t *sync, char *region, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);
 size_t prefill_plan_words(int64_t n, int E);
 hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipStream_t s);
+// nterms bf16 terms of the router weight; with one term the logits are
+// written directly, rounded to bf16 (the bf16 router), else the partial sums
 hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3, int E,
-                             float *part, hipStream_t s);
+                             int nterms, float *part, float *logits, float *logits2,
+                             hipStream_t s);
 hipError_t launch_router_sum(const float *part, int64_t T, int E, const float *br, float *logits,
                              float *logits2, hipStream_t s);
 hipError_t launch_prefill_plan(const int32_t *ids, int64_t n, int E, int32_t *plan,

@@ -181,10 +181,11 @@ struct Launches {
     if (rc_ != MOE_OK) return rc_;                    \
   } while (0)
 
-int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, const float *br,
-                    int32_t E, const uint16_t *Wg, const uint16_t *Wu, const uint16_t *Wd,
-                    int32_t I, int32_t k1, int32_t k2, uint16_t *y, float *logits_out,
-                    int32_t *ids_out, float *w_out, char *ws, Launches &run) {
+int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, bool router_bf16,
+                    const float *br, int32_t E, const uint16_t *Wg, const uint16_t *Wu,
+                    const uint16_t *Wd, int32_t I, int32_t k1, int32_t k2, uint16_t *y,
+                    float *logits_out, int32_t *ids_out, float *w_out, char *ws,
+                    Launches &run) {
   const PrefillLayout L = prefill_layout(T, H, E, I, k1);
   float *logits = reinterpret_cast<float *>(ws + L.logits);
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
@@ -195,12 +196,17 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, co
   uint16_t *zbf = reinterpret_cast<uint16_t *>(ws + L.zbf);
   const int64_t n = T * k1;
   const hipStream_t s = run.s;
-  RUN("split_router", moe::launch_split_router(Wr, E, H, w3, s));
-  float *part = reinterpret_cast<float *>(ws + L.part);
-  RUN("router_mma", moe::launch_router_mma(x, T, H, w3, E, part, s));
-  RUN("router_sum", moe::launch_router_sum(part, T, E, br, logits, logits_out, s));
+  if (router_bf16) {
+    RUN("router_mma", moe::launch_router_mma(x, T, H, static_cast<const uint16_t *>(Wr), E, 1,
+                                             nullptr, logits, logits_out, s));
+  } else {
+    RUN("split_router", moe::launch_split_router(static_cast<const float *>(Wr), E, H, w3, s));
+    float *part = reinterpret_cast<float *>(ws + L.part);
+    RUN("router_mma", moe::launch_router_mma(x, T, H, w3, E, 3, part, nullptr, nullptr, s));
+    RUN("router_sum", moe::launch_router_sum(part, T, E, br, logits, logits_out, s));
+  }
   RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
-                                      nullptr, s));
+                                      nullptr, router_bf16, s));
   RUN("prefill_plan", moe::launch_prefill_plan(ids, n, E, plan, s));
   RUN("gateup_mma", moe::launch_gateup_mma(x, H, Wg, Wu, I, plan, E, n, k1, w, abf, s));
   RUN("down_mma", moe::launch_down_mma(abf, H, Wd, I, plan, E, n, zbf, s));
@@ -209,21 +215,22 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const float *Wr, co
 }
 
 template <typename WT, typename XT>
-int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const float *br, int32_t E,
-                  const WT *Wg, const WT *Wu, const WT *Wd, int32_t I, int32_t k1, int32_t k2,
-                  XT *y, float *logits_out, int32_t *ids_out, float *w_out, Path path,
-                  char *ws, const Layout &L, Launches &run) {
+int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router_bf16,
+                  const float *br, int32_t E, const WT *Wg, const WT *Wu, const WT *Wd, int32_t I,
+                  int32_t k1, int32_t k2, XT *y, float *logits_out, int32_t *ids_out,
+                  float *w_out, Path path, char *ws, const Layout &L, Launches &run) {
   const hipStream_t s = run.s;
+  const float *Wr32 = static_cast<const float *>(Wr);  // meaningful without router_bf16
   if constexpr (sizeof(WT) == 2) {
     if (path == Path::Prefill)
-      return forward_prefill(reinterpret_cast<const uint16_t *>(x), T, H, Wr, br, E,
+      return forward_prefill(reinterpret_cast<const uint16_t *>(x), T, H, Wr, router_bf16, br, E,
                              reinterpret_cast<const uint16_t *>(Wg),
                              reinterpret_cast<const uint16_t *>(Wu),
                              reinterpret_cast<const uint16_t *>(Wd), I, k1, k2,
                              reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, run);
   }
   if (path == Path::Fused) {
-    RUN("fused_decode", (moe::launch_fused_decode<WT, XT>(x, T, H, Wr, br, E, Wg, Wu, Wd, I, k1,
+    RUN("fused_decode", (moe::launch_fused_decode<WT, XT>(x, T, H, Wr32, br, E, Wg, Wu, Wd, I, k1,
                                                           k2, y, logits_out, ids_out, w_out, ws,
                                                           s)));
     return MOE_OK;
@@ -238,23 +245,30 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const float *Wr, const floa
   const int64_t n_assign = T * k1;
   int32_t *ticket = sync + moe::kRouteTicketWord;
   if (T == 1 && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2)) {
-    RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, br, E, Wg, Wu, Wd, I, k1, k2, y,
-                                                   logits_out, ids_out, w_out, sync,
+    RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
+                                                   k1, k2, y, logits_out, ids_out, w_out, sync,
                                                    ws + L.tagged, s)));
     return MOE_OK;
   }
-  if (T == 1 && moe::router_route_supported(H)) {
-    RUN("router_route", moe::launch_router_route<XT>(x, H, Wr, br, E, k1, k2, logits, logits_out,
-                                                     ids, w, ids_out, w_out, plan, ticket, s));
+  if (T == 1 && !router_bf16 && moe::router_route_supported(H)) {
+    RUN("router_route", moe::launch_router_route<XT>(x, H, Wr32, br, E, k1, k2, logits,
+                                                     logits_out, ids, w, ids_out, w_out, plan,
+                                                     ticket, s));
     if (n_assign > 64) RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
   } else {
-    RUN("router", moe::launch_router<XT>(x, T, H, Wr, br, E, logits, logits_out, s));
+    if (router_bf16) {
+      if constexpr (sizeof(XT) == 2)
+        RUN("router", moe::launch_router_bf16(x, T, H, static_cast<const moe::bf16_t *>(Wr), E,
+                                              logits, logits_out, s));
+    } else {
+      RUN("router", moe::launch_router<XT>(x, T, H, Wr32, br, E, logits, logits_out, s));
+    }
     if (n_assign <= 64) {
       RUN("route_plan", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, plan,
-                                               ticket, s));
+                                               ticket, router_bf16, s));
     } else {
       RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
-                                          nullptr, s));
+                                          nullptr, router_bf16, s));
       RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
     }
   }
@@ -300,7 +314,7 @@ int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1, int32_t k2,
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
     return fail(MOE_EALIGN, "logits, ids and weights need 4-byte alignment");
   hipError_t e = moe::launch_route_plan(logits, T, E, k1, k2, ids, weights, nullptr, nullptr,
-                                        nullptr, nullptr, (hipStream_t)stream);
+                                        nullptr, nullptr, false, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "route kernel");
   return MOE_OK;
 }
@@ -315,7 +329,7 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   return workspace_bytes_for(T, H, E, I, k1);
 }
 
-int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const float *Wr,
+int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
                 const float *br, int32_t E, const void *Wgate, const void *Wup,
                 const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
                 float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
@@ -326,13 +340,22 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
   if (I < 8 || I % 8 != 0) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 8", I);
   if ((int64_t)H * I > (int64_t(1) << 31))
     return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
-  const uint32_t all = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
-  if (flags & ~all) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
-  if (__builtin_popcount(flags) > 1) return fail(MOE_EINVAL, "more than one path flag set");
+  const uint32_t paths = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
+  if (flags & ~(paths | MOE_FLAG_ROUTER_BF16))
+    return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if (__builtin_popcount(flags & paths) > 1)
+    return fail(MOE_EINVAL, "more than one path flag set");
+  const bool router_bf16 = (flags & MOE_FLAG_ROUTER_BF16) != 0;
   const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
   const bool b16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
   if (!f32 && !b16)
     return fail(MOE_ENOTSUP, "dtype pair (act=%d, w=%d) not supported", act_dtype, w_dtype);
+  if (router_bf16 && !b16)
+    return fail(MOE_ENOTSUP, "the bf16 router takes bf16 activations and weights");
+  if (router_bf16 && br)
+    return fail(MOE_EINVAL, "the bf16 router takes no bias (br must be NULL)");
+  if (router_bf16 && (flags & MOE_FLAG_FORCE_FUSED))
+    return fail(MOE_ENOTSUP, "the fused path has no bf16 router");
   if (T == 0) return MOE_OK;
   if (!x || !Wr || !Wgate || !Wup || !Wdown || !y) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wgate, 16) || !aligned(Wup, 16) ||
@@ -352,11 +375,11 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const fl
   char *ws = static_cast<char *>(workspace);
   if (f32)
     return forward_typed<float, float>(
-        static_cast<const float *>(x), T, H, Wr, br, E, static_cast<const float *>(Wgate),
+        static_cast<const float *>(x), T, H, Wr, false, br, E, static_cast<const float *>(Wgate),
         static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2,
         static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
   return forward_typed<moe::bf16_t, moe::bf16_t>(
-      static_cast<const moe::bf16_t *>(x), T, H, Wr, br, E,
+      static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
       static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
       static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, static_cast<moe::bf16_t *>(y),
       logits_out, ids_out, w_out, path, ws, L, run);

@@ -348,13 +348,18 @@ __global__ void split_router_kernel(const float *__restrict__ Wr, int64_t n,
 // Tile (64 tokens, 64 experts) of one term: part[term, t, e] = x[t] . W_term[e]
 // (fp32 accumulation).  The three terms run as separate workgroups (three
 // times the parallelism) and router_sum_kernel adds them in a fixed order.
+// With one term (a bf16 router weight, the router method on a bf16 model)
+// the tile is the logits themselves, rounded to bf16.
 // Experts beyond E read a valid row and are not stored.
 constexpr int RM = 64, RN = 64;
 
 __global__ __launch_bounds__(kThreads) void router_mma_kernel(const uint16_t *__restrict__ x,
                                                               int64_t T, int H,
                                                               const uint16_t *__restrict__ w3,
-                                                              int E, float *__restrict__ part) {
+                                                              int E, int nterms,
+                                                              float *__restrict__ part,
+                                                              float *__restrict__ logits,
+                                                              float *__restrict__ logits2) {
   __shared__ Tile<RM, RN> Tl;
   const int n_nt = (E + RN - 1) / RN;
   const int64_t n_tiles = ((T + RM - 1) / RM) * n_nt;
@@ -379,11 +384,23 @@ __global__ __launch_bounds__(kThreads) void router_mma_kernel(const uint16_t *__
     ld.brow[j] = w3 + (int64_t)term * E * H + (int64_t)e * H;
   }
   mma_k_loop<RM, RN>(Tl, ld, H, wm, wn, acc);
+  const int e = e0 + wn * 32 + (lane_id() & 31);
+  if (nterms == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + acc_row<RM>(wm, 0, r);
+      if (t < T && e < E) {
+        const float l = round_bf16(acc[0][0][r]);
+        logits[t * E + e] = l;
+        if (logits2) logits2[t * E + e] = l;
+      }
+    }
+    return;
+  }
   float *pt = part + (int64_t)term * T * E;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t t = t0 + acc_row<RM>(wm, 0, r);
-    const int e = e0 + wn * 32 + (lane_id() & 31);
     if (t < T && e < E) pt[t * E + e] = acc[0][0][r];
   }
 }
@@ -418,10 +435,11 @@ hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipS
 }
 
 hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3, int E,
-                             float *part, hipStream_t s) {
+                             int nterms, float *part, float *logits, float *logits2,
+                             hipStream_t s) {
   const int64_t tiles = ((T + pf::RM - 1) / pf::RM) * ((E + pf::RN - 1) / pf::RN);
-  pf::router_mma_kernel<<<dim3((unsigned)(3 * tiles)), dim3(pf::kThreads), 0, s>>>(x, T, H, w3, E,
-                                                                                   part);
+  pf::router_mma_kernel<<<dim3((unsigned)(nterms * tiles)), dim3(pf::kThreads), 0, s>>>(
+      x, T, H, w3, E, nterms, part, logits, logits2);
   return hipGetLastError();
 }
 

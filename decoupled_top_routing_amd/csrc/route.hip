@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
 // One workgroup per token.  With `plan`, the last block to finish (ticket)
 // also builds the batch plan (T*k1 <= 64); the ids it reads were stored
 // device-coherently by the other blocks.  The ticket word is zero before
-// and after the kernel.
+// and after the kernel.  wbf16 rounds the weights to bf16.
 template <int V>
 __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict__ logits,
                                                          int64_t T, int E, int k1, int k2,
@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict
                                                          int32_t *__restrict__ ids2,
                                                          float *__restrict__ w2,
                                                          int32_t *__restrict__ plan,
-                                                         int32_t *__restrict__ ticket) {
+                                                         int32_t *__restrict__ ticket,
+                                                         bool wbf16) {
   __shared__ float sl[kBlockThreads];
   __shared__ int32_t s_ids[kMaxExperts];
   __shared__ float s_w[kMaxExperts];
@@ -55,9 +56,9 @@ __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict
   if (E <= kBlockThreads) {
     if (tid < E) sl[tid] = lrow[tid];
     __syncthreads();
-    route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S);
+    route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S, wbf16);
   } else {
-    route_into_lds<V>(lrow, E, k1, k2, s_ids, s_w, S);
+    route_into_lds<V>(lrow, E, k1, k2, s_ids, s_w, S, wbf16);
   }
   const int64_t o = t * k1;
   for (int r = tid; r < k1; r += kBlockThreads) {
@@ -77,18 +78,18 @@ __global__ __launch_bounds__(256) void route_plan_kernel(const float *__restrict
 
 hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int k2,
                              int32_t *ids, float *w, int32_t *ids2, float *w2, int32_t *plan,
-                             int32_t *ticket, hipStream_t s) {
+                             int32_t *ticket, bool wbf16, hipStream_t s) {
   const dim3 grid((unsigned)T), block(256);
   if (E <= 64)
-    route_plan_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+    route_plan_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   else if (E <= 128)
-    route_plan_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+    route_plan_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   else if (E <= 256)
-    route_plan_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+    route_plan_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   else if (E <= 512)
-    route_plan_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+    route_plan_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   else
-    route_plan_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket);
+    route_plan_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   return hipGetLastError();
 }
 
@@ -218,6 +219,56 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__
       }
     }
   }
+}
+
+// bf16 router (the router method on a bf16 model): logits[t, e] =
+// bf16(sum_h x[t, h] Wr[e, h]) with bf16 x and Wr, the products exact and the
+// sum in fp32, rounded once to bf16 (kept as fp32 values).  One wave per
+// (expert, group of kRowsTok tokens); lanes take 16-byte chunks of the row
+// and of x, four tokens per pass.
+__global__ __launch_bounds__(256) void router_bf16_kernel(const bf16_t *__restrict__ x, int64_t T,
+                                                          int H, const bf16_t *__restrict__ Wr,
+                                                          int E, float *__restrict__ logits,
+                                                          float *__restrict__ logits2) {
+  const int n_eb = (E + 3) / 4;
+  const int64_t tg = blockIdx.x / n_eb;
+  const int e = (int)(blockIdx.x - tg * n_eb) * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int lane = lane_id();
+  const bf16_t *wrow = Wr + (int64_t)e * H;
+  const int nch = H / 8;
+  const int64_t t_end = min<int64_t>(T, (tg + 1) * kRowsTok);
+  for (int64_t t0 = tg * kRowsTok; t0 < t_end; t0 += 4) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = lane; c < nch; c += kWave) {
+      const uint4 wq = ld16(wrow + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t t = min<int64_t>(t0 + q, t_end - 1);
+        const uint4 xq = ld16(x + t * H + c * 8);
+        acc[q] = dot2_bf16(wq.x, xq.x, acc[q]);
+        acc[q] = dot2_bf16(wq.y, xq.y, acc[q]);
+        acc[q] = dot2_bf16(wq.z, xq.z, acc[q]);
+        acc[q] = dot2_bf16(wq.w, xq.w, acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float l = round_bf16(wave_sum_dpp(acc[q]));
+      const int64_t t = t0 + q;
+      if (lane == 0 && t < t_end) {
+        logits[t * E + e] = l;
+        if (logits2) logits2[t * E + e] = l;
+      }
+    }
+  }
+}
+
+hipError_t launch_router_bf16(const bf16_t *x, int64_t T, int H, const bf16_t *Wr, int E,
+                              float *logits, float *logits2, hipStream_t s) {
+  const dim3 grid((unsigned)(((E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok))), block(256);
+  router_bf16_kernel<<<grid, block, 0, s>>>(x, T, H, Wr, E, logits, logits2);
+  return hipGetLastError();
 }
 
 // One token: router, route and plan in one launch.  Wave e computes logit

@@ -69,14 +69,17 @@ __device__ __forceinline__ float exp_nonpos(float d) {
 //     Only the first R = min(k2, E) ranks are read (k1 when k2 >= E: no mass
 //     needed);
 //  6. M = p_(0) + p_(1) + ... left to right over the min(k2, E) ranked values;
-//     w_r = p_(r) / M, or p_(r) when k2 >= E.
+//     w_r = p_(r) / M, or p_(r) when k2 >= E;
+//  7. with wbf16 (the router run on a bf16 model, where the method casts the
+//     weights to the logits' dtype), w_r is then rounded to bf16.
 // Rank r is held by lane r % 64 in slot r / 64 until the end.
 // COHERENT: read the logits with device-coherent loads (they were written by
 // other workgroups of the same kernel).  ids and w may point to LDS.
 template <int V, bool COHERENT = false>
 __device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
                             int32_t *__restrict__ ids, float *__restrict__ w,
-                            int32_t *__restrict__ ids2, float *__restrict__ w2) {
+                            int32_t *__restrict__ ids2, float *__restrict__ w2,
+                            bool wbf16 = false) {
 #pragma clang fp contract(off)
   const int lane = lane_id();
   float ex[V];
@@ -210,7 +213,8 @@ __device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
   for (int q = 0; q < V; ++q) {
     const int r = q * kWave + lane;
     if (r < k1) {
-      const float wr = renorm ? my_p[q] / M : my_p[q];
+      float wr = renorm ? my_p[q] / M : my_p[q];
+      if (wbf16) wr = round_bf16(wr);
       ids[r] = my_id[q];
       w[r] = wr;
       if (ids2) ids2[r] = my_id[q];
@@ -227,7 +231,8 @@ constexpr int kBlockWaves = kBlockThreads / kWave;
 // (each wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
 // (p descending, index ascending) counted in parallel (element e by
 // min(256 / P, P) threads, P = next_pow2(E), each over a slice of the keys);
-// the mass summed in rank order by one thread; w = p / M or p.
+// the mass summed in rank order by one thread; w = p / M or p, rounded to
+// bf16 with wbf16.
 
 struct BlockRoute {
   alignas(16) uint64_t K[kBlockThreads];
@@ -239,7 +244,8 @@ struct BlockRoute {
 };
 
 __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
-                                  int32_t *ids_out, float *w_out, BlockRoute &S) {
+                                  int32_t *ids_out, float *w_out, BlockRoute &S,
+                                  bool wbf16 = false) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const bool valid = tid < E;
@@ -318,7 +324,8 @@ __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t
   }
   __syncthreads();
   if (tid < k1) {
-    const float wr = renorm ? S.sp[tid] / S.M : S.sp[tid];
+    float wr = renorm ? S.sp[tid] / S.M : S.sp[tid];
+    if (wbf16) wr = round_bf16(wr);
     ids[tid] = S.sid[tid];
     w[tid] = wr;
     if (ids_out) ids_out[tid] = S.sid[tid];
@@ -375,14 +382,15 @@ __device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
 }
 
 // Route one token into LDS (s_ids, s_w: rank order), by the whole block
-// (E <= 256, k1 <= 256) or by its first wave.
+// (E <= 256, k1 <= 256) or by its first wave; wbf16 rounds the weights to
+// bf16.
 template <int V>
 __device__ void route_into_lds(const float *l, int E, int k1, int k2, int32_t *s_ids, float *s_w,
-                               BlockRoute &S) {
+                               BlockRoute &S, bool wbf16 = false) {
   if (E <= kBlockThreads && k1 <= kBlockThreads) {
-    route_token_block(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S);
+    route_token_block(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
   } else {
-    if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr);
+    if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, wbf16);
     __syncthreads();
   }
 }

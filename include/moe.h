@@ -79,6 +79,23 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_FLAG_FORCE_GROUPED 2u
 #define MOE_FLAG_FORCE_PREFILL 4u
 
+/* moe_forward flag: the bf16 router -- the router method of "Paper of the
+ * Week #3" (section "Ship It - Code of the Week") as it runs on a bf16 model,
+ * where the linear layer runs in the model's dtype and the weights are cast
+ * back to the logits' dtype.  With it:
+ *   Wr is bf16 [E, H] and br must be NULL (MOE_EINVAL otherwise);
+ *   logits[t, e] = bf16(x[t] . Wr[e]): fp32 accumulation of the exact bf16
+ *       products, rounded once to bf16 (nearest, ties to even);
+ *   the softmax, ranking and Eq. 2 run in fp32 on those logits, exactly as
+ *       without the flag;
+ *   each weight is then rounded to bf16, and the experts are scaled by it.
+ * logits_out and w_out still receive fp32 arrays, holding the bf16 values.
+ * At k1 = k2 this is the stock renormalising bf16 router.  It needs the
+ * (BF16, BF16) dtype pair (MOE_ENOTSUP otherwise) and combines with
+ * MOE_FLAG_FORCE_GROUPED or MOE_FLAG_FORCE_PREFILL; with
+ * MOE_FLAG_FORCE_FUSED it returns MOE_ENOTSUP. */
+#define MOE_FLAG_ROUTER_BF16 8u
+
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
@@ -117,7 +134,8 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *   e = ids[t,r],  logits[t] = Wr x[t] (+ br).
  *
  *   x      [T, H]    act_dtype (MOE_F32 or MOE_BF16)          16-byte aligned
- *   Wr     [E, H]    fp32 router weight                       16-byte aligned
+ *   Wr     [E, H]    fp32 router weight (bf16 with MOE_FLAG_ROUTER_BF16)
+ *                                                            16-byte aligned
  *   br     [E]       fp32 router bias, or NULL                 4-byte aligned
  *   Wgate  [E, I, H] w_dtype: row c of expert e = gate row of channel c
  *   Wup    [E, I, H] w_dtype: row c of expert e = up row of channel c
@@ -131,7 +149,8 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *          leaves its synchronisation words at zero after every call, so one
  *          zero fill at allocation lasts for the workspace's lifetime.  Calls
  *          that run concurrently need separate workspaces.
- *   flags: 0 or one MOE_FLAG_FORCE_* value.
+ *   flags: 0 or one MOE_FLAG_FORCE_* value, optionally with
+ *          MOE_FLAG_ROUTER_BF16.
  *
  *   Supported dtype pairs (act, w): (F32, F32) and (BF16, BF16); accumulation
  *   is fp32.  1 <= E <= 1024; H and I multiples of 8; 1 <= k1 <= E;
@@ -139,7 +158,7 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *   Identical inputs give bitwise identical logits, ids, weights and y.
  */
 int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
-                const float *Wr, const float *br, int32_t E,
+                const void *Wr, const float *br, int32_t E,
                 const void *Wgate, const void *Wup, const void *Wdown,
                 int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
                 float *logits_out, int32_t *ids_out, float *w_out,
@@ -155,7 +174,7 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
  * owned by the caller (NULL disarms).  Returns MOE_EINVAL for launch < 0.
  *
  * moe_profile_launch_name -- the kernel name of the launch bracketed by the
- * last armed call on this thread ("" if none was), e.g. "b1_front".
+ * last armed call on this thread ("" if none was), e.g. "b1_layer".
  */
 int moe_profile_launch(int32_t launch, void *start, void *stop);
 const char *moe_profile_launch_name(void);

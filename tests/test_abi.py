@@ -96,6 +96,9 @@ def _fwd(lib, **kw):
     (dict(ws=None), 3), (dict(ws=128), 3), (dict(wsb=1024), 3),
     (dict(x=None), 1), (dict(flags=3), 1), (dict(flags=16), 1),
     (dict(flags=4, act=0, wt=0), 4), (dict(flags=4, I=776), 4), (dict(flags=4, H=2056), 4),
+    # the bf16 router: bf16 pair only, no bias, not on the fused path
+    (dict(flags=8, act=0, wt=0), 4), (dict(flags=8, br=16), 1), (dict(flags=9), 4),
+    (dict(flags=8 | 3), 1), (dict(flags=8 | 32), 1),
 ])
 def test_forward_rejects_bad_arguments(kw, code):
     lib = moe.load_library()

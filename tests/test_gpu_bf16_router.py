@@ -1,0 +1,157 @@
+"""The bf16 router (MOE_FLAG_ROUTER_BF16) on the GPU against the oracle.
+
+The router method of "Paper of the Week #3 - Half the FLOPs Is Not Half the
+Time" (section "Ship It - Code of the Week") on a bf16 model: bf16 logits,
+fp32 softmax and Eq. 2, weights cast to bf16.  For every path:
+(i) the GPU's logits are bf16 values within one bf16 step of the oracle's
+exact-then-rounded logits; (ii) the oracle's bf16-weight route on the GPU's
+own logits equals the GPU's ids and weights bit for bit, and at k1 = k2 both
+equal the stock renormalising router, cast included; (iii) y matches the
+oracle's experts on that route within the bf16 tolerance; (iv) an
+independent oracle route picks the same experts on every token whose logits
+came out identical.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import decoupled_top_routing_amd as moe
+import oracle
+from decoupled_top_routing_amd import synth
+from parity import TOL_BF16, bits, host_layer, normwise_err, to_dev, to_f64
+from test_oracle_bf16_router_pins import stock_router
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_steps(a, b):
+    """Distance between float32 arrays of bf16 values, in bf16 steps."""
+    def key(v):
+        u = (np.ascontiguousarray(v, np.float32).view(np.uint32) >> 16).astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(key(a) - key(b))
+
+
+def with_bf16_router(L):
+    """The layer with its router weight cast to bf16 and no bias."""
+    return dict(L, Wr=L["Wr"].to(torch.bfloat16), br=None)
+
+
+def check_bf16_router(name, L, Lh, k1, k2, flags=0, token_sample=None):
+    g = to_dev(L) if L["Wg"].device.type == "cpu" else L
+    print(f"{name} T={g['x'].shape[0]} k1={k1} k2={k2} flags={flags} bf16 router", flush=True)
+    assert g["Wr"].dtype == torch.bfloat16 and g["br"] is None
+    y, lg, ids, w = moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], k1, k2,
+                                return_route=True, flags=flags)
+    torch.cuda.synchronize()
+    lg_h = lg.cpu().numpy()
+    T = lg_h.shape[0]
+    sel = np.arange(T) if token_sample is None else np.asarray(token_sample)
+    # (i) logits: bf16 values, within one bf16 step of the oracle
+    assert not (lg_h.view(np.uint32) & 0xFFFF).any(), "logits are not bf16 values"
+    x_h = Lh["x"][sel]
+    ref_l = oracle.logits_bf16(x_h, synth.to_numpy(g["Wr"].cpu()), nthreads=8)
+    assert bf16_steps(lg_h[sel], ref_l).max() <= 1
+    # (ii) route on the GPU's logits, bit for bit
+    oids, ow = oracle.route_bf16w(lg_h, k1, k2)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    bad = np.nonzero((gi != oids).any(1) | (bits(gw) != bits(ow)).any(1))[0]
+    assert bad.size == 0, f"{bad.size} tokens differ, first {bad[:5]}"
+    if k1 == k2:
+        p = oracle.softmax(lg_h)
+        for t in range(min(T, 64)):
+            sid, sw = stock_router(p[t], k1)
+            assert np.array_equal(gi[t], sid) and np.array_equal(bits(gw[t]), bits(sw)), t
+    # (iii) y on that route
+    Wg, Wu, Wd = Lh["Wg"], Lh["Wu"], Lh["Wd"]
+    y_ref = oracle.experts(x_h, Wg, Wu, Wd, oids[sel], ow[sel], nthreads=8)
+    err = normwise_err(to_f64(y)[sel], y_ref)
+    assert err <= TOL_BF16, f"normwise error {err} > {TOL_BF16}"
+    # (iv) independent route: same experts wherever the logits agree exactly
+    iids, _ = oracle.route_bf16w(ref_l, k1, k2)
+    same_logits = (bits(lg_h[sel]) == bits(ref_l)).all(1)
+    differ = (iids != gi[sel]).any(1)
+    assert not (differ & same_logits).any()
+    return err
+
+
+@pytest.fixture(scope="module")
+def a3b():
+    L = with_bf16_router(to_dev(synth.make_layer(synth.DECODE_B8)))
+    return L, host_layer(L)
+
+
+@pytest.mark.parametrize("k1,k2", [(8, 8), (4, 4), (4, 16), (2, 16), (3, 16), (4, 128)])
+@pytest.mark.parametrize("T", [1, 8])
+def test_bf16_router_decode(a3b, k1, k2, T):
+    """T = 1 runs the one-launch kernel, T = 8 the grouped path."""
+    L, Lh = a3b
+    check_bf16_router(synth.DECODE_B8.name, dict(L, x=L["x"][:T]), dict(Lh, x=Lh["x"][:T]),
+                      k1, k2)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_bf16_router_forced_grouped(a3b, T):
+    L, Lh = a3b
+    check_bf16_router(synth.DECODE_B8.name, dict(L, x=L["x"][:T]), dict(Lh, x=Lh["x"][:T]),
+                      4, 16, flags=moe.FORCE_GROUPED)
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    L = with_bf16_router(to_dev(synth.make_layer(synth.PREFILL)))
+    return L, host_layer(L)
+
+
+@pytest.mark.parametrize("k1,k2", synth.PREFILL.k_pairs)
+def test_bf16_router_prefill_4096(prefill, k1, k2):
+    L, Lh = prefill
+    rng = np.random.default_rng(12)
+    sample = np.array(sorted(set(rng.choice(4096, 64, replace=False).tolist()) | {0, 4095}))
+    check_bf16_router(synth.PREFILL.name, L, Lh, k1, k2, token_sample=sample)
+
+
+@pytest.mark.parametrize("T", [1, 63, 300])
+@pytest.mark.parametrize("flags", [moe.FORCE_PREFILL, moe.FORCE_GROUPED])
+def test_bf16_router_paths_on_small_batches(prefill, T, flags):
+    L, Lh = prefill
+    check_bf16_router(synth.PREFILL.name, dict(L, x=L["x"][:T]), dict(Lh, x=Lh["x"][:T]),
+                      4, 16, flags=flags)
+
+
+SMALL = replace(synth.TINY, dtype="bf16", rms_norm_x=True, router_var_times_H=4.0)
+
+
+@pytest.mark.parametrize("E,k1,k2,H,I,T,flags", [
+    (40, 3, 7, 264, 72, 1, 0),        # no one-launch shape: grouped at T = 1, ragged rows
+    (40, 3, 7, 264, 72, 5, 0),
+    (300, 6, 12, 512, 64, 1, 0),      # E > 256: the one-launch kernel's wave route
+    (300, 6, 12, 512, 64, 8, 0),      # E > 256 on the grouped path
+    (1, 1, 1, 256, 64, 3, 0),         # one expert: p = 1, w = 1
+    (33, 5, 9, 1024, 192, 257, moe.FORCE_PREFILL),  # E not a multiple of the router tile
+])
+def test_bf16_router_edge_shapes(E, k1, k2, H, I, T, flags):
+    cfg = replace(SMALL, name=f"hf-E{E}-H{H}-I{I}", T=T, H=H, E=E, I=I)
+    L = with_bf16_router(to_dev(synth.make_layer(cfg)))
+    check_bf16_router(cfg.name, L, host_layer(L), k1, k2, flags=flags)
+
+
+def test_bf16_router_is_deterministic(a3b):
+    L, _ = a3b
+    outs = [moe.forward(L["x"], L["Wr"], L["Wg"], L["Wu"], L["Wd"], 4, 16, return_route=True)
+            for _ in range(2)]
+    for u, v in zip(*outs):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+def test_bf16_router_rejected_where_unsupported(a3b):
+    L, _ = a3b
+    with pytest.raises(moe.MoeError):   # the fused path has no bf16 router
+        moe.forward(L["x"][:1], L["Wr"], L["Wg"], L["Wu"], L["Wd"], 4, 16,
+                    flags=moe.FORCE_FUSED)
+    with pytest.raises(moe.MoeError):   # no bias with the bf16 router
+        moe.forward(L["x"][:1], L["Wr"], L["Wg"], L["Wu"], L["Wd"], 4, 16,
+                    br=torch.zeros(L["Wr"].shape[0], device=L["x"].device))
