@@ -38,6 +38,12 @@ the linear layer in bf16 (the exact dot product rounded once to bf16, to
 nearest with ties to even), the softmax upcast to fp32, and the weights cast
 back to bf16 (same rounding) before they scale the experts.
 
+The shared expert (``shared``) always runs beside the routed ones ("Channel
+Selection for Mixture-of-Experts Decoding Needs No Calibration Data",
+appendix B): a gated MLP of Is channels whose output is added to the routed
+sum, scaled by sigmoid(x . sg) with a gate vector sg, else by 1 (a reading:
+the pages do not give the gating).
+
 The route functions (``softmax``, ``route``) are exact fp32 definitions; the
 expert functions are accumulated in fp64.  Arrays are numpy; bf16 tensors are
 passed as ``uint16`` bit patterns.
@@ -115,6 +121,8 @@ def _open(path):
     lib.oracle_forward_bf16_router.restype = cint
     lib.oracle_forward_bf16_router.argtypes = [P, i64, i32, P, i32, P, P, P, i32,
                                                i32, i32, P, P, P, P, cint]
+    lib.oracle_shared.restype = cint
+    lib.oracle_shared.argtypes = [P, cint, i64, i32, P, P, P, cint, i32, P, P, cint]
     return lib
 
 
@@ -300,3 +308,21 @@ def forward_bf16_router(x, Wr, Wg, Wu, Wd, k1: int, k2: int, nthreads: int = 1):
                                           _ptr(Wd), I, k1, k2, _ptr(y), _ptr(lg), _ptr(ids),
                                           _ptr(w), nthreads), "oracle_forward_bf16_router")
     return y, lg, ids, w
+
+
+def shared(x, Sg, Su, Sd, sg=None, nthreads: int = 1):
+    """The shared expert's term [T,H] float32: g * Sd (silu(Sg x) * (Su x)),
+    g = sigmoid(x . sg) (sg [H] float32) or 1 without sg."""
+    lib = _load()
+    x = _c(x)
+    Sg, Su, Sd = _c(Sg), _c(Su), _c(Sd)
+    T, H = x.shape
+    Is = Sg.shape[0]
+    assert Sg.shape == (Is, H) and Su.shape == Sg.shape and Sd.shape == (H, Is)
+    wt = _dtype_code(Sg)
+    assert _dtype_code(Su) == wt and _dtype_code(Sd) == wt
+    sg = None if sg is None else _c(sg, np.float32)
+    ys = np.empty((T, H), np.float32)
+    _check(lib.oracle_shared(_ptr(x), _dtype_code(x), T, H, _ptr(Sg), _ptr(Su), _ptr(Sd), wt,
+                             Is, _ptr(sg), _ptr(ys), nthreads), "oracle_shared")
+    return ys

@@ -458,3 +458,68 @@ int oracle_forward_bf16_router(const uint16_t *x, int64_t T, int32_t H,
     return oracle_experts(x, OR_BF16, T, H, Wg, Wu, Wd, OR_BF16, E, I, k1, ids,
                           w, y, nthreads);
 }
+
+/* ================================================================== */
+/* Shared expert ("Channel Selection for Mixture-of-Experts Decoding  */
+/* Needs No Calibration Data", appendix B "Experimental setup": shared */
+/* experts always run in full, beside the routed ones).  The pages do  */
+/* not give its gating; the reading taken: the shared expert is a     */
+/* gated MLP like a routed one, with Is channels, added to the routed */
+/* sum with the factor g = sigmoid(x . sg) when a gate vector sg is   */
+/* given and g = 1 without one:                                       */
+/*   y = sum_r w_r E_{id_r}(x) + g * Sd (silu(Sg x) * (Su x)).         */
+/* fp64 throughout, rounded once to fp32.                             */
+/* ================================================================== */
+int oracle_shared(const void *x, int act, int64_t T, int32_t H,
+                  const void *Sg, const void *Su, const void *Sd, int wt,
+                  int32_t Is, const float *sg, float *ys, int nthreads)
+{
+    if (T < 0 || H < 1 || Is < 1 || (act != OR_F32 && act != OR_BF16) ||
+        (wt != OR_F32 && wt != OR_BF16))
+        return OR_EINVAL;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+    for (int64_t t = 0; t < T; ++t) {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+        double *a = (double *)malloc(sizeof(double) * (size_t)Is);
+        if (!xv || !a) {
+            free(xv); free(a);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            bad = 1;
+            continue;
+        }
+        for (int32_t h = 0; h < H; ++h)
+            xv[h] = load_elem(x, act, t * H + h);
+        double g = 1.0;
+        if (sg) {
+            double z = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                z += xv[h] * (double)sg[h];
+            g = 1.0 / (1.0 + exp(-z));
+        }
+        for (int32_t c = 0; c < Is; ++c) {
+            int64_t row = (int64_t)c * H;
+            double gg = 0.0, u = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                gg += load_elem(Sg, wt, row + h) * xv[h];
+                u += load_elem(Su, wt, row + h) * xv[h];
+            }
+            a[c] = silu(gg) * u;
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            int64_t row = (int64_t)h * Is;
+            double z = 0.0;
+            for (int32_t c = 0; c < Is; ++c)
+                z += load_elem(Sd, wt, row + c) * a[c];
+            ys[t * H + h] = (float)(g * z);
+        }
+        free(xv); free(a);
+    }
+    return bad ? OR_ENOMEM : OR_OK;
+}

@@ -11,6 +11,7 @@ import pytest
 import oracle
 import test_oracle_bf16_router_pins as hf_pins
 import test_oracle_pins as pins
+import test_oracle_shared_pins as shared_pins
 
 MUTANTS = {
     "tie break takes the higher index":
@@ -51,6 +52,14 @@ MUTANTS = {
         ("logits[t * E + e] = round_bf16(s);", "logits[t * E + e] = (float)s;"),
     "bf16 router weights not cast":
         ("w[i] = round_bf16((double)w[i]);", "w[i] = w[i];"),
+    "shared expert gate not applied":
+        ("ys[t * H + h] = (float)(g * z);", "ys[t * H + h] = (float)z;"),
+    "shared expert gate with the wrong sign":
+        ("g = 1.0 / (1.0 + exp(-z));", "g = 1.0 / (1.0 + exp(z));"),
+    "shared expert silu on the up projection":
+        ("a[c] = silu(gg) * u;", "a[c] = gg * silu(u);"),
+    "shared expert gate and up read the same row":
+        ("u += load_elem(Su, wt, row + h) * xv[h];", "u += load_elem(Sg, wt, row + h) * xv[h];"),
 }
 
 PIN_CHECKS = [
@@ -70,6 +79,8 @@ PIN_CHECKS = [
     hf_pins.test_round_bf16_matches_torch_cast_from_fp32,
     hf_pins.test_bf16_logits_are_the_exact_dot_product_rounded_once,
     lambda: hf_pins.test_bf16_router_at_k1_eq_k2_is_stock_bitwise(128, 8),
+    lambda: shared_pins.test_shared_matches_numpy_fp64(False, True),
+    shared_pins.test_zero_gate_vector_halves_the_expert,
 ]
 
 
