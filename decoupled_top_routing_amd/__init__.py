@@ -70,6 +70,12 @@ def load_library():
         lib.moe_forward.restype = ctypes.c_int
         lib.moe_forward.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
                                     i32, P, P, P, P, u32, P, ctypes.c_size_t, P]
+        lib.moe_forward_shared.restype = ctypes.c_int
+        lib.moe_forward_shared.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
+                                           i32, P, P, P, i32, P, P, P, P, P, u32, P,
+                                           ctypes.c_size_t, P]
+        lib.moe_forward_shared_workspace.restype = ctypes.c_size_t
+        lib.moe_forward_shared_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
         lib.moe_profile_launch.restype = ctypes.c_int
         lib.moe_profile_launch.argtypes = [i32, P, P]
         lib.moe_profile_launch_name.restype = ctypes.c_char_p
@@ -154,7 +160,8 @@ def _workspace(device, stream_ptr: int, nbytes: int) -> torch.Tensor:
 
 
 def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
-            return_route: bool = False, flags: int = 0, out=None, workspace=None):
+            return_route: bool = False, flags: int = 0, out=None, workspace=None,
+            shared=None):
     """The whole routed MoE layer.
 
     x [T,H] (fp32 or bf16), Wr [E,H] fp32, br [E] fp32 or None, Wgate and Wup
@@ -163,7 +170,11 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
 
     A bf16 ``Wr`` selects the bf16 router (``ROUTER_BF16``, the page's router
     method on a bf16 model): bf16 logits, fp32 softmax and Eq. 2, weights
-    rounded to bf16; it takes bf16 x and expert weights and no ``br``.  ``out`` receives y if
+    rounded to bf16; it takes bf16 x and expert weights and no ``br``.
+
+    ``shared`` = (Sgate [Is,H], Sup [Is,H], Sdown [H,Is]) or the same with a
+    fourth fp32 gate vector sgate [H] adds the shared expert, which runs on
+    every token: y += sigmoid(x . sgate) (or 1) * Sdown(silu(Sgate x) * Sup x).  ``out`` receives y if
     given; ``workspace`` is an optional zero-filled uint8 device tensor of at
     least ``moe_forward_workspace`` bytes (needed under graph capture, where
     nothing may be allocated).
@@ -183,6 +194,19 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
     if H2 != H or Wup.shape != Wgate.shape or tuple(Wdown.shape) != (E, H, I) \
             or tuple(Wr.shape) != (E, H):
         raise MoeError(1, "shape mismatch between x, Wr, Wgate, Wup and Wdown")
+    Is, sgate = 0, None
+    if shared is not None:
+        Sg, Su, Sd = shared[:3]
+        sgate = shared[3] if len(shared) > 3 else None
+        for n, t in (("Sgate", Sg), ("Sup", Su), ("Sdown", Sd)):
+            _need_cuda(n, t, x.dtype)
+        Is = Sg.shape[0]
+        if tuple(Sg.shape) != (Is, H) or Su.shape != Sg.shape or tuple(Sd.shape) != (H, Is):
+            raise MoeError(1, "shape mismatch between x, Sgate, Sup and Sdown")
+        if sgate is not None:
+            _need_cuda("sgate", sgate, torch.float32)
+            if tuple(sgate.shape) != (H,):
+                raise MoeError(1, "sgate must be [H]")
     dev = x.device
     y = out if out is not None else torch.empty((T, H), dtype=x.dtype, device=dev)
     lg = ids = w = None
@@ -190,7 +214,7 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
         lg = torch.empty((T, E), dtype=torch.float32, device=dev)
         ids = torch.empty((T, k1), dtype=torch.int32, device=dev)
         w = torch.empty((T, k1), dtype=torch.float32, device=dev)
-    nbytes = lib.moe_forward_workspace(T, H, E, I, k1, act, act)
+    nbytes = lib.moe_forward_shared_workspace(T, H, E, I, k1, Is, act, act)
     if nbytes == 0 and T > 0:
         raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
     stream = _stream(dev)
@@ -199,9 +223,15 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
         ws = workspace
     else:
         ws = _workspace(dev, stream.value or 0, nbytes)
-    _check(lib.moe_forward(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
-                           _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(y), _ptr(lg),
-                           _ptr(ids), _ptr(w), flags, _ptr(ws), ws.numel(), stream))
+    if shared is None:
+        _check(lib.moe_forward(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
+                               _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(y), _ptr(lg),
+                               _ptr(ids), _ptr(w), flags, _ptr(ws), ws.numel(), stream))
+    else:
+        _check(lib.moe_forward_shared(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
+                                      _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(Sg), _ptr(Su),
+                                      _ptr(Sd), Is, _ptr(sgate), _ptr(y), _ptr(lg), _ptr(ids),
+                                      _ptr(w), flags, _ptr(ws), ws.numel(), stream))
     if return_route:
         return y, lg, ids, w
     return y

@@ -480,22 +480,74 @@ hipError_t launch_down_one_token(const WT *Wd, int H, int I, const int32_t *plan
 }
 
 // ---------------------------------------------------------------- combine
-// y[t,h] = sum over the token's k1 slots of z[t*k1 + r, h], in slot order.
+// y[t,h] = sum over the token's k1 slots of z[t*k1 + r, h], in slot order,
+// then the shared expert's term zs[t, h] if there is one.
 template <typename XT>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ zbuf, int64_t T,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ zbuf,
+                                                      const float *__restrict__ zs, int64_t T,
                                                       int H, int k1, XT *__restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= T * H) return;
   const int64_t t = i / H, h = i - t * H;
   float s = 0.0f;
   for (int r = 0; r < k1; ++r) s = s + zbuf[(t * k1 + r) * H + h];
+  if (zs) s = s + zs[i];
   Elem<XT>::store1(y + i, s);
 }
 
 template <typename XT>
-hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hipStream_t s) {
+hipError_t launch_combine(const float *zbuf, const float *zs, int64_t T, int H, int k1, XT *y,
+                          hipStream_t s) {
   const int64_t n = T * H;
-  combine_kernel<XT><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(zbuf, T, H, k1, y);
+  combine_kernel<XT><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(zbuf, zs, T, H, k1,
+                                                                             y);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- shared expert
+// The shared expert ("Channel Selection for Mixture-of-Experts Decoding Needs
+// No Calibration Data", appendix B: shared experts always run in full) runs
+// as a one-expert layer over every token.  This kernel writes its plan in
+// the layout above for E = 1 (one unique expert holding assignments 0..T-1
+// in order), zero ids for the prefill plan (either may be NULL), and the
+// factor gs[t] = sigmoid(x[t] . sg), or 1 without sg.  One wave per token.
+template <typename XT>
+__global__ __launch_bounds__(256) void shared_prep_kernel(const XT *__restrict__ x, int64_t T,
+                                                          int H, const float *__restrict__ sgw,
+                                                          int32_t *__restrict__ plan,
+                                                          int32_t *__restrict__ ids0,
+                                                          float *__restrict__ gs) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (plan && blockIdx.x == 0 && threadIdx.x == 0) {
+    plan[0] = 1;             // U
+    plan[4] = 0;             // uniq[0]
+    plan[5] = 0;             // off[0]
+    plan[6] = (int32_t)T;    // off[1]
+  }
+  if (t >= T) return;
+  const int lane = lane_id();
+  float g = 1.0f;
+  if (sgw) {
+    const XT *xr = x + t * H;
+    float z = 0.0f;
+    for (int h = lane; h < H; h += kWave) z = __builtin_fmaf(Elem<XT>::load1(xr + h), sgw[h], z);
+    z = wave_sum_dpp(z);
+    g = 1.0f / (1.0f + __expf(-z));
+  }
+  if (lane == 0) {
+    if (plan) plan[7 + t] = (int32_t)t;  // list
+    if (ids0) ids0[t] = 0;
+    gs[t] = g;
+  }
+}
+
+size_t shared_plan_words(int64_t T) { return 7 + (size_t)T; }
+
+template <typename XT>
+hipError_t launch_shared_prep(const XT *x, int64_t T, int H, const float *sgw, int32_t *plan,
+                              int32_t *ids0, float *gs, hipStream_t s) {
+  shared_prep_kernel<XT><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(x, T, H, sgw, plan,
+                                                                             ids0, gs);
   return hipGetLastError();
 }
 
@@ -505,7 +557,10 @@ hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hi
                                             const float *, float *, hipStream_t);         \
   template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t, \
                                       const float *, float *, hipStream_t);               \
-  template hipError_t launch_combine<XT>(const float *, int64_t, int, int, XT *, hipStream_t); \
+  template hipError_t launch_combine<XT>(const float *, const float *, int64_t, int, int, XT *, \
+                                         hipStream_t);                                        \
+  template hipError_t launch_shared_prep<XT>(const XT *, int64_t, int, const float *, int32_t *, \
+                                             int32_t *, float *, hipStream_t);                \
   template hipError_t launch_down_one_token<WT, XT>(const WT *, int, int, const int32_t *, int, \
                                                     const float *, XT *, hipStream_t);
 MOE_INST_DECODE(float, float)

@@ -17,18 +17,31 @@
 //                         (tag, 0) and publishes (expert, weight) of the
 //                         activated experts, ascending by expert, in kRepP
 //                         copies;
-//   GU  [.., +k1*n_cb)    (activated expert u, block of channels): waits for
-//                         the two words of u, streams the gate and up rows
-//                         once, stores a[u, c] = silu(g) * up * w_u
-//                         device-coherently, then adds 1 to u's counter; the
-//                         block that completes the count publishes "u
-//                         complete" in every copy;
+//   GU  [.., +(k1+m)*n_cb) (expert u, block of channels): the first m*n_cb
+//                         blocks are the shared expert's, its Is = m*I
+//                         channels as m pieces u = k1..k1+m-1 of I channels
+//                         (each channel owns a gate row, an up row and a down
+//                         column, so the pieces add up to the whole); they
+//                         need no route and stream while it is computed.
+//                         A routed block waits for the two words of its u.
+//                         Each streams the gate and up rows once, stores
+//                         a[u, c] = silu(g) * up * w_u (w_u: the Eq. 2
+//                         weight, or the shared gate factor) device-
+//                         coherently, then adds 1 to u's counter (a shared
+//                         block first waits for the route, which is
+//                         published after the counters are set); the block
+//                         that completes the count publishes "u complete" in
+//                         every copy;
 //   D   [.., +n_d)        (block of four output rows): marks itself started,
 //                         waits for the route, issues the down rows of the
-//                         activated experts (they stream while gate/up runs),
-//                         waits until every activated expert is complete,
-//                         stages a in LDS and writes
-//                         y[h] = sum_u Wd[e_u, h, :] . a[u, :].
+//                         activated experts and shared pieces (they stream
+//                         while gate/up runs), waits until every one is
+//                         complete, stages a in LDS and writes
+//                         y[h] = sum_u Wd[e_u, h, :] . a[u, :] (+ the shared
+//                         pieces' Sd[h, piece] . a[u, :]).
+// The shared expert ("Channel Selection for Mixture-of-Experts Decoding Needs
+// No Calibration Data", appendix B: shared experts always run in full) is
+// added with the factor sigmoid(x . sg), or 1 without a gate vector sg.
 // The gate/up block that completes the last expert advances the workspace
 // epoch, the source of the call's tags, once every D block has marked itself
 // started (by then every block of the call has read the epoch).
@@ -68,10 +81,13 @@ struct Args {
   uint64_t *tp;       // kRepP copies of 3*k1 tagged words: (expert, weight) per
                       // activated expert, then one "complete" word each
   int64_t tp_rep;     // copy stride in words
-  uint64_t *cnt;      // k1 + 1 counters (tag << 32 | count), kCntStride apart:
-                      // blocks done per activated expert, then experts complete
+  uint64_t *cnt;      // k1 + m + 1 counters (tag << 32 | count), kCntStride
+                      // apart: blocks done per expert u, then experts complete
   uint64_t *started;  // n_d tagged words
-  void *abuf;         // [k1, I] channel activations (bf16 or fp32), row u
+  void *abuf;         // [k1 + m, I] channel activations (bf16 or fp32), row u
+  const void *Sg, *Su, *Sd;  // shared expert [Is, H], [Is, H], [H, Is] (m > 0)
+  const float *sgw;   // shared gate vector [H], or NULL (factor 1)
+  int m, Is;          // shared pieces (Is / I, 0 without a shared expert)
   int H, E, I, k1, k2, n_r, n_cb, n_gu, n_d;
   bool router_bf16;   // bf16 router: bf16 Wr, logits and weights rounded to bf16
 };
@@ -111,20 +127,19 @@ __device__ uint64_t await_lane(const uint64_t *p, int n, uint32_t tag, int32_t *
 
 // gate and up rows of CPW channels per wave (NCH 16-byte chunks per lane of
 // a row, all 2*CPW*NCH loads in flight before any arithmetic), dotted with x;
-// the activations are stored device-coherently.
+// the activations are stored device-coherently.  Wg and Wu point at the
+// first of the I rows of expert (or shared piece) u.
 template <typename WT, typename XT, int NCH, int CPW>
-__device__ void gateup_rows(const Args &a, int u, int e, float wt, int c0) {
+__device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, float wt, int c0) {
   constexpr int NW = Elem<WT>::kPer16B;
   const int lane = lane_id();
-  const WT *Wg = static_cast<const WT *>(a.Wg);
-  const WT *Wu = static_cast<const WT *>(a.Wu);
   const XT *x = static_cast<const XT *>(a.x);
   uint4 gq[CPW][NCH], uq[CPW][NCH];
 #pragma unroll
   for (int ci = 0; ci < CPW; ++ci) {
     const int c = min(c0 + ci, a.I - 1);
-    const WT *grow = Wg + ((int64_t)e * a.I + c) * a.H;
-    const WT *urow = Wu + ((int64_t)e * a.I + c) * a.H;
+    const WT *grow = Wg + (int64_t)c * a.H;
+    const WT *urow = Wu + (int64_t)c * a.H;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       gq[ci][j] = ld16_stream(grow + (j * kWave + lane) * NW);
@@ -204,17 +219,19 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int 
   int32_t *err = a.sync + kErrorWord;
   // mark this block started (it has read the epoch)
   if (tid == 0) coh_st(a.started + d, (uint64_t)tag << 32);
-  // the activated experts, ascending
+  // the activated experts, ascending, then the shared pieces
   if (wv == 0) {
     const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, 2 * a.k1, tag, err);
     if ((lane & 1) == 0 && lane < 2 * a.k1)
       s_uniq[lane >> 1] = min(max(__float_as_int(__uint_as_float((uint32_t)w)), 0), a.E - 1);
+    if (lane < a.m) s_uniq[a.k1 + lane] = lane;
   }
   __syncthreads();
   const int h = min(d * kWaves + wv, a.H - 1);
   const WT *Wd = static_cast<const WT *>(a.Wd);
+  const WT *Sd = static_cast<const WT *>(a.Sd);
   const int nch = a.I / NW;
-  const int U = a.k1;
+  const int U = a.k1 + a.m;
   float acc = 0.0f;
   for (int ub = 0; ub < U; ub += kPF) {
     const int nu = min(kPF, U - ub);
@@ -222,7 +239,9 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int 
 #pragma unroll
     for (int s = 0; s < kPF; ++s) {
       if (s < nu) {
-        const WT *drow = Wd + ((int64_t)s_uniq[ub + s] * a.H + h) * a.I;
+        const int uu = ub + s;
+        const WT *drow = uu < a.k1 ? Wd + ((int64_t)s_uniq[uu] * a.H + h) * a.I
+                                   : Sd + (int64_t)h * a.Is + (int64_t)s_uniq[uu] * a.I;
 #pragma unroll
         for (int j = 0; j < NCD; ++j) {
           const int ch = j * kWave + lane;
@@ -231,8 +250,8 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int 
       }
     }
     if (ub == 0) {
-      // every activated expert's activations are stored
-      if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, a.k1, tag, err);
+      // every activated expert's and shared piece's activations are stored
+      if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, U, tag, err);
       __syncthreads();
     }
     // stage this round's activations (device-coherent 8-byte loads)
@@ -280,6 +299,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
   __shared__ int s_uniq[kWave];
   __shared__ int s_e, s_last;
   __shared__ float s_wt;
+  __shared__ float s_red[kWaves];
   const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const uint32_t tag_epoch = (uint32_t)coh_ld(a.sync + kEpochWord);
   const uint32_t tag = call_tag(tag_epoch);
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     // experts) are set to (tag, 0) first; the staging below waits for every
     // earlier memory operation of the block, so they are in place before the
     // route is published.
-    if (tid <= a.k1) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
+    if (tid <= a.k1 + a.m) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
     stage_tagged<kMaxExperts / kSyncThreads>(L.r.sl, a.E, [&](int i) { return a.tl + i; }, tag,
                                              err);
     route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S, a.router_bf16);
@@ -367,20 +387,50 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     return;
   }
   if (b < a.n_r + 1 + a.n_gu) {
-    // ---- gate/up of (activated expert u, block of channels)
+    // ---- gate/up of (expert or shared piece u, block of channels); the
+    // shared pieces' blocks come first
     const int item = b - a.n_r - 1;
-    const int u = item / a.n_cb, cb = item - u * a.n_cb;
-    if (wv == 0) {
-      const uint64_t w = await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err);
-      const uint64_t we = __shfl(w, 0), ww = __shfl(w, 1);
-      if (lane == 0) {
-        // a timed-out wait leaves any value here: keep the index in range
-        s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
-        s_wt = __uint_as_float((uint32_t)ww);
+    const int n_sh = a.m * a.n_cb;
+    const bool shared = item < n_sh;
+    const int u = shared ? a.k1 + item / a.n_cb : (item - n_sh) / a.n_cb;
+    const int cb = shared ? item % a.n_cb : (item - n_sh) % a.n_cb;
+    const WT *gbase, *ubase;
+    if (shared) {
+      // factor sigmoid(x . sg), or 1
+      if (a.sgw) {
+        const XT *x = static_cast<const XT *>(a.x);
+        float z = 0.0f;
+        for (int h = tid; h < a.H; h += kThreads) z = __builtin_fmaf(Elem<XT>::load1(x + h), a.sgw[h], z);
+        z = wave_sum_dpp(z);
+        if (lane == 0) s_red[wv] = z;
+        __syncthreads();
+        if (tid == 0) s_wt = 1.0f / (1.0f + __expf(-((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]))));
+      } else if (tid == 0) {
+        s_wt = 1.0f;
       }
+      __syncthreads();
+      const int64_t off = (int64_t)(u - a.k1) * a.I * a.H;
+      gbase = static_cast<const WT *>(a.Sg) + off;
+      ubase = static_cast<const WT *>(a.Su) + off;
+    } else {
+      if (wv == 0) {
+        const uint64_t w = await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err);
+        const uint64_t we = __shfl(w, 0), ww = __shfl(w, 1);
+        if (lane == 0) {
+          // a timed-out wait leaves any value here: keep the index in range
+          s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
+          s_wt = __uint_as_float((uint32_t)ww);
+        }
+      }
+      __syncthreads();
+      const int64_t off = (int64_t)s_e * a.I * a.H;
+      gbase = static_cast<const WT *>(a.Wg) + off;
+      ubase = static_cast<const WT *>(a.Wu) + off;
     }
-    __syncthreads();
-    gateup_rows<WT, XT, NCH, CPW>(a, u, s_e, s_wt, (cb * kWaves + wv) * CPW);
+    gateup_rows<WT, XT, NCH, CPW>(a, u, gbase, ubase, s_wt, (cb * kWaves + wv) * CPW);
+    // a shared block counts itself only once the route is published: the
+    // route block sets the counters before it publishes
+    if (shared && wv == 0) await_lane(a.tp + (item % kRepP) * a.tp_rep, 2, tag, err);
     // every activation store of the block is complete, then count the block
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -392,9 +442,10 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
         // the last block of expert u: every block of u counted itself after
         // its stores were complete; publish "u complete" in every copy
         for (int c = 0; c < kRepP; ++c) coh_st(a.tp + c * a.tp_rep + 2 * a.k1 + u, (uint64_t)tag << 32);
-        const uint64_t done = __hip_atomic_fetch_add(a.cnt + a.k1 * kCntStride, (uint64_t)1,
+        const int n_exp = a.k1 + a.m;
+        const uint64_t done = __hip_atomic_fetch_add(a.cnt + n_exp * kCntStride, (uint64_t)1,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = done == (((uint64_t)tag << 32) | (uint32_t)(a.k1 - 1));
+        s_last = done == (((uint64_t)tag << 32) | (uint32_t)(n_exp - 1));
       }
     }
     __syncthreads();
@@ -427,34 +478,37 @@ static int b1_nch(int H, int esz) { return H * esz / (16 * kWave); }
 
 // Shapes the one-launch path takes: the router row in 1..16 and the gate/up
 // row in 1..8 chunks of 16 bytes per lane, the down row in at most 2, k1 <=
-// 32 (two published words per activated expert, one per lane), and one round
-// of activations within a D block's LDS.
-bool decode_b1_supported(int H, int I, int k1, bool bf16) {
+// 32 (two published words per activated expert, one per lane), k1 + m <= 64
+// (one completion word per lane), and one round of activations within a D
+// block's LDS.  m = shared pieces (Is / I).
+bool decode_b1_supported(int H, int I, int k1, bool bf16, int m) {
   const int esz = bf16 ? 2 : 4;
-  if (2 * k1 > kWave || H % (4 * kWave) != 0 || (H * esz) % (16 * kWave) != 0) return false;
+  if (2 * k1 > kWave || k1 + m > kWave || H % (4 * kWave) != 0 ||
+      (H * esz) % (16 * kWave) != 0)
+    return false;
   const int nchr = H / (4 * kWave), nch = b1_nch(H, esz);
   if (!(nchr == 1 || nchr == 2 || nchr == 4 || nchr == 8 || nchr == 16)) return false;
   if (!(nch == 1 || nch == 2 || nch == 4 || nch == 8)) return false;
   const int ab = bf16 ? 2 : 4;
-  const int round_bytes = (k1 < b1::kPF ? k1 : b1::kPF) * I * ab;
+  const int round_bytes = (k1 + m < b1::kPF ? k1 + m : b1::kPF) * I * ab;
   return I * esz / 16 <= 2 * kWave && round_bytes <= b1::kLdsBytes && (I * ab) % 8 == 0;
 }
 
-B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16) {
+B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16, int m) {
   B1Layout L;
   auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
   size_t o = 0;
   L.tl = o;
   o += r256((size_t)E * 8);
   L.tp = o;
-  L.tp_rep_words = (int64_t)(((((size_t)3 * k1 * 8 + 4095) & ~(size_t)4095) + 1280) / 8);
+  L.tp_rep_words = (int64_t)(((((size_t)(3 * k1 + m) * 8 + 4095) & ~(size_t)4095) + 1280) / 8);
   o += r256(b1::kRepP * (size_t)L.tp_rep_words * 8);
   L.cnt = o;
-  o += r256((size_t)(k1 + 1) * b1::kCntStride * 8);
+  o += r256((size_t)(k1 + m + 1) * b1::kCntStride * 8);
   L.started = o;
   o += r256((size_t)((H + b1::kWaves - 1) / b1::kWaves) * 8);
   L.abuf = o;
-  o += r256((size_t)k1 * I * (bf16 ? 2 : 4));
+  o += r256((size_t)(k1 + m) * I * (bf16 ? 2 : 4));
   L.total = o;
   return L;
 }
@@ -463,7 +517,7 @@ template <typename WT, typename XT, int NCHR, int V>
 static void launch_nch(b1::Args &a, int nch, int ncd, hipStream_t s) {
   auto go = [&](auto kern, int cpw) {
     a.n_cb = (a.I + b1::kWaves * cpw - 1) / (b1::kWaves * cpw);
-    a.n_gu = a.k1 * a.n_cb;
+    a.n_gu = (a.k1 + a.m) * a.n_cb;
     const int grid = a.n_r + 1 + a.n_gu + a.n_d;
     kern<<<dim3((unsigned)grid), dim3(b1::kThreads), 0, s>>>(a);
   };
@@ -495,10 +549,12 @@ static void launch_v(b1::Args &a, int nchr, int nch, int ncd, hipStream_t s) {
 template <typename WT, typename XT>
 hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16, const float *br,
                             int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
-                            int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
-                            int32_t *sync, char *region, hipStream_t s) {
+                            int k2, const WT *Sg, const WT *Su, const WT *Sd, int Is,
+                            const float *sgw, XT *y, float *logits_out, int32_t *ids_out,
+                            float *w_out, int32_t *sync, char *region, hipStream_t s) {
   constexpr int esz = sizeof(WT);
-  const B1Layout Lb = decode_b1_layout(H, E, I, k1, esz == 2);
+  const int m = Sg ? Is / I : 0;
+  const B1Layout Lb = decode_b1_layout(H, E, I, k1, esz == 2, m);
   b1::Args a;
   a.x = x;
   a.Wr = Wr;
@@ -507,6 +563,12 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
   a.Wg = Wg;
   a.Wu = Wu;
   a.Wd = Wd;
+  a.Sg = Sg;
+  a.Su = Su;
+  a.Sd = Sd;
+  a.sgw = sgw;
+  a.m = m;
+  a.Is = Is;
   a.y = y;
   a.logits_out = logits_out;
   a.ids_out = ids_out;
@@ -539,9 +601,10 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
 #define MOE_INST_B1(WT, XT)                                                                 \
   template hipError_t launch_decode_b1<WT, XT>(const XT *, int, const void *, bool,           \
                                                const float *, int, const WT *, const WT *,    \
-                                               const WT *, int, int, int, XT *, float *,      \
-                                               int32_t *, float *, int32_t *, char *,         \
-                                               hipStream_t);
+                                               const WT *, int, int, int, const WT *,         \
+                                               const WT *, const WT *, int, const float *,    \
+                                               XT *, float *, int32_t *, float *, int32_t *,  \
+                                               char *, hipStream_t);
 MOE_INST_B1(float, float)
 MOE_INST_B1(bf16_t, bf16_t)
 

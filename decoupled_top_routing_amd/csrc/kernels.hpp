@@ -72,13 +72,15 @@ struct B1Layout {
   size_t tl, tp, cnt, started, abuf, total;  // byte offsets in the path's region
   int64_t tp_rep_words;
 };
-bool decode_b1_supported(int H, int I, int k1, bool bf16);
-B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16);
+// m = pieces of I channels of the shared expert (0 without one)
+bool decode_b1_supported(int H, int I, int k1, bool bf16, int m);
+B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16, int m);
 template <typename WT, typename XT>
 hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16, const float *br,
                             int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
-                            int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
-                            int32_t *sync, char *region, hipStream_t s);
+                            int k2, const WT *Sg, const WT *Su, const WT *Sd, int Is,
+                            const float *sgw, XT *y, float *logits_out, int32_t *ids_out,
+                            float *w_out, int32_t *sync, char *region, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);
@@ -98,8 +100,9 @@ hipError_t launch_gateup_mma(const uint16_t *x, int H, const uint16_t *Wg, const
                              uint16_t *abf, hipStream_t s);
 hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I,
                            const int32_t *plan, int E, int64_t n, uint16_t *zbf, hipStream_t s);
-hipError_t launch_combine_bf16(const uint16_t *zbf, int64_t T, int H, int k1, uint16_t *y,
-                               hipStream_t s);
+// zs: the shared expert's bf16 term [T, H], or NULL
+hipError_t launch_combine_bf16(const uint16_t *zbf, const uint16_t *zs, int64_t T, int H, int k1,
+                               uint16_t *y, hipStream_t s);
 
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
@@ -113,8 +116,17 @@ template <typename WT>
 hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
                        const float *abuf, float *zbuf, hipStream_t s);
 
+// zs: the shared expert's term [T, H], or NULL
 template <typename XT>
-hipError_t launch_combine(const float *zbuf, int64_t T, int H, int k1, XT *y, hipStream_t s);
+hipError_t launch_combine(const float *zbuf, const float *zs, int64_t T, int H, int k1, XT *y,
+                          hipStream_t s);
+
+// ---- shared expert as a one-expert layer: its plan (grouped layout, E = 1),
+// zero ids for the prefill plan, and the per-token factor
+size_t shared_plan_words(int64_t T);
+template <typename XT>
+hipError_t launch_shared_prep(const XT *x, int64_t T, int H, const float *sgw, int32_t *plan,
+                              int32_t *ids0, float *gs, hipStream_t s);
 
 
 }  // namespace moe

@@ -31,12 +31,23 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace layout of moe_forward (each segment 256-byte aligned).
-struct Layout {
-  size_t logits, ids, w, plan, abuf, zbuf, tagged, total;
+// The shared expert of moe_forward_shared (Sg == NULL: none).
+struct Shared {
+  const void *Sg = nullptr, *Su = nullptr, *Sd = nullptr;
+  int32_t Is = 0;
+  const float *sgw = nullptr;
 };
 
-Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
+// pieces of I channels the one-launch kernel splits the shared expert into
+// (0: none, or Is not a multiple of I)
+int shared_pieces(int32_t I, int32_t Is) { return Is > 0 && Is % I == 0 ? Is / I : 0; }
+
+// Workspace layout of moe_forward (each segment 256-byte aligned).
+struct Layout {
+  size_t logits, ids, w, plan, abuf, zbuf, tagged, plan_s, gs, abuf_s, zbuf_s, total;
+};
+
+Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   Layout L;
   size_t o = moe::kSyncRegionBytes;  // reserved: sync words of the fused path
   const size_t n_assign = (size_t)T * (size_t)k1;
@@ -53,18 +64,30 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
   L.zbuf = o;
   o += round256(n_assign * (size_t)H * 4);
   L.tagged = o;
-  o += round256(moe::decode_b1_layout(H, E, I, k1, true).total);
-  o += round256(moe::decode_b1_layout(H, E, I, k1, false).total);
+  const int m = shared_pieces(I, Is);
+  o += round256(moe::decode_b1_layout(H, E, I, k1, true, m).total);
+  o += round256(moe::decode_b1_layout(H, E, I, k1, false, m).total);
+  L.plan_s = L.gs = L.abuf_s = L.zbuf_s = o;
+  if (Is > 0) {
+    L.plan_s = o;
+    o += round256(moe::shared_plan_words(T) * 4);
+    L.gs = o;
+    o += round256((size_t)T * 4);
+    L.abuf_s = o;
+    o += round256((size_t)T * Is * 4);
+    L.zbuf_s = o;
+    o += round256((size_t)T * H * 4);
+  }
   L.total = o;
   return L;
 }
 
 // Workspace layout of the prefill path.
 struct PrefillLayout {
-  size_t logits, ids, w, plan, w3, part, abf, zbf, total;
+  size_t logits, ids, w, plan, w3, part, abf, zbf, ids_s, plan_s, gs, abf_s, zbf_s, total;
 };
 
-PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
+PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   PrefillLayout L;
   size_t o = moe::kSyncRegionBytes;
   const size_t n = (size_t)T * (size_t)k1;
@@ -84,6 +107,19 @@ PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   o += round256(n * (size_t)I * 2);
   L.zbf = o;
   o += round256(n * (size_t)H * 2);
+  L.ids_s = L.plan_s = L.gs = L.abf_s = L.zbf_s = o;
+  if (Is > 0) {
+    L.ids_s = o;
+    o += round256((size_t)T * 4);
+    L.plan_s = o;
+    o += round256(moe::prefill_plan_words(T, 1) * 4);
+    L.gs = o;
+    o += round256((size_t)T * 4);
+    L.abf_s = o;
+    o += round256((size_t)T * Is * 2);
+    L.zbf_s = o;
+    o += round256((size_t)T * H * 2);
+  }
   L.total = o;
   return L;
 }
@@ -113,17 +149,20 @@ constexpr int64_t kPrefillMinAssign = 512;
 // the single-launch fused path at every decode batch (its gate/up and down
 // kernels sustain more bandwidth than the fused kernel's, which is limited
 // by register-bound occupancy); the fused path stays available on request.
-int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf16,
+int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is, bool bf16,
                 uint32_t flags, Path *path) {
-  const bool fused_ok = moe::fused_decode_supported(T, H, E, I, k1, bf16);
+  const bool fused_ok = Is == 0 && moe::fused_decode_supported(T, H, E, I, k1, bf16);
   if (flags & MOE_FLAG_FORCE_FUSED) {
     if (!fused_ok) return fail(MOE_ENOTSUP, "the fused path does not take these shapes");
     *path = Path::Fused;
     return MOE_OK;
   }
-  const bool prefill_ok = moe::prefill_supported(H, I, bf16);
+  const bool prefill_ok =
+      moe::prefill_supported(H, I, bf16) && (Is == 0 || moe::prefill_supported(H, Is, bf16));
   if (flags & MOE_FLAG_FORCE_PREFILL) {
-    if (!prefill_ok) return fail(MOE_ENOTSUP, "the prefill path takes bf16, H % 128 == 0 and I % 64 == 0");
+    if (!prefill_ok)
+      return fail(MOE_ENOTSUP,
+                  "the prefill path takes bf16, H % 128 == 0 and I % 64 == 0 (and Is % 64 == 0)");
     *path = Path::Prefill;
     return MOE_OK;
   }
@@ -137,11 +176,11 @@ int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, bool bf1
   return MOE_OK;
 }
 
-size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1) {
+size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   moe::DecodeLayout D;
   size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
-  const size_t b = layout(T, H, E, I, k1).total;
-  const size_t c = prefill_layout(T, H, E, I, k1).total;
+  const size_t b = layout(T, H, E, I, k1, Is).total;
+  const size_t c = prefill_layout(T, H, E, I, k1, Is).total;
   if (b > a) a = b;
   return c > a ? c : a;
 }
@@ -183,10 +222,10 @@ struct Launches {
 
 int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, bool router_bf16,
                     const float *br, int32_t E, const uint16_t *Wg, const uint16_t *Wu,
-                    const uint16_t *Wd, int32_t I, int32_t k1, int32_t k2, uint16_t *y,
-                    float *logits_out, int32_t *ids_out, float *w_out, char *ws,
+                    const uint16_t *Wd, int32_t I, int32_t k1, int32_t k2, const Shared &sh,
+                    uint16_t *y, float *logits_out, int32_t *ids_out, float *w_out, char *ws,
                     Launches &run) {
-  const PrefillLayout L = prefill_layout(T, H, E, I, k1);
+  const PrefillLayout L = prefill_layout(T, H, E, I, k1, sh.Is);
   float *logits = reinterpret_cast<float *>(ws + L.logits);
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
   float *w = reinterpret_cast<float *>(ws + L.w);
@@ -210,15 +249,35 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, boo
   RUN("prefill_plan", moe::launch_prefill_plan(ids, n, E, plan, s));
   RUN("gateup_mma", moe::launch_gateup_mma(x, H, Wg, Wu, I, plan, E, n, k1, w, abf, s));
   RUN("down_mma", moe::launch_down_mma(abf, H, Wd, I, plan, E, n, zbf, s));
-  RUN("combine", moe::launch_combine_bf16(zbf, T, H, k1, y, s));
+  uint16_t *zbf_s = nullptr;
+  if (sh.Sg) {
+    // the shared expert as a one-expert layer over every token
+    int32_t *ids_s = reinterpret_cast<int32_t *>(ws + L.ids_s);
+    int32_t *plan_s = reinterpret_cast<int32_t *>(ws + L.plan_s);
+    float *gs = reinterpret_cast<float *>(ws + L.gs);
+    uint16_t *abf_s = reinterpret_cast<uint16_t *>(ws + L.abf_s);
+    zbf_s = reinterpret_cast<uint16_t *>(ws + L.zbf_s);
+    RUN("shared_prep", moe::launch_shared_prep<moe::bf16_t>(
+                           reinterpret_cast<const moe::bf16_t *>(x), T, H, sh.sgw, nullptr, ids_s,
+                           gs, s));
+    RUN("shared_plan", moe::launch_prefill_plan(ids_s, T, 1, plan_s, s));
+    RUN("shared_gateup_mma",
+        moe::launch_gateup_mma(x, H, static_cast<const uint16_t *>(sh.Sg),
+                               static_cast<const uint16_t *>(sh.Su), sh.Is, plan_s, 1, T, 1, gs,
+                               abf_s, s));
+    RUN("shared_down_mma", moe::launch_down_mma(abf_s, H, static_cast<const uint16_t *>(sh.Sd),
+                                                sh.Is, plan_s, 1, T, zbf_s, s));
+  }
+  RUN("combine", moe::launch_combine_bf16(zbf, zbf_s, T, H, k1, y, s));
   return MOE_OK;
 }
 
 template <typename WT, typename XT>
 int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router_bf16,
                   const float *br, int32_t E, const WT *Wg, const WT *Wu, const WT *Wd, int32_t I,
-                  int32_t k1, int32_t k2, XT *y, float *logits_out, int32_t *ids_out,
-                  float *w_out, Path path, char *ws, const Layout &L, Launches &run) {
+                  int32_t k1, int32_t k2, const Shared &sh, XT *y, float *logits_out,
+                  int32_t *ids_out, float *w_out, Path path, char *ws, const Layout &L,
+                  Launches &run) {
   const hipStream_t s = run.s;
   const float *Wr32 = static_cast<const float *>(Wr);  // meaningful without router_bf16
   if constexpr (sizeof(WT) == 2) {
@@ -226,7 +285,7 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
       return forward_prefill(reinterpret_cast<const uint16_t *>(x), T, H, Wr, router_bf16, br, E,
                              reinterpret_cast<const uint16_t *>(Wg),
                              reinterpret_cast<const uint16_t *>(Wu),
-                             reinterpret_cast<const uint16_t *>(Wd), I, k1, k2,
+                             reinterpret_cast<const uint16_t *>(Wd), I, k1, k2, sh,
                              reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, run);
   }
   if (path == Path::Fused) {
@@ -244,9 +303,13 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   int32_t *sync = reinterpret_cast<int32_t *>(ws);
   const int64_t n_assign = T * k1;
   int32_t *ticket = sync + moe::kRouteTicketWord;
-  if (T == 1 && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2)) {
+  const WT *Sg = static_cast<const WT *>(sh.Sg), *Su = static_cast<const WT *>(sh.Su),
+           *Sd = static_cast<const WT *>(sh.Sd);
+  const int m = shared_pieces(I, sh.Is);
+  if (T == 1 && (!Sg || m > 0) && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2, m)) {
     RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
-                                                   k1, k2, y, logits_out, ids_out, w_out, sync,
+                                                   k1, k2, Sg, Su, Sd, sh.Is, sh.sgw, y,
+                                                   logits_out, ids_out, w_out, sync,
                                                    ws + L.tagged, s)));
     return MOE_OK;
   }
@@ -274,16 +337,92 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   }
   RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)));
   const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
-  if (T == 1 && ncd <= 2) {
+  if (T == 1 && ncd <= 2 && !Sg) {
     RUN("down_one_token", (moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)));
     return MOE_OK;
   }
   RUN("down", moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s));
-  RUN("combine", moe::launch_combine<XT>(zbuf, T, H, k1, y, s));
+  float *zbuf_s = nullptr;
+  if (Sg) {
+    // the shared expert as a one-expert layer over every token
+    int32_t *plan_s = reinterpret_cast<int32_t *>(ws + L.plan_s);
+    float *gs = reinterpret_cast<float *>(ws + L.gs);
+    float *abuf_s = reinterpret_cast<float *>(ws + L.abuf_s);
+    zbuf_s = reinterpret_cast<float *>(ws + L.zbuf_s);
+    RUN("shared_prep", moe::launch_shared_prep<XT>(x, T, H, sh.sgw, plan_s, nullptr, gs, s));
+    RUN("shared_gateup",
+        (moe::launch_gateup<WT, XT>(x, H, Sg, Su, sh.Is, plan_s, 1, T, 1, gs, abuf_s, s)));
+    RUN("shared_down", moe::launch_down<WT>(Sd, H, sh.Is, plan_s, 1, T, abuf_s, zbuf_s, s));
+  }
+  RUN("combine", moe::launch_combine<XT>(zbuf, zbuf_s, T, H, k1, y, s));
   return MOE_OK;
 }
 
 #undef RUN
+
+// moe_forward and moe_forward_shared: argument checks, then the path.
+int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
+                 const float *br, int32_t E, const void *Wgate, const void *Wup,
+                 const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2,
+                 const Shared &sh, void *y, float *logits_out, int32_t *ids_out, float *w_out,
+                 uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_route_args(T, E, k1, k2);
+  if (rc != MOE_OK) return rc;
+  if (H < 8 || H % 8 != 0) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 8", H);
+  if (I < 8 || I % 8 != 0) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 8", I);
+  if ((int64_t)H * I > (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
+  if (sh.Sg && (sh.Is < 8 || sh.Is % 8 != 0 || (int64_t)H * sh.Is > (int64_t(1) << 31)))
+    return fail(MOE_EINVAL, "Is=%d must be a positive multiple of 8 with H*Is <= 2^31", sh.Is);
+  const uint32_t paths = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
+  if (flags & ~(paths | MOE_FLAG_ROUTER_BF16))
+    return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if (__builtin_popcount(flags & paths) > 1)
+    return fail(MOE_EINVAL, "more than one path flag set");
+  const bool router_bf16 = (flags & MOE_FLAG_ROUTER_BF16) != 0;
+  const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
+  const bool b16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
+  if (!f32 && !b16)
+    return fail(MOE_ENOTSUP, "dtype pair (act=%d, w=%d) not supported", act_dtype, w_dtype);
+  if (router_bf16 && !b16)
+    return fail(MOE_ENOTSUP, "the bf16 router takes bf16 activations and weights");
+  if (router_bf16 && br)
+    return fail(MOE_EINVAL, "the bf16 router takes no bias (br must be NULL)");
+  if (router_bf16 && (flags & MOE_FLAG_FORCE_FUSED))
+    return fail(MOE_ENOTSUP, "the fused path has no bf16 router");
+  if (sh.Sg && (flags & MOE_FLAG_FORCE_FUSED))
+    return fail(MOE_ENOTSUP, "the fused path has no shared expert");
+  if (T == 0) return MOE_OK;
+  if (!x || !Wr || !Wgate || !Wup || !Wdown || !y) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wgate, 16) || !aligned(Wup, 16) ||
+      !aligned(Wdown, 16) || !aligned(y, 16))
+    return fail(MOE_EALIGN, "x, Wr, Wgate, Wup, Wdown and y need 16-byte alignment");
+  if (sh.Sg && (!aligned(sh.Sg, 16) || !aligned(sh.Su, 16) || !aligned(sh.Sd, 16)))
+    return fail(MOE_EALIGN, "Sgate, Sup and Sdown need 16-byte alignment");
+  if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
+      (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)) ||
+      (sh.sgw && !aligned(sh.sgw, 4)))
+    return fail(MOE_EALIGN, "br, sgate and the route outputs need 4-byte alignment");
+  const Layout L = layout(T, H, E, I, k1, sh.Is);
+  const size_t need = workspace_bytes_for(T, H, E, I, k1, sh.Is);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
+                need, workspace_bytes, workspace);
+  Path path;
+  if ((rc = choose_path(T, H, E, I, k1, sh.Is, b16, flags, &path)) != MOE_OK) return rc;
+  Launches run((hipStream_t)stream);
+  char *ws = static_cast<char *>(workspace);
+  if (f32)
+    return forward_typed<float, float>(
+        static_cast<const float *>(x), T, H, Wr, false, br, E, static_cast<const float *>(Wgate),
+        static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2, sh,
+        static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
+  return forward_typed<moe::bf16_t, moe::bf16_t>(
+      static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
+      static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
+      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, sh, static_cast<moe::bf16_t *>(y),
+      logits_out, ids_out, w_out, path, ws, L, run);
+}
 
 }  // namespace
 
@@ -321,12 +460,17 @@ int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1, int32_t k2,
 
 size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1,
                              int32_t act_dtype, int32_t w_dtype) {
+  return moe_forward_shared_workspace(T, H, E, I, k1, 0, act_dtype, w_dtype);
+}
+
+size_t moe_forward_shared_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1,
+                                    int32_t Is, int32_t act_dtype, int32_t w_dtype) {
   (void)act_dtype;
   (void)w_dtype;
   if (T < 0 || T > kMaxT || E < 1 || E > MOE_MAX_EXPERTS || k1 < 1 || k1 > E || H < 8 ||
-      I < 8)
+      I < 8 || Is < 0 || (Is > 0 && Is < 8))
     return 0;
-  return workspace_bytes_for(T, H, E, I, k1);
+  return workspace_bytes_for(T, H, E, I, k1, Is);
 }
 
 int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
@@ -334,55 +478,27 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const vo
                 const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
                 float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
                 void *workspace, size_t workspace_bytes, void *stream) {
-  int rc = check_route_args(T, E, k1, k2);
-  if (rc != MOE_OK) return rc;
-  if (H < 8 || H % 8 != 0) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 8", H);
-  if (I < 8 || I % 8 != 0) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 8", I);
-  if ((int64_t)H * I > (int64_t(1) << 31))
-    return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
-  const uint32_t paths = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
-  if (flags & ~(paths | MOE_FLAG_ROUTER_BF16))
-    return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
-  if (__builtin_popcount(flags & paths) > 1)
-    return fail(MOE_EINVAL, "more than one path flag set");
-  const bool router_bf16 = (flags & MOE_FLAG_ROUTER_BF16) != 0;
-  const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
-  const bool b16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
-  if (!f32 && !b16)
-    return fail(MOE_ENOTSUP, "dtype pair (act=%d, w=%d) not supported", act_dtype, w_dtype);
-  if (router_bf16 && !b16)
-    return fail(MOE_ENOTSUP, "the bf16 router takes bf16 activations and weights");
-  if (router_bf16 && br)
-    return fail(MOE_EINVAL, "the bf16 router takes no bias (br must be NULL)");
-  if (router_bf16 && (flags & MOE_FLAG_FORCE_FUSED))
-    return fail(MOE_ENOTSUP, "the fused path has no bf16 router");
-  if (T == 0) return MOE_OK;
-  if (!x || !Wr || !Wgate || !Wup || !Wdown || !y) return fail(MOE_EINVAL, "NULL pointer");
-  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wgate, 16) || !aligned(Wup, 16) ||
-      !aligned(Wdown, 16) || !aligned(y, 16))
-    return fail(MOE_EALIGN, "x, Wr, Wgate, Wup, Wdown and y need 16-byte alignment");
-  if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
-      (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
-    return fail(MOE_EALIGN, "br and the route outputs need 4-byte alignment");
-  const Layout L = layout(T, H, E, I, k1);
-  const size_t need = workspace_bytes_for(T, H, E, I, k1);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
-    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
-                need, workspace_bytes, workspace);
-  Path path;
-  if ((rc = choose_path(T, H, E, I, k1, b16, flags, &path)) != MOE_OK) return rc;
-  Launches run((hipStream_t)stream);
-  char *ws = static_cast<char *>(workspace);
-  if (f32)
-    return forward_typed<float, float>(
-        static_cast<const float *>(x), T, H, Wr, false, br, E, static_cast<const float *>(Wgate),
-        static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2,
-        static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
-  return forward_typed<moe::bf16_t, moe::bf16_t>(
-      static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
-      static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
-      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, static_cast<moe::bf16_t *>(y),
-      logits_out, ids_out, w_out, path, ws, L, run);
+  return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
+                      Shared{}, y, logits_out, ids_out, w_out, flags, workspace,
+                      workspace_bytes, stream);
+}
+
+int moe_forward_shared(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
+                       const float *br, int32_t E, const void *Wgate, const void *Wup,
+                       const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2,
+                       const void *Sgate, const void *Sup, const void *Sdown, int32_t Is,
+                       const float *sgate, void *y, float *logits_out, int32_t *ids_out,
+                       float *w_out, uint32_t flags, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  if (!Sgate || !Sup || !Sdown) return fail(MOE_EINVAL, "NULL shared expert pointer");
+  Shared sh;
+  sh.Sg = Sgate;
+  sh.Su = Sup;
+  sh.Sd = Sdown;
+  sh.Is = Is;
+  sh.sgw = sgate;
+  return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2, sh,
+                      y, logits_out, ids_out, w_out, flags, workspace, workspace_bytes, stream);
 }
 
 int moe_profile_launch(int32_t launch, void *start, void *stop) {

@@ -484,6 +484,7 @@ hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I
 // y[t, h] = sum over the token's k1 slots of z[t*k1 + r, h] (bf16 partials,
 // fp32 sum in slot order); 8 outputs per thread with 16-byte accesses.
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t *__restrict__ zbf,
+                                                           const uint16_t *__restrict__ zs,
                                                            int64_t T, int H, int k1,
                                                            uint16_t *__restrict__ y) {
   const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -498,6 +499,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t *__res
 #pragma unroll
     for (int k = 0; k < 8; ++k) s[k] = s[k] + v[k];
   }
+  if (zs) {
+    float v[8];
+    Elem<bf16_t>::widen(ld16(zs + t * H + h), v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s[k] = s[k] + v[k];
+  }
   uint4 o;
   o.x = f32_to_bf16_bits(s[0]) | (f32_to_bf16_bits(s[1]) << 16);
   o.y = f32_to_bf16_bits(s[2]) | (f32_to_bf16_bits(s[3]) << 16);
@@ -506,10 +513,11 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t *__res
   *reinterpret_cast<uint4 *>(y + i8) = o;
 }
 
-hipError_t launch_combine_bf16(const uint16_t *zbf, int64_t T, int H, int k1, uint16_t *y,
-                               hipStream_t s) {
+hipError_t launch_combine_bf16(const uint16_t *zbf, const uint16_t *zs, int64_t T, int H, int k1,
+                               uint16_t *y, hipStream_t s) {
   const int64_t n8 = T * H / 8;
-  combine_bf16_kernel<<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s>>>(zbf, T, H, k1, y);
+  combine_bf16_kernel<<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s>>>(zbf, zs, T, H, k1,
+                                                                              y);
   return hipGetLastError();
 }
 

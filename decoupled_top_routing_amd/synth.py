@@ -18,9 +18,14 @@ is Gaussian:
 * gate, up and down weights ~ N(0, 0.02^2), rounded to bf16 (RNE) for the
   bf16 layers.
 
+A shared expert (``make_shared``: always run beside the routed experts, "Channel
+Selection ..." appendix B) has Is channels drawn like an expert's, Sg and Su
+[Is,H], Sd [H,Is], and an optional gate vector sg ~ N(0, 1/H) [H] fp32.
+
 Seeds: each tensor has its own generator seeded with
-``base + 1000 * layer + tensor_id`` (x=0, Wr=1, br=2, Wg=3, Wu=4, Wd=5), so a
-layer is a pure function of (config, layer, base, device).  The CPU and GPU
+``base + 1000 * layer + tensor_id`` (x=0, Wr=1, br=2, Wg=3, Wu=4, Wd=5, Sg=6,
+Su=7, Sd=8, sg=9), so a layer is a pure function of (config, layer, base,
+device).  The CPU and GPU
 generators of torch draw different streams: a config's device is part of its
 definition.
 """
@@ -30,7 +35,8 @@ from dataclasses import dataclass, field, replace
 
 import torch
 
-TENSOR_ID = {"x": 0, "Wr": 1, "br": 2, "Wg": 3, "Wu": 4, "Wd": 5}
+TENSOR_ID = {"x": 0, "Wr": 1, "br": 2, "Wg": 3, "Wu": 4, "Wd": 5, "Sg": 6, "Su": 7, "Sd": 8,
+             "sg": 9}
 
 
 @dataclass(frozen=True)
@@ -141,6 +147,23 @@ def make_weights(cfg: LayerConfig, layer: int = 0, base: int = 0, device=None):
     Wu = _normal_cast((E, I, H), cfg.w_std, s + TENSOR_ID["Wu"], device, wd)
     Wd = _normal_cast((E, H, I), cfg.w_std, s + TENSOR_ID["Wd"], device, wd)
     return {"Wr": Wr, "br": br, "Wg": Wg, "Wu": Wu, "Wd": Wd}
+
+
+def make_shared(cfg: LayerConfig, Is: int, gate: bool = True, layer: int = 0, base: int = 0,
+                device=None):
+    """A shared expert of Is channels for the layer: dict Sg, Su [Is,H], Sd [H,Is]
+    in the layer's dtype, and sg [H] fp32 (None without a gate)."""
+    device = device or cfg.gen_device
+    s = base + 1000 * layer
+    wd = cfg.torch_dtype
+    H = cfg.H
+    out = {"Sg": _normal_cast((Is, H), cfg.w_std, s + TENSOR_ID["Sg"], device, wd),
+           "Su": _normal_cast((Is, H), cfg.w_std, s + TENSOR_ID["Su"], device, wd),
+           "Sd": _normal_cast((H, Is), cfg.w_std, s + TENSOR_ID["Sd"], device, wd),
+           "sg": None}
+    if gate:
+        out["sg"] = _normal((H,), H ** -0.5, s + TENSOR_ID["sg"], device)
+    return out
 
 
 def make_layer(cfg: LayerConfig, layer: int = 0, base: int = 0, device=None,

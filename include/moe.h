@@ -166,6 +166,46 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
                 void *stream);
 
 /*
+ * moe_forward_shared -- moe_forward plus a shared expert, which runs on every
+ * token beside the routed ones ("Channel Selection for Mixture-of-Experts
+ * Decoding Needs No Calibration Data", appendix B "Experimental setup":
+ * shared experts always run in full).  The pages do not give its gating; the
+ * layer computed here is
+ *
+ *   y[t] = sum_{r<k1} w[t,r] * E_{ids[t,r]}(x[t])  +  g[t] * S(x[t]),
+ *   S(x) = Sdown (silu(Sgate x) * (Sup x)),
+ *   g[t] = sigmoid(x[t] . sgate) with a gate vector, 1 with sgate = NULL.
+ *
+ *   Sgate  [Is, H]   w_dtype: row c = gate row of shared channel c  16-byte aligned
+ *   Sup    [Is, H]   w_dtype: row c = up row of shared channel c    16-byte aligned
+ *   Sdown  [H, Is]   w_dtype: column c = down column of channel c   16-byte aligned
+ *   Is     shared channels: a positive multiple of 8, H * Is <= 2^31
+ *   sgate  [H] fp32 gate vector, or NULL                            4-byte aligned
+ * Every other argument, and the route outputs, as for moe_forward (the
+ * route is unchanged by the shared expert).  The workspace size comes from
+ * moe_forward_shared_workspace.  MOE_FLAG_FORCE_FUSED returns MOE_ENOTSUP;
+ * MOE_FLAG_FORCE_PREFILL also needs Is % 64 == 0.  For one token with
+ * Is % I == 0 the shared expert runs inside the single launch of the layer,
+ * streaming while the token is routed.
+ */
+int moe_forward_shared(const void *x, int32_t act_dtype, int64_t T, int32_t H,
+                       const void *Wr, const float *br, int32_t E,
+                       const void *Wgate, const void *Wup, const void *Wdown,
+                       int32_t w_dtype, int32_t I, int32_t k1, int32_t k2,
+                       const void *Sgate, const void *Sup, const void *Sdown,
+                       int32_t Is, const float *sgate, void *y,
+                       float *logits_out, int32_t *ids_out, float *w_out,
+                       uint32_t flags, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* moe_forward_shared_workspace -- bytes of workspace moe_forward_shared needs
+ * (a multiple of 256); 0 for invalid sizes.  Is = 0 gives
+ * moe_forward_workspace's size. */
+size_t moe_forward_shared_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
+                                    int32_t k1, int32_t Is, int32_t act_dtype,
+                                    int32_t w_dtype);
+
+/*
  * moe_profile_launch -- profiling aid; changes no output.  Arms the NEXT
  * moe_forward call on the calling thread: it records the hipEvent_t `start`
  * on its stream immediately before its kernel launch number `launch` (0 =

@@ -108,3 +108,42 @@ def test_forward_rejects_bad_arguments(kw, code):
 def test_forward_zero_tokens_is_a_no_op():
     lib = moe.load_library()
     assert _fwd(lib, T=0, x=None, y=None, ws=None, wsb=0) == 0
+
+
+def _fwd_shared(lib, **kw):
+    a = dict(x=16, act=1, T=1, H=2048, Wr=16, br=None, E=128, Wg=16, Wu=16, Wd=16, wt=1,
+             I=768, k1=4, k2=16, Sg=16, Su=16, Sd=16, Is=768, sg=None, y=16, lo=None,
+             io=None, wo=None, flags=0, ws=256, wsb=1 << 30, stream=None)
+    a.update(kw)
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.moe_forward_shared(v(a["x"]), a["act"], a["T"], a["H"], v(a["Wr"]), v(a["br"]),
+                                  a["E"], v(a["Wg"]), v(a["Wu"]), v(a["Wd"]), a["wt"], a["I"],
+                                  a["k1"], a["k2"], v(a["Sg"]), v(a["Su"]), v(a["Sd"]), a["Is"],
+                                  v(a["sg"]), v(a["y"]), v(a["lo"]), v(a["io"]), v(a["wo"]),
+                                  a["flags"], v(a["ws"]), a["wsb"], v(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Sg=None), 1), (dict(Sd=None), 1), (dict(Is=4), 1), (dict(Is=772), 1),
+    (dict(Sg=24), 2), (dict(Sd=8), 2), (dict(sg=2), 2),
+    (dict(flags=1), 4),                   # the fused path has no shared expert
+    (dict(flags=4, Is=72), 4),            # the prefill path needs Is % 64 == 0
+    (dict(k2=3), 1), (dict(ws=None), 3),
+])
+def test_forward_shared_rejects_bad_arguments(kw, code):
+    lib = moe.load_library()
+    assert _fwd_shared(lib, **kw) == code, lib.moe_last_error_str()
+
+
+def test_forward_shared_workspace_size():
+    lib = moe.load_library()
+    plain = lib.moe_forward_workspace(8, 2048, 128, 768, 4, 1, 1)
+    assert lib.moe_forward_shared_workspace(8, 2048, 128, 768, 4, 0, 1, 1) == plain
+    sh = lib.moe_forward_shared_workspace(8, 2048, 128, 768, 4, 1536, 1, 1)
+    assert sh > plain and sh % 256 == 0
+    assert lib.moe_forward_shared_workspace(8, 2048, 128, 768, 4, 4, 1, 1) == 0
+
+
+def test_forward_shared_zero_tokens_is_a_no_op():
+    lib = moe.load_library()
+    assert _fwd_shared(lib, T=0, x=None, y=None, ws=None, wsb=0) == 0
