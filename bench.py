@@ -42,6 +42,10 @@ DEFAULT_CELLS = ",".join([
     "C3:32:4:16", "C3:32:8:8", "C3:64:4:16", "C3:64:8:8", "C3:128:4:16", "C3:128:8:8",
     "C3:256:4:16", "C3:256:8:8",
     "C5:1:10:10", "C5:1:5:5", "C5:1:5:20", "C5:64:10:10", "C5:64:5:5", "C5:64:5:20",
+    # the bf16 router (router weight bf16, bf16 logits and weights), same layers
+    "C2h:1:4:16", "C2h:1:8:8", "C3h:8:4:16", "C3h:8:8:8", "C4h:4096:4:16", "C4h:4096:8:8",
+    # plus a gated shared expert of I channels, same layers
+    "C2s:1:4:16", "C2s:1:8:8", "C3s:8:4:16", "C3s:8:8:8", "C4s:4096:4:16", "C4s:4096:8:8",
 ])
 
 
@@ -54,27 +58,42 @@ def parse():
     ap.add_argument("--ring", type=int, default=RING)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cells", default=DEFAULT_CELLS,
-                    help="CONFIG:T:k1:k2[:path] list; the first is the headline")
+                    help="CONFIG:T:k1:k2[:path] list; the first is the headline; a "
+                         "CONFIG ending in h runs that config's layers with the bf16 router, "
+                         "one ending in s adds a gated shared expert of I channels")
     return ap.parse_args()
 
 
 # ------------------------------------------------------------------ workloads
 def make_sets(synth, torch, names, ring):
-    """Device layers per configuration name."""
+    """Device layers per configuration name; NAMEh is NAME's layers with the
+    router weight cast to bf16 and no bias (the bf16 router), NAMEs adds a
+    gated shared expert of I channels to each layer."""
     sets = {}
     t0 = time.perf_counter()
-    if names & {"C2", "C3"}:
+    base = {n[:2] for n in names}
+    if base & {"C2", "C3"}:
         # x holds 256 tokens; a cell of T tokens uses the first T
         sets["C2"] = sets["C3"] = (synth.DECODE_B8,
                                    [synth.make_layer(synth.DECODE_B8, layer=i, device="cuda",
                                                      T=256)
                                     for i in range(ring)])
-    if "C4" in names:
+    if "C4" in base:
         sets["C4"] = (synth.PREFILL, [synth.make_layer(synth.PREFILL, device="cuda")])
-    if "C5" in names:
+    if "C5" in base:
         cfg = synth.LARGE
         sets["C5"] = (cfg, [synth.make_layer(cfg, layer=i, device="cuda", T=64)
                             for i in range(cfg.layers)])
+    for n in names:
+        if n.endswith("h"):
+            cfg, layers = sets[n[:2]]
+            sets[n] = (cfg, [dict(lay, Wr=lay["Wr"].to(torch.bfloat16), br=None)
+                             for lay in layers])
+        elif n.endswith("s"):
+            cfg, layers = sets[n[:2]]
+            sets[n] = (cfg, [dict(lay, shared=synth.make_shared(cfg, cfg.I, gate=True, layer=i,
+                                                                device="cuda"))
+                             for i, lay in enumerate(layers)])
     torch.cuda.synchronize()
     print(f"# generated {sorted(names)} on the device in {time.perf_counter() - t0:.1f} s",
           file=sys.stderr, flush=True)
@@ -89,38 +108,56 @@ def expert_bytes(cfg, U):
     return 3 * cfg.I * cfg.H * (2 if cfg.dtype == "bf16" else 4) * U
 
 
-def layer_bytes(cfg, T, U, bias):
-    """Algorithmic bytes of one call: activated experts, router, x, y."""
+def shared_bytes(cfg, lay):
+    """Weights of the layer's shared expert (gate, up, down, gate vector), or 0."""
+    sh = lay.get("shared")
+    if not sh:
+        return 0
+    return sum(sh[k].numel() * sh[k].element_size() for k in ("Sg", "Su", "Sd", "sg")
+               if sh[k] is not None)
+
+
+def layer_bytes(cfg, T, U, bias, wr_elt=4, shared=0):
+    """Algorithmic bytes of one call: activated experts, shared expert, router, x, y."""
     elt = 2 if cfg.dtype == "bf16" else 4
-    return expert_bytes(cfg, U) + cfg.E * cfg.H * 4 + (cfg.E * 4 if bias else 0) + \
-        2 * T * cfg.H * elt
+    return expert_bytes(cfg, U) + shared + cfg.E * cfg.H * wr_elt + \
+        (cfg.E * 4 if bias else 0) + 2 * T * cfg.H * elt
 
 
 def expert_flops(cfg, T, k1):
     return 6.0 * T * k1 * cfg.H * cfg.I
 
 
-def kernel_work(name, cfg, T, k1, U, bias):
+def kernel_work(name, cfg, T, k1, U, bias, wr_elt=4, shared=0):
     """(algorithmic bytes, flops) of one launch of the named kernel."""
     elt = 2 if cfg.dtype == "bf16" else 4
     H, E, I = cfg.H, cfg.E, cfg.I
-    router = E * H * 4 + (E * 4 if bias else 0) + T * H * elt
+    router = E * H * wr_elt + (E * 4 if bias else 0) + T * H * elt
     gu = 2 * U * I * H * elt
     dn = U * I * H * elt
     n = T * k1
     table = {
-        "b1_layer": (layer_bytes(cfg, T, U, bias), 2.0 * E * H + expert_flops(cfg, T, k1)),
+        "b1_layer": (layer_bytes(cfg, T, U, bias, wr_elt, shared),
+                     2.0 * E * H + expert_flops(cfg, T, k1)),
         "router": (router + T * E * 4, 2.0 * T * E * H),
         "router_route": (router, 2.0 * T * E * H),
         "gateup": (gu + T * H * elt, 4.0 * n * I * H),
         "down": (dn, 2.0 * n * I * H),
         "down_one_token": (dn + H * elt, 2.0 * n * I * H),
-        "fused_decode": (layer_bytes(cfg, T, U, bias), expert_flops(cfg, T, k1)),
+        "fused_decode": (layer_bytes(cfg, T, U, bias, wr_elt), expert_flops(cfg, T, k1)),
         "router_mma": (router + T * E * 4, 2.0 * T * E * H),
         "gateup_mma": (gu + T * H * elt, 4.0 * n * I * H),
         "down_mma": (dn, 2.0 * n * I * H),
     }
     return table.get(name, (None, None))
+
+
+def shared_args(lay):
+    """moe.forward's shared argument for a layer dict (None without one)."""
+    sh = lay.get("shared")
+    if not sh:
+        return None
+    return (sh["Sg"], sh["Su"], sh["Sd"]) + ((sh["sg"],) if sh["sg"] is not None else ())
 
 
 # ------------------------------------------------------------------ timing
@@ -133,7 +170,8 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
     ys = [torch.empty_like(x) for x in xs]
     lib = moe.load_library()
     act = 1 if cfg.dtype == "bf16" else 0
-    ws = torch.zeros(lib.moe_forward_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act),
+    Is = layers[0]["shared"]["Sg"].shape[0] if layers[0].get("shared") else 0
+    ws = torch.zeros(lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act),
                      dtype=torch.uint8, device=dev)
     ids_list = []
 
@@ -141,7 +179,8 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
         for i, lay in enumerate(layers):
             r = moe.forward(xs[i], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
                             br=lay["br"], out=ys[i], workspace=ws,
-                            return_route=record_ids, flags=PATH_FLAGS[path])
+                            return_route=record_ids, flags=PATH_FLAGS[path],
+                            shared=shared_args(lay))
             if record_ids:
                 ids_list.append(r[2].cpu().numpy())
 
@@ -184,11 +223,14 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
     U = unique_experts(ids_list)
     bias = layers[0]["br"] is not None
     per_rep.sort()
-    counted = expert_bytes(cfg, U)
-    total = layer_bytes(cfg, T, U, bias)
+    shb = shared_bytes(cfg, layers[0])
+    counted = expert_bytes(cfg, U) + shb
+    total = layer_bytes(cfg, T, U, bias, layers[0]["Wr"].element_size(), shb)
     flops = expert_flops(cfg, T, k1)
     return {
         "T": T, "k1": k1, "k2": k2, "path": path, "layers": L, "steps": n_rep * L,
+        "router": "bf16" if layers[0]["Wr"].dtype == torch.bfloat16 else "fp32",
+        "shared_expert_channels": Is,
         "us_per_layer": us,
         "us_p10": per_rep[len(per_rep) // 10], "us_p90": per_rep[(9 * len(per_rep)) // 10],
         "tokens_per_s": T / (us * 1e-6),
@@ -212,14 +254,16 @@ def profile_launches(moe, torch, cfg, layers, T, k1, k2, path, n_calls):
     ys = [torch.empty_like(x) for x in xs]
     lib = moe.load_library()
     act = 1 if cfg.dtype == "bf16" else 0
-    ws = torch.zeros(lib.moe_forward_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act),
+    Is = layers[0]["shared"]["Sg"].shape[0] if layers[0].get("shared") else 0
+    ws = torch.zeros(lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act),
                      dtype=torch.uint8, device=layers[0]["Wg"].device)
 
     def call(i):
         j = i % len(layers)
         lay = layers[j]
         moe.forward(xs[j], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
-                    br=lay["br"], out=ys[j], workspace=ws, flags=PATH_FLAGS[path])
+                    br=lay["br"], out=ys[j], workspace=ws, flags=PATH_FLAGS[path],
+                    shared=shared_args(lay))
 
     launches = []
     with torch.cuda.stream(stream):
@@ -261,11 +305,13 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
     import numpy as np
     x = layer["x"][:T]
     y, lg, ids, w = moe.forward(x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1, k2,
-                                br=layer["br"], return_route=True, flags=PATH_FLAGS[path])
+                                br=layer["br"], return_route=True, flags=PATH_FLAGS[path],
+                                shared=shared_args(layer))
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_dev.view(torch.int16)), "timed output differs"
     lg_h = lg.cpu().numpy()
-    oids, ow = oracle.route(lg_h, k1, k2)
+    bf16_router = layer["Wr"].dtype == torch.bfloat16
+    oids, ow = (oracle.route_bf16w if bf16_router else oracle.route)(lg_h, k1, k2)
     assert np.array_equal(oids, ids.cpu().numpy()) and \
         np.array_equal(ow.view(np.int32), w.cpu().numpy().view(np.int32)), "route differs"
     sel = np.unique(np.linspace(0, T - 1, min(T, n_tok)).astype(int))
@@ -276,6 +322,10 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
     Wg, Wu, Wd = (n(layer[k].index_select(0, idx)) for k in ("Wg", "Wu", "Wd"))
     rids = np.searchsorted(uniq, sids).astype(np.int32)
     y_ref = oracle.experts(n(x)[sel], Wg, Wu, Wd, rids, ow[sel], nthreads=8)
+    if layer.get("shared"):
+        sh = {k: n(v) for k, v in layer["shared"].items()}
+        y_ref = y_ref.astype(np.float64) + oracle.shared(n(x)[sel], sh["Sg"], sh["Su"], sh["Sd"],
+                                                         sh["sg"], nthreads=8)
     yd = y.float().cpu().numpy().astype(np.float64)[sel]
     err = float((np.abs(yd - y_ref).max(1) / np.abs(y_ref).max(1)).max())
     assert err <= 2e-2, f"normwise error {err}"
@@ -362,9 +412,9 @@ def main():
     cells = []
     for idx, (name, T, k1, k2, path) in enumerate(specs):
         cfg, layers = sets[name]
-        if name == "C4":
+        if name.startswith("C4"):
             steps = 50
-        elif name == "C5":
+        elif name.startswith("C5"):
             steps = len(layers) * (20 if T > 1 else 40)
         else:
             steps = args.steps if idx == 0 else min(args.steps, 50 * len(layers))
@@ -392,7 +442,8 @@ def main():
     launches, dom, dom_us = profile_launches(moe, torch, hcfg, hlayers, hT, hk1, hk2, hpath,
                                              min(args.steps, 50 * len(hlayers)))
     bias = hlayers[0]["br"] is not None
-    dom_bytes, _ = kernel_work(dom["kernel"], hcfg, hT, hk1, head["unique_experts"], bias)
+    dom_bytes, _ = kernel_work(dom["kernel"], hcfg, hT, hk1, head["unique_experts"], bias,
+                               hlayers[0]["Wr"].element_size(), shared_bytes(hcfg, hlayers[0]))
     print(f"# launches {launches}; dominant {dom['kernel']}: {dom_us:.2f} us per launch",
           file=sys.stderr, flush=True)
     calib = copy_calibration(torch)
@@ -409,10 +460,12 @@ def main():
 
     ratios = {}
     for cfgname, T in (("C2", 1), ("C3", 2), ("C3", 4), ("C3", 8), ("C3", 16), ("C3", 32),
-                       ("C3", 64), ("C3", 128), ("C3", 256)):
+                       ("C3", 64), ("C3", 128), ("C3", 256), ("C2h", 1), ("C3h", 8),
+                       ("C4", 4096), ("C4h", 4096), ("C2s", 1), ("C3s", 8), ("C4s", 4096)):
         a, b = find(cfgname, T, 4, 16), find(cfgname, T, 8, 8)
         if a and b:
-            ratios[f"b{T}_4:16_over_8:8"] = b["us_per_layer"] / a["us_per_layer"]
+            tag = {"h": "_bf16_router", "s": "_shared_expert"}.get(cfgname[2:], "")
+            ratios[f"b{T}_4:16_over_8:8{tag}"] = b["us_per_layer"] / a["us_per_layer"]
 
     us = head["us_per_layer"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None

@@ -126,17 +126,119 @@ hipError_t launch_plan(const int32_t *ids, int64_t n_assign, int E, int32_t *pla
 // token routed to u: a[t,r,c] = silu(Wg[e,c,:] x_t) * (Wu[e,c,:] x_t) * w[t,r].
 constexpr int kGuWaves = 4;
 
+// The weights, plan and outputs of one group of experts in a gate/up launch.
+// A launch takes the routed experts and, optionally, the shared expert as a
+// one-expert layer over every token; blocks [0, n0) take group g0 and the
+// rest g1.  The shared expert, when there is one, is g0: its blocks loop over
+// every token, so they start first and overlap the routed blocks.
+template <typename WT>
+struct GuGroup {
+  const WT *Wg, *Wu;
+  int I;
+  const int32_t *plan;
+  int E, k1;
+  const float *w;
+  float *abuf;
+};
+
+// NT assignments (list entries asg) against a wave's CPW gate and up rows
+// already in registers: a[asg, c] = silu(g . x) * (u . x) * w[asg].
+template <int NT, typename WT, typename XT, int NCH, int CPW>
+__device__ __forceinline__ void gateup_tokens(const XT *__restrict__ x, int H, int I, int k1,
+                                              const int32_t *__restrict__ asgs,
+                                              const float *__restrict__ w,
+                                              float *__restrict__ abuf,
+                                              const uint4 (&gq)[CPW][NCH],
+                                              const uint4 (&uq)[CPW][NCH], int c0) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  const int lane = lane_id();
+  int asg[NT];
+  const XT *xr[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    asg[q] = asgs[q];
+    xr[q] = x + (int64_t)(asg[q] / k1) * H;
+  }
+  float ag[NT][CPW], au[NT][CPW];
+#pragma unroll
+  for (int q = 0; q < NT; ++q)
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) ag[q][ci] = au[q][ci] = 0.0f;
+  if constexpr (sizeof(WT) == 2 && sizeof(XT) == 2) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      uint4 xq[NT];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) xq[q] = ld16(xr[q] + (j * kWave + lane) * NW);
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+          ag[q][ci] = dot2_bf16(gq[ci][j].x, xq[q].x, ag[q][ci]);
+          ag[q][ci] = dot2_bf16(gq[ci][j].y, xq[q].y, ag[q][ci]);
+          ag[q][ci] = dot2_bf16(gq[ci][j].z, xq[q].z, ag[q][ci]);
+          ag[q][ci] = dot2_bf16(gq[ci][j].w, xq[q].w, ag[q][ci]);
+          au[q][ci] = dot2_bf16(uq[ci][j].x, xq[q].x, au[q][ci]);
+          au[q][ci] = dot2_bf16(uq[ci][j].y, xq[q].y, au[q][ci]);
+          au[q][ci] = dot2_bf16(uq[ci][j].z, xq[q].z, au[q][ci]);
+          au[q][ci] = dot2_bf16(uq[ci][j].w, xq[q].w, au[q][ci]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      float xv[NT][NW];
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int k = 0; k < NW; ++k) xv[q][k] = Elem<XT>::load1(xr[q] + (j * kWave + lane) * NW + k);
+#pragma unroll
+      for (int ci = 0; ci < CPW; ++ci) {
+        float gv[NW], uv[NW];
+        Elem<WT>::widen(gq[ci][j], gv);
+        Elem<WT>::widen(uq[ci][j], uv);
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+#pragma unroll
+          for (int k = 0; k < NW; ++k) {
+            ag[q][ci] = __builtin_fmaf(gv[k], xv[q][k], ag[q][ci]);
+            au[q][ci] = __builtin_fmaf(uv[k], xv[q][k], au[q][ci]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const float wt = w[asg[q]];
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) {
+      const float g = wave_sum_dpp(ag[q][ci]);
+      const float uu = wave_sum_dpp(au[q][ci]);
+      const int c = c0 + ci;
+      if (lane == 0 && c < I) abuf[(int64_t)asg[q] * I + c] = silu(g) * uu * wt;
+    }
+  }
+}
+
 template <typename WT, typename XT, int NCH, int CPW>
 __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, int H,
-                                                     const WT *__restrict__ Wg,
-                                                     const WT *__restrict__ Wu, int I,
-                                                     const int32_t *__restrict__ plan, int E,
-                                                     int k1, const float *__restrict__ w,
-                                                     float *__restrict__ abuf) {
+                                                     GuGroup<WT> g0, GuGroup<WT> g1,
+                                                     unsigned n0) {
   constexpr int NW = Elem<WT>::kPer16B;
+  const bool second = blockIdx.x >= n0;
+  const GuGroup<WT> G = second ? g1 : g0;
+  const unsigned bid = second ? blockIdx.x - n0 : blockIdx.x;
+  const WT *__restrict__ Wg = G.Wg;
+  const WT *__restrict__ Wu = G.Wu;
+  const int I = G.I, E = G.E, k1 = G.k1;
+  const int32_t *__restrict__ plan = G.plan;
+  const float *__restrict__ w = G.w;
+  float *__restrict__ abuf = G.abuf;
   const int n_cb = (I + kGuWaves * CPW - 1) / (kGuWaves * CPW);
-  const int u = blockIdx.x / n_cb;
-  const int cb = blockIdx.x - u * n_cb;
+  const int u = bid / n_cb;
+  const int cb = bid - u * n_cb;
   if (u >= plan[0]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
@@ -157,70 +259,29 @@ __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, i
       uq[ci][j] = ld16_stream(urow + (j * kWave + lane) * NW);
     }
   }
-  for (int i = 0; i < ln; ++i) {
-    const int asg = list[lb + i];
-    const XT *xr = x + (int64_t)(asg / k1) * H;
-    const float wt = w[asg];
-    float ag[CPW], au[CPW];
-#pragma unroll
-    for (int ci = 0; ci < CPW; ++ci) ag[ci] = au[ci] = 0.0f;
-    if constexpr (sizeof(WT) == 2 && sizeof(XT) == 2) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const uint4 xq = ld16(xr + (j * kWave + lane) * NW);
-#pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-          ag[ci] = dot2_bf16(gq[ci][j].x, xq.x, ag[ci]);
-          ag[ci] = dot2_bf16(gq[ci][j].y, xq.y, ag[ci]);
-          ag[ci] = dot2_bf16(gq[ci][j].z, xq.z, ag[ci]);
-          ag[ci] = dot2_bf16(gq[ci][j].w, xq.w, ag[ci]);
-          au[ci] = dot2_bf16(uq[ci][j].x, xq.x, au[ci]);
-          au[ci] = dot2_bf16(uq[ci][j].y, xq.y, au[ci]);
-          au[ci] = dot2_bf16(uq[ci][j].z, xq.z, au[ci]);
-          au[ci] = dot2_bf16(uq[ci][j].w, xq.w, au[ci]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        float xv[NW];
-#pragma unroll
-        for (int k = 0; k < NW; ++k) xv[k] = Elem<XT>::load1(xr + (j * kWave + lane) * NW + k);
-#pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-          float gv[NW], uv[NW];
-          Elem<WT>::widen(gq[ci][j], gv);
-          Elem<WT>::widen(uq[ci][j], uv);
-#pragma unroll
-          for (int k = 0; k < NW; ++k) {
-            ag[ci] = __builtin_fmaf(gv[k], xv[k], ag[ci]);
-            au[ci] = __builtin_fmaf(uv[k], xv[k], au[ci]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int ci = 0; ci < CPW; ++ci) {
-      const float g = wave_sum_dpp(ag[ci]);
-      const float uu = wave_sum_dpp(au[ci]);
-      const int c = c0 + ci;
-      if (lane == 0 && c < I) abuf[(int64_t)asg * I + c] = silu(g) * uu * wt;
-    }
-  }
+  // one token at a time (two at a time measured slower: register pressure)
+  for (int i = 0; i < ln; ++i)
+    gateup_tokens<1, WT, XT, NCH, CPW>(x, H, I, k1, list + lb + i, w, abuf, gq, uq, c0);
 }
 
 // Any H (a multiple of 8): one channel per wave, chunks walked in a loop.
 template <typename WT, typename XT>
 __global__ __launch_bounds__(256) void gateup_any_kernel(const XT *__restrict__ x, int H,
-                                                         const WT *__restrict__ Wg,
-                                                         const WT *__restrict__ Wu, int I,
-                                                         const int32_t *__restrict__ plan, int E,
-                                                         int k1, const float *__restrict__ w,
-                                                         float *__restrict__ abuf) {
+                                                         GuGroup<WT> g0, GuGroup<WT> g1,
+                                                         unsigned n0) {
   constexpr int NW = Elem<WT>::kPer16B;
+  const bool second = blockIdx.x >= n0;
+  const GuGroup<WT> G = second ? g1 : g0;
+  const unsigned bid = second ? blockIdx.x - n0 : blockIdx.x;
+  const WT *__restrict__ Wg = G.Wg;
+  const WT *__restrict__ Wu = G.Wu;
+  const int I = G.I, E = G.E, k1 = G.k1;
+  const int32_t *__restrict__ plan = G.plan;
+  const float *__restrict__ w = G.w;
+  float *__restrict__ abuf = G.abuf;
   const int n_cb = (I + kGuWaves - 1) / kGuWaves;
-  const int u = blockIdx.x / n_cb;
-  const int cb = blockIdx.x - u * n_cb;
+  const int u = bid / n_cb;
+  const int cb = bid - u * n_cb;
   if (u >= plan[0]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
@@ -256,14 +317,19 @@ __global__ __launch_bounds__(256) void gateup_any_kernel(const XT *__restrict__ 
 template <typename WT, typename XT>
 hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
-                         float *abuf, hipStream_t s) {
+                         float *abuf, hipStream_t s, const WT *Sg, const WT *Su, int Is,
+                         const int32_t *plan_s, const float *gs, float *abuf_s) {
   const int64_t umax = n_assign < E ? n_assign : E;
   const int nch = (H * (int)sizeof(WT)) % (16 * kWave) == 0 ? (int)(H * sizeof(WT) / 16 / kWave) : 0;
+  const GuGroup<WT> gr{Wg, Wu, I, plan, E, k1, w, abuf};
+  const GuGroup<WT> gsh{Sg, Su, Is, plan_s, 1, 1, gs, abuf_s};
+  const GuGroup<WT> g0 = Sg ? gsh : gr;
   auto go = [&](auto nch_c, auto cpw_c) {
     constexpr int NCH = decltype(nch_c)::value, CPW = decltype(cpw_c)::value;
-    const int n_cb = (I + kGuWaves * CPW - 1) / (kGuWaves * CPW);
-    gateup_kernel<WT, XT, NCH, CPW><<<dim3((unsigned)(umax * n_cb)), dim3(256), 0, s>>>(
-        x, H, Wg, Wu, I, plan, E, k1, w, abuf);
+    const unsigned n_r = (unsigned)(umax * ((I + kGuWaves * CPW - 1) / (kGuWaves * CPW)));
+    const unsigned n_sh = Sg ? (unsigned)((Is + kGuWaves * CPW - 1) / (kGuWaves * CPW)) : 0u;
+    gateup_kernel<WT, XT, NCH, CPW><<<dim3(n_r + n_sh), dim3(256), 0, s>>>(x, H, g0, gr,
+                                                                           Sg ? n_sh : n_r);
   };
   using std::integral_constant;
   switch (nch) {
@@ -272,9 +338,10 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
     case 4: go(integral_constant<int, 4>{}, integral_constant<int, 2>{}); break;
     case 8: go(integral_constant<int, 8>{}, integral_constant<int, 1>{}); break;
     default: {
-      const int n_cb = (I + kGuWaves - 1) / kGuWaves;
-      gateup_any_kernel<WT, XT><<<dim3((unsigned)(umax * n_cb)), dim3(256), 0, s>>>(
-          x, H, Wg, Wu, I, plan, E, k1, w, abuf);
+      const unsigned n_r = (unsigned)(umax * ((I + kGuWaves - 1) / kGuWaves));
+      const unsigned n_sh = Sg ? (unsigned)((Is + kGuWaves - 1) / kGuWaves) : 0u;
+      gateup_any_kernel<WT, XT><<<dim3(n_r + n_sh), dim3(256), 0, s>>>(x, H, g0, gr,
+                                                                        Sg ? n_sh : n_r);
     }
   }
   return hipGetLastError();
@@ -288,15 +355,85 @@ constexpr int kDnWaves = 4;
 constexpr int kRPW = 2;
 constexpr int kDnRB = kDnWaves * kRPW;
 
-template <typename WT, int NCD>
-__global__ __launch_bounds__(256) void down_kernel(const WT *__restrict__ Wd, int H, int I,
-                                                   const int32_t *__restrict__ plan, int E,
-                                                   const float *__restrict__ abuf,
-                                                   float *__restrict__ zbuf) {
+// One group of experts in a down launch (see GuGroup, whose block order it
+// follows): Wd holds E experts' [H, I] down matrices; the shared expert's
+// [H, Is] is one such expert.
+template <typename WT>
+struct DnGroup {
+  const WT *Wd;
+  int I;
+  const int32_t *plan;
+  int E;
+  const float *abuf;
+  float *zbuf;
+};
+
+// NT assignments against a wave's kRPW down rows already in registers:
+// z[asg, h] = Wd[e, h, :] . a[asg, :].
+template <int NT, typename WT, int NCD>
+__device__ __forceinline__ void down_tokens(int H, int I, const int32_t *__restrict__ asgs,
+                                            const float *__restrict__ abuf,
+                                            float *__restrict__ zbuf,
+                                            const uint4 (&dq)[kRPW][NCD], int h0) {
   constexpr int NW = Elem<WT>::kPer16B;
+  const int lane = lane_id();
+  const int nch = I / NW;
+  int asg[NT];
+  float av[NT][NCD][NW];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    asg[q] = asgs[q];
+    const float *arow = abuf + (int64_t)asg[q] * I;
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      const int ch = j * kWave + lane;
+      if (ch < nch) {
+        Elem<float>::widen(ld16(arow + ch * NW), av[q][j]);
+        if constexpr (NW == 8) Elem<float>::widen(ld16(arow + ch * NW + 4), av[q][j] + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) av[q][j][k] = 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int ri = 0; ri < kRPW; ++ri) {
+    float acc[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      float dv[NW];
+      Elem<WT>::widen(dq[ri][j], dv);
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int k = 0; k < NW; ++k) acc[q] = __builtin_fmaf(dv[k], av[q][j][k], acc[q]);
+    }
+    const int h = h0 + ri;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const float z = wave_sum_dpp(acc[q]);
+      if (lane == 0 && h < H) zbuf[(int64_t)asg[q] * H + h] = z;
+    }
+  }
+}
+
+template <typename WT, int NCD>
+__global__ __launch_bounds__(256) void down_kernel(int H, DnGroup<WT> g0, DnGroup<WT> g1,
+                                                   unsigned n0) {
+  constexpr int NW = Elem<WT>::kPer16B;
+  const bool second = blockIdx.x >= n0;
+  const DnGroup<WT> G = second ? g1 : g0;
+  const unsigned bid = second ? blockIdx.x - n0 : blockIdx.x;
+  const WT *__restrict__ Wd = G.Wd;
+  const int I = G.I, E = G.E;
+  const int32_t *__restrict__ plan = G.plan;
+  const float *__restrict__ abuf = G.abuf;
+  float *__restrict__ zbuf = G.zbuf;
   const int n_hb = (H + kDnRB - 1) / kDnRB;
-  const int u = blockIdx.x / n_hb;
-  const int hb = blockIdx.x - u * n_hb;
+  const int u = bid / n_hb;
+  const int hb = bid - u * n_hb;
   if (u >= plan[0]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
@@ -316,49 +453,26 @@ __global__ __launch_bounds__(256) void down_kernel(const WT *__restrict__ Wd, in
       dq[ri][j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
     }
   }
-  for (int i = 0; i < ln; ++i) {
-    const int asg = list[lb + i];
-    const float *arow = abuf + (int64_t)asg * I;
-    float av[NCD][NW];
-#pragma unroll
-    for (int j = 0; j < NCD; ++j) {
-      const int ch = j * kWave + lane;
-      if (ch < nch) {
-        const uint4 q0 = ld16(arow + ch * NW);
-        Elem<float>::widen(q0, av[j]);
-        if constexpr (NW == 8) Elem<float>::widen(ld16(arow + ch * NW + 4), av[j] + 4);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) av[j][k] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int ri = 0; ri < kRPW; ++ri) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCD; ++j) {
-        float dv[NW];
-        Elem<WT>::widen(dq[ri][j], dv);
-#pragma unroll
-        for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[j][k], acc);
-      }
-      acc = wave_sum_dpp(acc);
-      const int h = h0 + ri;
-      if (lane == 0 && h < H) zbuf[(int64_t)asg * H + h] = acc;
-    }
-  }
+  // one token at a time (two at a time measured slower: register pressure)
+  for (int i = 0; i < ln; ++i) down_tokens<1, WT, NCD>(H, I, list + lb + i, abuf, zbuf, dq, h0);
 }
 
 // Any I: one row per wave, chunks walked in a loop.
 template <typename WT>
-__global__ __launch_bounds__(256) void down_any_kernel(const WT *__restrict__ Wd, int H, int I,
-                                                       const int32_t *__restrict__ plan, int E,
-                                                       const float *__restrict__ abuf,
-                                                       float *__restrict__ zbuf) {
+__global__ __launch_bounds__(256) void down_any_kernel(int H, DnGroup<WT> g0, DnGroup<WT> g1,
+                                                       unsigned n0) {
   constexpr int NW = Elem<WT>::kPer16B;
+  const bool second = blockIdx.x >= n0;
+  const DnGroup<WT> G = second ? g1 : g0;
+  const unsigned bid = second ? blockIdx.x - n0 : blockIdx.x;
+  const WT *__restrict__ Wd = G.Wd;
+  const int I = G.I, E = G.E;
+  const int32_t *__restrict__ plan = G.plan;
+  const float *__restrict__ abuf = G.abuf;
+  float *__restrict__ zbuf = G.zbuf;
   const int n_hb = (H + kDnWaves - 1) / kDnWaves;
-  const int u = blockIdx.x / n_hb;
-  const int hb = blockIdx.x - u * n_hb;
+  const int u = bid / n_hb;
+  const int hb = bid - u * n_hb;
   if (u >= plan[0]) return;
   const int32_t *uniq = plan + 4;
   const int32_t *off = uniq + E;
@@ -387,20 +501,28 @@ __global__ __launch_bounds__(256) void down_any_kernel(const WT *__restrict__ Wd
 
 template <typename WT>
 hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
-                       const float *abuf, float *zbuf, hipStream_t s) {
+                       const float *abuf, float *zbuf, hipStream_t s, const WT *Sd, int Is,
+                       const int32_t *plan_s, const float *abuf_s, float *zbuf_s) {
   const int64_t umax = n_assign < E ? n_assign : E;
   const int n_hb = (H + kDnRB - 1) / kDnRB;
-  const int ncd = (int)((I * sizeof(WT) / 16 + kWave - 1) / kWave);
-  const dim3 grid((unsigned)(umax * n_hb)), block(256);
+  auto ncd_of = [](int i) { return (int)((i * sizeof(WT) / 16 + kWave - 1) / kWave); };
+  // one NCD for both groups: the wider one (chunks past a row's end are masked)
+  const int ncd = Sd ? max(ncd_of(I), ncd_of(Is)) : ncd_of(I);
+  const DnGroup<WT> gr{Wd, I, plan, E, abuf, zbuf};
+  const DnGroup<WT> gsh{Sd, Is, plan_s, 1, abuf_s, zbuf_s};
+  const DnGroup<WT> g0 = Sd ? gsh : gr;
+  const unsigned n_r = (unsigned)(umax * n_hb), n_sh = Sd ? (unsigned)n_hb : 0u;
+  const unsigned n0 = Sd ? n_sh : n_r;
+  const dim3 grid(n_r + n_sh), block(256);
   switch (ncd) {
-    case 1: down_kernel<WT, 1><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
-    case 2: down_kernel<WT, 2><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
-    case 3: down_kernel<WT, 3><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
-    case 4: down_kernel<WT, 4><<<grid, block, 0, s>>>(Wd, H, I, plan, E, abuf, zbuf); break;
+    case 1: down_kernel<WT, 1><<<grid, block, 0, s>>>(H, g0, gr, n0); break;
+    case 2: down_kernel<WT, 2><<<grid, block, 0, s>>>(H, g0, gr, n0); break;
+    case 3: down_kernel<WT, 3><<<grid, block, 0, s>>>(H, g0, gr, n0); break;
+    case 4: down_kernel<WT, 4><<<grid, block, 0, s>>>(H, g0, gr, n0); break;
     default: {
       const int n_hb1 = (H + kDnWaves - 1) / kDnWaves;
-      down_any_kernel<WT><<<dim3((unsigned)(umax * n_hb1)), block, 0, s>>>(Wd, H, I, plan, E, abuf,
-                                                                           zbuf);
+      const unsigned m_r = (unsigned)(umax * n_hb1), m_sh = Sd ? (unsigned)n_hb1 : 0u;
+      down_any_kernel<WT><<<dim3(m_r + m_sh), block, 0, s>>>(H, g0, gr, Sd ? m_sh : m_r);
     }
   }
   return hipGetLastError();
@@ -554,9 +676,12 @@ hipError_t launch_shared_prep(const XT *x, int64_t T, int H, const float *sgw, i
 #define MOE_INST_DECODE(WT, XT)                                                             \
   template hipError_t launch_gateup<WT, XT>(const XT *, int, const WT *, const WT *, int, \
                                             const int32_t *, int, int64_t, int,           \
-                                            const float *, float *, hipStream_t);         \
+                                            const float *, float *, hipStream_t,          \
+                                            const WT *, const WT *, int, const int32_t *, \
+                                            const float *, float *);                      \
   template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t, \
-                                      const float *, float *, hipStream_t);               \
+                                      const float *, float *, hipStream_t, const WT *, int, \
+                                      const int32_t *, const float *, float *);           \
   template hipError_t launch_combine<XT>(const float *, const float *, int64_t, int, int, XT *, \
                                          hipStream_t);                                        \
   template hipError_t launch_shared_prep<XT>(const XT *, int64_t, int, const float *, int32_t *, \

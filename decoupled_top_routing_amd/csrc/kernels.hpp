@@ -107,14 +107,21 @@ hipError_t launch_combine_bf16(const uint16_t *zbf, const uint16_t *zs, int64_t 
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
 
+// Grouped gate/up and down over the plan's experts; with Sg (Sd) the same
+// launch also runs the shared expert as a one-expert layer (plan_s, factors
+// gs, activations abuf_s [T, Is], outputs zbuf_s [T, H]).
 template <typename WT, typename XT>
 hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
-                         float *abuf, hipStream_t s);
+                         float *abuf, hipStream_t s, const WT *Sg = nullptr,
+                         const WT *Su = nullptr, int Is = 0, const int32_t *plan_s = nullptr,
+                         const float *gs = nullptr, float *abuf_s = nullptr);
 
 template <typename WT>
 hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
-                       const float *abuf, float *zbuf, hipStream_t s);
+                       const float *abuf, float *zbuf, hipStream_t s, const WT *Sd = nullptr,
+                       int Is = 0, const int32_t *plan_s = nullptr,
+                       const float *abuf_s = nullptr, float *zbuf_s = nullptr);
 
 // zs: the shared expert's term [T, H], or NULL
 template <typename XT>

@@ -335,25 +335,26 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
       RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
     }
   }
-  RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s)));
+  // the shared expert runs as a one-expert layer over every token, inside
+  // the routed gate/up and down launches
+  int32_t *plan_s = nullptr;
+  float *gs = nullptr, *abuf_s = nullptr, *zbuf_s = nullptr;
+  if (Sg) {
+    plan_s = reinterpret_cast<int32_t *>(ws + L.plan_s);
+    gs = reinterpret_cast<float *>(ws + L.gs);
+    abuf_s = reinterpret_cast<float *>(ws + L.abuf_s);
+    zbuf_s = reinterpret_cast<float *>(ws + L.zbuf_s);
+    RUN("shared_prep", moe::launch_shared_prep<XT>(x, T, H, sh.sgw, plan_s, nullptr, gs, s));
+  }
+  RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s,
+                                            Sg, Su, sh.Is, plan_s, gs, abuf_s)));
   const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
   if (T == 1 && ncd <= 2 && !Sg) {
     RUN("down_one_token", (moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)));
     return MOE_OK;
   }
-  RUN("down", moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s));
-  float *zbuf_s = nullptr;
-  if (Sg) {
-    // the shared expert as a one-expert layer over every token
-    int32_t *plan_s = reinterpret_cast<int32_t *>(ws + L.plan_s);
-    float *gs = reinterpret_cast<float *>(ws + L.gs);
-    float *abuf_s = reinterpret_cast<float *>(ws + L.abuf_s);
-    zbuf_s = reinterpret_cast<float *>(ws + L.zbuf_s);
-    RUN("shared_prep", moe::launch_shared_prep<XT>(x, T, H, sh.sgw, plan_s, nullptr, gs, s));
-    RUN("shared_gateup",
-        (moe::launch_gateup<WT, XT>(x, H, Sg, Su, sh.Is, plan_s, 1, T, 1, gs, abuf_s, s)));
-    RUN("shared_down", moe::launch_down<WT>(Sd, H, sh.Is, plan_s, 1, T, abuf_s, zbuf_s, s));
-  }
+  RUN("down", moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s, Sd, sh.Is, plan_s,
+                                   abuf_s, zbuf_s));
   RUN("combine", moe::launch_combine<XT>(zbuf, zbuf_s, T, H, k1, y, s));
   return MOE_OK;
 }
