@@ -44,6 +44,12 @@ appendix B): a gated MLP of Is channels whose output is added to the routed
 sum, scaled by sigmoid(x . sg) with a gate vector sg, else by 1 (a reading:
 the pages do not give the gating).
 
+Channel top-k (``down_column_norms``, ``channel_scores``, ``channel_select``,
+``experts_kept``): "Channel Selection ..." section 5.2 scores each channel of
+a token's activated experts by router weight x down-column norm x activation
+magnitude, keeps the exact top ``keep`` over the token's k1*I channels (equal
+scores: lower flat index r*I + c first, a reading) and sums only those.
+
 The route functions (``softmax``, ``route``) are exact fp32 definitions; the
 expert functions are accumulated in fp64.  Arrays are numpy; bf16 tensors are
 passed as ``uint16`` bit patterns.
@@ -123,6 +129,16 @@ def _open(path):
                                                i32, i32, P, P, P, P, cint]
     lib.oracle_shared.restype = cint
     lib.oracle_shared.argtypes = [P, cint, i64, i32, P, P, P, cint, i32, P, P, cint]
+    lib.oracle_down_column_norms.restype = cint
+    lib.oracle_down_column_norms.argtypes = [P, cint, i32, i32, i32, P]
+    lib.oracle_channel_scores.restype = cint
+    lib.oracle_channel_scores.argtypes = [P, cint, i64, i32, P, P, cint, i32, i32, i32, P, P,
+                                          P, P]
+    lib.oracle_channel_select.restype = cint
+    lib.oracle_channel_select.argtypes = [P, i64, i32, i32, P]
+    lib.oracle_experts_kept.restype = cint
+    lib.oracle_experts_kept.argtypes = [P, cint, i64, i32, P, P, P, cint, i32, i32, i32, P, P,
+                                        P, P]
     return lib
 
 
@@ -326,3 +342,57 @@ def shared(x, Sg, Su, Sd, sg=None, nthreads: int = 1):
     _check(lib.oracle_shared(_ptr(x), _dtype_code(x), T, H, _ptr(Sg), _ptr(Su), _ptr(Sd), wt,
                              Is, _ptr(sg), _ptr(ys), nthreads), "oracle_shared")
     return ys
+
+
+def down_column_norms(Wd):
+    """dn [E,I] float32: the 2-norm of each down column Wd[e,:,c]."""
+    lib = _load()
+    Wd = _c(Wd)
+    E, H, I = Wd.shape
+    dn = np.empty((E, I), np.float32)
+    _check(lib.oracle_down_column_norms(_ptr(Wd), _dtype_code(Wd), E, H, I, _ptr(dn)),
+           "oracle_down_column_norms")
+    return dn
+
+
+def channel_scores(x, Wg, Wu, ids, w, dn):
+    """scores [T, k1*I] float32 = w_r * dn[e_r, c] * |silu(g) * u|."""
+    lib = _load()
+    x, Wg, Wu = _c(x), _c(Wg), _c(Wu)
+    ids, w, dn = _c(ids, np.int32), _c(w, np.float32), _c(dn, np.float32)
+    T, H = x.shape
+    E, I, _ = Wg.shape
+    k1 = ids.shape[1]
+    out = np.empty((T, k1 * I), np.float32)
+    _check(lib.oracle_channel_scores(_ptr(x), _dtype_code(x), T, H, _ptr(Wg), _ptr(Wu),
+                                     _dtype_code(Wg), E, I, k1, _ptr(ids), _ptr(w), _ptr(dn),
+                                     _ptr(out)), "oracle_channel_scores")
+    return out
+
+
+def channel_select(scores, keep: int):
+    """kept [T, n] bool: the keep highest scores per row, lower index on ties."""
+    lib = _load()
+    scores = _c(scores, np.float32)
+    T, n = scores.shape
+    kept = np.zeros((T, n), np.uint8)
+    _check(lib.oracle_channel_select(_ptr(scores), T, n, keep, _ptr(kept)),
+           "oracle_channel_select")
+    return kept.astype(bool)
+
+
+def experts_kept(x, Wg, Wu, Wd, ids, w, kept):
+    """y [T,H] float32 from the kept channels only."""
+    lib = _load()
+    x, Wg, Wu, Wd = _c(x), _c(Wg), _c(Wu), _c(Wd)
+    ids, w = _c(ids, np.int32), _c(w, np.float32)
+    kept = _c(np.asarray(kept, np.uint8))
+    T, H = x.shape
+    E, I, _ = Wg.shape
+    k1 = ids.shape[1]
+    assert kept.shape == (T, k1 * I)
+    y = np.empty((T, H), np.float32)
+    _check(lib.oracle_experts_kept(_ptr(x), _dtype_code(x), T, H, _ptr(Wg), _ptr(Wu), _ptr(Wd),
+                                   _dtype_code(Wg), E, I, k1, _ptr(ids), _ptr(w), _ptr(kept),
+                                   _ptr(y)), "oracle_experts_kept")
+    return y

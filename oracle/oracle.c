@@ -523,3 +523,133 @@ int oracle_shared(const void *x, int act, int64_t T, int32_t H,
     }
     return bad ? OR_ENOMEM : OR_OK;
 }
+
+/* ================================================================== */
+/* Channel top-k inside the activated experts ("Channel Selection for */
+/* Mixture-of-Experts Decoding Needs No Calibration Data", section 5.2 */
+/* "output-scaled score"; section 2: a channel owns one gate row, one  */
+/* up row and one down column).  For a token routed to experts e_r    */
+/* with weights w_r, channel (r, c) has                                */
+/*   a = silu(Wg[e_r,c,:] . x) * (Wu[e_r,c,:] . x),                    */
+/*   score = w_r * ||Wd[e_r,:,c]||_2 * |a|,                             */
+/* an estimate of its output contribution in output units, so channels */
+/* of different experts compare; the keep highest scores over the     */
+/* token's k1*I channels are kept (exact top-k; reading: equal scores */
+/* go to the lower flat index r*I + c), and                            */
+/*   y = sum over kept (r, c), in flat-index order, of w_r a Wd[e_r,:,c]. */
+/* fp64 throughout; scores rounded once to fp32.                       */
+/* ================================================================== */
+
+/* dn[e, c] = ||Wd[e, :, c]||_2 */
+int oracle_down_column_norms(const void *Wd, int wt, int32_t E, int32_t H,
+                             int32_t I, float *dn)
+{
+    if (E < 1 || H < 1 || I < 1 || (wt != OR_F32 && wt != OR_BF16))
+        return OR_EINVAL;
+    for (int64_t e = 0; e < E; ++e)
+        for (int32_t c = 0; c < I; ++c) {
+            double s = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                double v = load_elem(Wd, wt, (e * H + h) * (int64_t)I + c);
+                s += v * v;
+            }
+            dn[e * I + c] = (float)sqrt(s);
+        }
+    return OR_OK;
+}
+
+/* scores [T, k1*I] of the channels of each token's activated experts */
+int oracle_channel_scores(const void *x, int act, int64_t T, int32_t H,
+                          const void *Wg, const void *Wu, int wt, int32_t E,
+                          int32_t I, int32_t k1, const int32_t *ids,
+                          const float *w, const float *dn, float *scores)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k1 < 1)
+        return OR_EINVAL;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t r = 0; r < k1; ++r) {
+            int64_t e = ids[t * k1 + r];
+            if (e < 0 || e >= E)
+                return OR_EINVAL;
+            for (int32_t c = 0; c < I; ++c) {
+                int64_t row = (e * I + c) * (int64_t)H;
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    double xv = load_elem(x, act, t * H + h);
+                    g += load_elem(Wg, wt, row + h) * xv;
+                    u += load_elem(Wu, wt, row + h) * xv;
+                }
+                double a = silu(g) * u;
+                scores[(t * k1 + r) * (int64_t)I + c] =
+                    (float)((double)w[t * k1 + r] * (double)dn[e * I + c] * fabs(a));
+            }
+        }
+    return OR_OK;
+}
+
+/* kept[t, j] = 1 for the keep highest scores of row t (n = k1*I scores),
+ * equal scores to the lower j; keep rounds of "take the best not taken". */
+int oracle_channel_select(const float *scores, int64_t T, int32_t n, int32_t keep,
+                          unsigned char *kept)
+{
+    if (T < 0 || n < 1 || keep < 0 || keep > n)
+        return OR_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *s = scores + t * n;
+        unsigned char *k = kept + t * n;
+        memset(k, 0, (size_t)n);
+        for (int32_t q = 0; q < keep; ++q) {
+            int32_t best = -1;
+            for (int32_t j = 0; j < n; ++j) {
+                if (k[j])
+                    continue;
+                if (best < 0 || s[j] > s[best])
+                    best = j; /* strict '>' keeps the lower index on ties */
+            }
+            k[best] = 1;
+        }
+    }
+    return OR_OK;
+}
+
+/* y [T, H] from the kept channels only (flat-index order). */
+int oracle_experts_kept(const void *x, int act, int64_t T, int32_t H,
+                        const void *Wg, const void *Wu, const void *Wd, int wt,
+                        int32_t E, int32_t I, int32_t k1, const int32_t *ids,
+                        const float *w, const unsigned char *kept, float *y)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k1 < 1)
+        return OR_EINVAL;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!acc)
+        return OR_ENOMEM;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h)
+            acc[h] = 0.0;
+        for (int32_t r = 0; r < k1; ++r) {
+            int64_t e = ids[t * k1 + r];
+            if (e < 0 || e >= E) {
+                free(acc);
+                return OR_EINVAL;
+            }
+            for (int32_t c = 0; c < I; ++c) {
+                if (!kept[(t * k1 + r) * (int64_t)I + c])
+                    continue;
+                int64_t row = (e * I + c) * (int64_t)H;
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    double xv = load_elem(x, act, t * H + h);
+                    g += load_elem(Wg, wt, row + h) * xv;
+                    u += load_elem(Wu, wt, row + h) * xv;
+                }
+                double a = silu(g) * u * (double)w[t * k1 + r];
+                for (int32_t h = 0; h < H; ++h)
+                    acc[h] += load_elem(Wd, wt, (e * H + h) * (int64_t)I + c) * a;
+            }
+        }
+        for (int32_t h = 0; h < H; ++h)
+            y[t * H + h] = (float)acc[h];
+    }
+    free(acc);
+    return OR_OK;
+}

@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import test_oracle_bf16_router_pins as hf_pins
+import test_oracle_channel_topk_pins as ck_pins
 import test_oracle_pins as pins
 import test_oracle_shared_pins as shared_pins
 
@@ -60,6 +61,18 @@ MUTANTS = {
         ("a[c] = silu(gg) * u;", "a[c] = gg * silu(u);"),
     "shared expert gate and up read the same row":
         ("u += load_elem(Su, wt, row + h) * xv[h];", "u += load_elem(Sg, wt, row + h) * xv[h];"),
+    "channel select takes the higher index on ties":
+        ("if (best < 0 || s[j] > s[best])", "if (best < 0 || s[j] >= s[best])"),
+    "channel score without the down-column norm":
+        ("(float)((double)w[t * k1 + r] * (double)dn[e * I + c] * fabs(a));",
+         "(float)((double)w[t * k1 + r] * fabs(a));"),
+    "channel score on the signed activation":
+        ("(float)((double)w[t * k1 + r] * (double)dn[e * I + c] * fabs(a));",
+         "(float)((double)w[t * k1 + r] * (double)dn[e * I + c] * a);"),
+    "column norm without the square root":
+        ("dn[e * I + c] = (float)sqrt(s);", "dn[e * I + c] = (float)s;"),
+    "kept channels not weighted":
+        ("double a = silu(g) * u * (double)w[t * k1 + r];", "double a = silu(g) * u;"),
 }
 
 PIN_CHECKS = [
@@ -81,6 +94,10 @@ PIN_CHECKS = [
     lambda: hf_pins.test_bf16_router_at_k1_eq_k2_is_stock_bitwise(128, 8),
     lambda: shared_pins.test_shared_matches_numpy_fp64(False, True),
     shared_pins.test_zero_gate_vector_halves_the_expert,
+    ck_pins.test_down_column_norms_match_numpy,
+    ck_pins.test_scores_match_numpy_fp64,
+    lambda: ck_pins.test_select_matches_a_lexicographic_sort(50),
+    ck_pins.test_kept_layer_matches_numpy_masked_fp64,
 ]
 
 
