@@ -19,7 +19,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["route", "forward", "MoeError", "library_path", "load_library",
+__all__ = ["route", "forward", "forward_channel_topk", "down_column_norms", "MoeError", "library_path", "load_library",
            "F32", "BF16", "FORCE_FUSED", "FORCE_GROUPED", "FORCE_PREFILL", "ROUTER_BF16"]
 
 PKG = Path(__file__).resolve().parent
@@ -74,6 +74,12 @@ def load_library():
         lib.moe_forward_shared.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
                                            i32, P, P, P, i32, P, P, P, P, P, u32, P,
                                            ctypes.c_size_t, P]
+        lib.moe_down_column_norms.restype = ctypes.c_int
+        lib.moe_down_column_norms.argtypes = [P, i32, i32, i32, i32, P, P]
+        lib.moe_forward_channel_topk.restype = ctypes.c_int
+        lib.moe_forward_channel_topk.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32,
+                                                 i32, i32, P, i32, P, P, P, P, P, P, u32, P,
+                                                 ctypes.c_size_t, P]
         lib.moe_forward_shared_workspace.restype = ctypes.c_size_t
         lib.moe_forward_shared_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
         lib.moe_profile_launch.restype = ctypes.c_int
@@ -234,4 +240,61 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
                                       _ptr(w), flags, _ptr(ws), ws.numel(), stream))
     if return_route:
         return y, lg, ids, w
+    return y
+
+
+def down_column_norms(Wdown):
+    """dnorm [E, I] fp32: the 2-norm of each down column Wdown[e, :, c]."""
+    lib = load_library()
+    _need_cuda("Wdown", Wdown)
+    E, H, I = Wdown.shape
+    dn = torch.empty((E, I), dtype=torch.float32, device=Wdown.device)
+    _check(lib.moe_down_column_norms(_ptr(Wdown), _dtype_code(Wdown), E, H, I, _ptr(dn),
+                                     _stream(Wdown.device)))
+    return dn
+
+
+def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep: int,
+                         br=None, return_route: bool = False, flags: int = 0):
+    """The layer with channel top-k inside the activated experts: of each
+    token's k1*I channels only the ``keep`` highest-scoring (router weight x
+    down-column norm x |activation|) are summed.  ``dnorm`` comes from
+    ``down_column_norms``.  Returns y, or (y, logits, ids, w, scores, kept)
+    with ``return_route=True`` (scores [T, k1*I] fp32, kept [T, k1*I] bool)."""
+    lib = load_library()
+    _need_cuda("x", x)
+    act = _dtype_code(x)
+    if Wr.dtype == torch.bfloat16:
+        flags |= ROUTER_BF16
+    _need_cuda("Wr", Wr, torch.bfloat16 if flags & ROUTER_BF16 else torch.float32)
+    for n, t in (("Wgate", Wgate), ("Wup", Wup), ("Wdown", Wdown)):
+        _need_cuda(n, t, x.dtype)
+    _need_cuda("dnorm", dnorm, torch.float32)
+    if br is not None:
+        _need_cuda("br", br, torch.float32)
+    T, H = x.shape
+    E, I, H2 = Wgate.shape
+    if H2 != H or Wup.shape != Wgate.shape or tuple(Wdown.shape) != (E, H, I) \
+            or tuple(Wr.shape) != (E, H) or tuple(dnorm.shape) != (E, I):
+        raise MoeError(1, "shape mismatch between x, Wr, Wgate, Wup, Wdown and dnorm")
+    dev = x.device
+    y = torch.empty((T, H), dtype=x.dtype, device=dev)
+    lg = ids = w = sc = kept = None
+    if return_route:
+        lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k1), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k1), dtype=torch.float32, device=dev)
+        sc = torch.empty((T, k1 * I), dtype=torch.float32, device=dev)
+        kept = torch.empty((T, k1 * I), dtype=torch.uint8, device=dev)
+    nbytes = lib.moe_forward_workspace(T, H, E, I, k1, act, act)
+    if nbytes == 0 and T > 0:
+        raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
+    stream = _stream(dev)
+    ws = _workspace(dev, stream.value or 0, nbytes)
+    _check(lib.moe_forward_channel_topk(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
+                                        _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(dnorm), keep,
+                                        _ptr(y), _ptr(lg), _ptr(ids), _ptr(w), _ptr(sc),
+                                        _ptr(kept), flags, _ptr(ws), ws.numel(), stream))
+    if return_route:
+        return y, lg, ids, w, sc, kept.bool()
     return y

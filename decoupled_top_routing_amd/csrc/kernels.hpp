@@ -104,6 +104,16 @@ hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I
 hipError_t launch_combine_bf16(const uint16_t *zbf, const uint16_t *zs, int64_t T, int H, int k1,
                                uint16_t *y, hipStream_t s);
 
+// ---- channel top-k inside the activated experts
+bool channel_select_supported(int k1, int I);
+template <typename WT>
+hipError_t launch_down_column_norms(const WT *Wd, int E, int H, int I, float *dn, hipStream_t s);
+// zeroes every activation of abuf [T*k1, I] outside each token's top-keep
+// channels by score dn[e, c] * |a|; optional scores and kept flags [T, k1*I]
+hipError_t launch_channel_select(float *abuf, int64_t T, int k1, int I, const int32_t *ids,
+                                 const float *dn, int keep, float *scores_out, uint8_t *kept_out,
+                                 hipStream_t s);
+
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
 

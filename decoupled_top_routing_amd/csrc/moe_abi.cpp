@@ -38,6 +38,14 @@ struct Shared {
   const float *sgw = nullptr;
 };
 
+// Channel top-k of moe_forward_channel_topk (dn == NULL: off).
+struct ChannelTopk {
+  const float *dn = nullptr;
+  int32_t keep = 0;
+  float *scores_out = nullptr;
+  uint8_t *kept_out = nullptr;
+};
+
 // pieces of I channels the one-launch kernel splits the shared expert into
 // (0: none, or Is not a multiple of I)
 int shared_pieces(int32_t I, int32_t Is) { return Is > 0 && Is % I == 0 ? Is / I : 0; }
@@ -275,9 +283,9 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, boo
 template <typename WT, typename XT>
 int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router_bf16,
                   const float *br, int32_t E, const WT *Wg, const WT *Wu, const WT *Wd, int32_t I,
-                  int32_t k1, int32_t k2, const Shared &sh, XT *y, float *logits_out,
-                  int32_t *ids_out, float *w_out, Path path, char *ws, const Layout &L,
-                  Launches &run) {
+                  int32_t k1, int32_t k2, const Shared &sh, const ChannelTopk &ck, XT *y,
+                  float *logits_out, int32_t *ids_out, float *w_out, Path path, char *ws,
+                  const Layout &L, Launches &run) {
   const hipStream_t s = run.s;
   const float *Wr32 = static_cast<const float *>(Wr);  // meaningful without router_bf16
   if constexpr (sizeof(WT) == 2) {
@@ -306,7 +314,8 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   const WT *Sg = static_cast<const WT *>(sh.Sg), *Su = static_cast<const WT *>(sh.Su),
            *Sd = static_cast<const WT *>(sh.Sd);
   const int m = shared_pieces(I, sh.Is);
-  if (T == 1 && (!Sg || m > 0) && moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2, m)) {
+  if (T == 1 && !ck.dn && (!Sg || m > 0) &&
+      moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2, m)) {
     RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
                                                    k1, k2, Sg, Su, Sd, sh.Is, sh.sgw, y,
                                                    logits_out, ids_out, w_out, sync,
@@ -348,6 +357,9 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   }
   RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s,
                                             Sg, Su, sh.Is, plan_s, gs, abuf_s)));
+  if (ck.dn)
+    RUN("channel_select", moe::launch_channel_select(abuf, T, k1, I, ids, ck.dn, ck.keep,
+                                                     ck.scores_out, ck.kept_out, s));
   const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
   if (T == 1 && ncd <= 2 && !Sg) {
     RUN("down_one_token", (moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)));
@@ -365,8 +377,9 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
 int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
                  const float *br, int32_t E, const void *Wgate, const void *Wup,
                  const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2,
-                 const Shared &sh, void *y, float *logits_out, int32_t *ids_out, float *w_out,
-                 uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+                 const Shared &sh, const ChannelTopk &ck, void *y, float *logits_out,
+                 int32_t *ids_out, float *w_out, uint32_t flags, void *workspace,
+                 size_t workspace_bytes, void *stream) {
   int rc = check_route_args(T, E, k1, k2);
   if (rc != MOE_OK) return rc;
   if (H < 8 || H % 8 != 0) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 8", H);
@@ -393,6 +406,14 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
     return fail(MOE_ENOTSUP, "the fused path has no bf16 router");
   if (sh.Sg && (flags & MOE_FLAG_FORCE_FUSED))
     return fail(MOE_ENOTSUP, "the fused path has no shared expert");
+  if (ck.dn) {
+    if (!moe::channel_select_supported(k1, I))
+      return fail(MOE_ENOTSUP, "channel top-k takes k1*I <= 8192 (got %lld)", (long long)k1 * I);
+    if (ck.keep < 0 || (int64_t)ck.keep > (int64_t)k1 * I)
+      return fail(MOE_EINVAL, "keep=%d out of [0, k1*I=%lld]", ck.keep, (long long)k1 * I);
+    if (flags & (MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_PREFILL))
+      return fail(MOE_ENOTSUP, "channel top-k runs on the grouped path only");
+  }
   if (T == 0) return MOE_OK;
   if (!x || !Wr || !Wgate || !Wup || !Wdown || !y) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wgate, 16) || !aligned(Wup, 16) ||
@@ -402,26 +423,31 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
     return fail(MOE_EALIGN, "Sgate, Sup and Sdown need 16-byte alignment");
   if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
       (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)) ||
-      (sh.sgw && !aligned(sh.sgw, 4)))
-    return fail(MOE_EALIGN, "br, sgate and the route outputs need 4-byte alignment");
+      (sh.sgw && !aligned(sh.sgw, 4)) || (ck.dn && !aligned(ck.dn, 4)) ||
+      (ck.scores_out && !aligned(ck.scores_out, 4)))
+    return fail(MOE_EALIGN, "br, sgate, dnorm and the route outputs need 4-byte alignment");
   const Layout L = layout(T, H, E, I, k1, sh.Is);
   const size_t need = workspace_bytes_for(T, H, E, I, k1, sh.Is);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                 need, workspace_bytes, workspace);
   Path path;
-  if ((rc = choose_path(T, H, E, I, k1, sh.Is, b16, flags, &path)) != MOE_OK) return rc;
+  if (ck.dn) {
+    path = Path::Grouped;
+  } else if ((rc = choose_path(T, H, E, I, k1, sh.Is, b16, flags, &path)) != MOE_OK) {
+    return rc;
+  }
   Launches run((hipStream_t)stream);
   char *ws = static_cast<char *>(workspace);
   if (f32)
     return forward_typed<float, float>(
         static_cast<const float *>(x), T, H, Wr, false, br, E, static_cast<const float *>(Wgate),
-        static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2, sh,
+        static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2, sh, ck,
         static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
   return forward_typed<moe::bf16_t, moe::bf16_t>(
       static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
       static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
-      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, sh, static_cast<moe::bf16_t *>(y),
+      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, sh, ck, static_cast<moe::bf16_t *>(y),
       logits_out, ids_out, w_out, path, ws, L, run);
 }
 
@@ -480,7 +506,7 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H, const vo
                 float *logits_out, int32_t *ids_out, float *w_out, uint32_t flags,
                 void *workspace, size_t workspace_bytes, void *stream) {
   return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
-                      Shared{}, y, logits_out, ids_out, w_out, flags, workspace,
+                      Shared{}, ChannelTopk{}, y, logits_out, ids_out, w_out, flags, workspace,
                       workspace_bytes, stream);
 }
 
@@ -499,7 +525,44 @@ int moe_forward_shared(const void *x, int32_t act_dtype, int64_t T, int32_t H, c
   sh.Is = Is;
   sh.sgw = sgate;
   return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2, sh,
-                      y, logits_out, ids_out, w_out, flags, workspace, workspace_bytes, stream);
+                      ChannelTopk{}, y, logits_out, ids_out, w_out, flags, workspace,
+                      workspace_bytes, stream);
+}
+
+int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E, int32_t H, int32_t I,
+                          float *dnorm, void *stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || H < 1 || I < 1 || (int64_t)H * I > (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "E=%d H=%d I=%d out of range", E, H, I);
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16)
+    return fail(MOE_ENOTSUP, "weight dtype %d not supported", w_dtype);
+  if (!Wdown || !dnorm) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned(Wdown, 16) || !aligned(dnorm, 4))
+    return fail(MOE_EALIGN, "Wdown needs 16-byte and dnorm 4-byte alignment");
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e =
+      w_dtype == MOE_F32
+          ? moe::launch_down_column_norms(static_cast<const float *>(Wdown), E, H, I, dnorm, s)
+          : moe::launch_down_column_norms(static_cast<const moe::bf16_t *>(Wdown), E, H, I,
+                                          dnorm, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "down column norms");
+}
+
+int moe_forward_channel_topk(const void *x, int32_t act_dtype, int64_t T, int32_t H,
+                             const void *Wr, const float *br, int32_t E, const void *Wgate,
+                             const void *Wup, const void *Wdown, int32_t w_dtype, int32_t I,
+                             int32_t k1, int32_t k2, const float *dnorm, int32_t keep, void *y,
+                             float *logits_out, int32_t *ids_out, float *w_out,
+                             float *scores_out, uint8_t *kept_out, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dnorm) return fail(MOE_EINVAL, "NULL dnorm");
+  ChannelTopk ck;
+  ck.dn = dnorm;
+  ck.keep = keep;
+  ck.scores_out = scores_out;
+  ck.kept_out = kept_out;
+  return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
+                      Shared{}, ck, y, logits_out, ids_out, w_out, flags, workspace,
+                      workspace_bytes, stream);
 }
 
 int moe_profile_launch(int32_t launch, void *start, void *stop) {

@@ -206,6 +206,55 @@ size_t moe_forward_shared_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
                                     int32_t w_dtype);
 
 /*
+ * moe_down_column_norms -- dnorm[e, c] = ||Wdown[e, :, c]||_2, the norm of
+ * each channel's down column ("Channel Selection for Mixture-of-Experts
+ * Decoding Needs No Calibration Data", section 5.2 scales channel scores by
+ * it), accumulated in fp32.  Computed once per weight set; an input of
+ * moe_forward_channel_topk.
+ *
+ *   Wdown  [E, H, I] w_dtype (MOE_F32 or MOE_BF16)               16-byte aligned
+ *   dnorm  [E, I] fp32 out                                         4-byte aligned
+ */
+int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
+                          int32_t H, int32_t I, float *dnorm, void *stream);
+
+/*
+ * moe_forward_channel_topk -- moe_forward with channel selection inside the
+ * activated experts ("Channel Selection ...", section 5.2; section 2: a
+ * channel owns one gate row, one up row and one down column).  After the
+ * route and the gate/up projections, each channel (r, c) of a token's k1
+ * activated experts is scored
+ *
+ *   score = w_r * dnorm[e_r, c] * |silu(g) * u|     (output units),
+ *
+ * the `keep` highest scores over the token's k1*I channels are kept (exact
+ * top-k; equal scores keep the lower flat index j = r*I + c), and
+ *
+ *   y[t] = sum over the kept channels of w_r * a[r, c] * Wdown[e_r, :, c].
+ *
+ * keep = k1*I is the full layer (up to rounding), keep = 0 gives y = 0.
+ * Arguments as moe_forward, plus:
+ *   dnorm      [E, I] fp32 from moe_down_column_norms           4-byte aligned
+ *   keep       0 <= keep <= k1*I; k1*I <= 8192 (MOE_ENOTSUP beyond)
+ *   scores_out [T, k1*I] fp32, or NULL: the scores the selection used
+ *   kept_out   [T, k1*I] uint8, or NULL: 1 for a kept channel, else 0
+ * It runs on the grouped path: MOE_FLAG_FORCE_FUSED and
+ * MOE_FLAG_FORCE_PREFILL return MOE_ENOTSUP; MOE_FLAG_ROUTER_BF16 applies.
+ * The workspace is moe_forward_workspace's.  The down projection still
+ * reads whole down rows (the [E, H, I] layout puts a column's elements 2*I
+ * bytes apart), so the selection changes y, not the bytes read.
+ */
+int moe_forward_channel_topk(const void *x, int32_t act_dtype, int64_t T,
+                             int32_t H, const void *Wr, const float *br,
+                             int32_t E, const void *Wgate, const void *Wup,
+                             const void *Wdown, int32_t w_dtype, int32_t I,
+                             int32_t k1, int32_t k2, const float *dnorm,
+                             int32_t keep, void *y, float *logits_out,
+                             int32_t *ids_out, float *w_out, float *scores_out,
+                             uint8_t *kept_out, uint32_t flags, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * moe_profile_launch -- profiling aid; changes no output.  Arms the NEXT
  * moe_forward call on the calling thread: it records the hipEvent_t `start`
  * on its stream immediately before its kernel launch number `launch` (0 =

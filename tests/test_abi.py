@@ -147,3 +147,28 @@ def test_forward_shared_workspace_size():
 def test_forward_shared_zero_tokens_is_a_no_op():
     lib = moe.load_library()
     assert _fwd_shared(lib, T=0, x=None, y=None, ws=None, wsb=0) == 0
+
+
+def test_channel_topk_argument_checks():
+    lib = moe.load_library()
+    v = ctypes.c_void_p
+    # down column norms: E out of range, misaligned Wdown, unsupported dtype
+    assert lib.moe_down_column_norms(v(16), 1, 0, 2048, 768, v(16), None) == 1
+    assert lib.moe_down_column_norms(v(8), 1, 128, 2048, 768, v(16), None) == 2
+    assert lib.moe_down_column_norms(v(16), 7, 128, 2048, 768, v(16), None) == 4
+
+    def fwd(**kw):
+        a = dict(k1=4, keep=100, dn=16, flags=0)
+        a.update(kw)
+        return lib.moe_forward_channel_topk(v(16), 1, 1, 2048, v(16), None, 128, v(16), v(16),
+                                            v(16), 1, 768, a["k1"], 16,
+                                            None if a["dn"] is None else v(a["dn"]), a["keep"],
+                                            v(16), None, None, None, None, None, a["flags"],
+                                            v(256), 1 << 30, None)
+    assert fwd(dn=None) == 1
+    assert fwd(keep=-1) == 1
+    assert fwd(keep=4 * 768 + 1) == 1
+    assert fwd(k1=11, keep=10) == 4          # k1*I > 8192
+    assert fwd(flags=4) == 4                 # prefill path
+    assert fwd(flags=1) == 4                 # fused path
+    assert fwd(dn=2) == 2                    # misaligned dnorm
