@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
 RING = 32
 PATH_FLAGS = {"auto": 0, "f": 1, "g": 2, "p": 4}
+TOPK_FRAC = 0.18  # channel top-k cells keep this share of a token's k1*I channels
 DEFAULT_CELLS = ",".join([
     "C2:1:4:16", "C2:1:8:8", "C2:1:4:4", "C2:1:4:128", "C2:1:3:16", "C2:1:2:16",
     "C3:8:4:16", "C3:8:8:8", "C3:8:4:4", "C3:8:4:128", "C3:8:3:16", "C3:8:2:16",
@@ -46,6 +47,8 @@ DEFAULT_CELLS = ",".join([
     "C2h:1:4:16", "C2h:1:8:8", "C3h:8:4:16", "C3h:8:8:8", "C4h:4096:4:16", "C4h:4096:8:8",
     # plus a gated shared expert of I channels, same layers
     "C2s:1:4:16", "C2s:1:8:8", "C3s:8:4:16", "C3s:8:8:8", "C4s:4096:4:16", "C4s:4096:8:8",
+    # channel top-k: 18% of each token's k1*I channels kept, same layers
+    "C2k:1:4:16", "C2k:1:8:8", "C3k:8:4:16", "C3k:8:8:8",
 ])
 
 
@@ -60,7 +63,8 @@ def parse():
     ap.add_argument("--cells", default=DEFAULT_CELLS,
                     help="CONFIG:T:k1:k2[:path] list; the first is the headline; a "
                          "CONFIG ending in h runs that config's layers with the bf16 router, "
-                         "one ending in s adds a gated shared expert of I channels")
+                         "one ending in s adds a gated shared expert of I channels, one "
+                         "ending in k keeps the top 18%% of each token's channels")
     return ap.parse_args()
 
 
@@ -94,6 +98,12 @@ def make_sets(synth, torch, names, ring):
             sets[n] = (cfg, [dict(lay, shared=synth.make_shared(cfg, cfg.I, gate=True, layer=i,
                                                                 device="cuda"))
                              for i, lay in enumerate(layers)])
+        elif n.endswith("k"):
+            import decoupled_top_routing_amd as moe
+            cfg, layers = sets[n[:2]]
+            sets[n] = (cfg, [dict(lay, topk={"dn": moe.down_column_norms(lay["Wd"]),
+                                             "frac": TOPK_FRAC})
+                             for lay in layers])
     torch.cuda.synchronize()
     print(f"# generated {sorted(names)} on the device in {time.perf_counter() - t0:.1f} s",
           file=sys.stderr, flush=True)
@@ -152,6 +162,20 @@ def kernel_work(name, cfg, T, k1, U, bias, wr_elt=4, shared=0):
     return table.get(name, (None, None))
 
 
+def layer_call(moe, lay, x, k1, k2, cfg, **kw):
+    """One moe call on a layer dict: channel top-k layers go through
+    forward_channel_topk, the others through forward (with their shared expert)."""
+    ck = lay.get("topk")
+    if ck:
+        keep = int(round(ck["frac"] * k1 * cfg.I))
+        rr = kw.pop("return_route", False)
+        r = moe.forward_channel_topk(x, lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
+                                     ck["dn"], keep, br=lay["br"], return_route=rr, **kw)
+        return r[:4] if rr else r
+    return moe.forward(x, lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2, br=lay["br"],
+                       shared=shared_args(lay), **kw)
+
+
 def shared_args(lay):
     """moe.forward's shared argument for a layer dict (None without one)."""
     sh = lay.get("shared")
@@ -177,10 +201,8 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
 
     def one_pass(record_ids=False):
         for i, lay in enumerate(layers):
-            r = moe.forward(xs[i], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
-                            br=lay["br"], out=ys[i], workspace=ws,
-                            return_route=record_ids, flags=PATH_FLAGS[path],
-                            shared=shared_args(lay))
+            r = layer_call(moe, lay, xs[i], k1, k2, cfg, out=ys[i], workspace=ws,
+                           return_route=record_ids, flags=PATH_FLAGS[path])
             if record_ids:
                 ids_list.append(r[2].cpu().numpy())
 
@@ -261,9 +283,8 @@ def profile_launches(moe, torch, cfg, layers, T, k1, k2, path, n_calls):
     def call(i):
         j = i % len(layers)
         lay = layers[j]
-        moe.forward(xs[j], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
-                    br=lay["br"], out=ys[j], workspace=ws, flags=PATH_FLAGS[path],
-                    shared=shared_args(lay))
+        layer_call(moe, lay, xs[j], k1, k2, cfg, out=ys[j], workspace=ws,
+                   flags=PATH_FLAGS[path])
 
     launches = []
     with torch.cuda.stream(stream):
@@ -304,9 +325,16 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
     tolerance on a token sample (host copies of the activated experts only)."""
     import numpy as np
     x = layer["x"][:T]
-    y, lg, ids, w = moe.forward(x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1, k2,
-                                br=layer["br"], return_route=True, flags=PATH_FLAGS[path],
-                                shared=shared_args(layer))
+    ck = layer.get("topk")
+    if ck:
+        keep = int(round(ck["frac"] * k1 * layer["Wg"].shape[1]))
+        y, lg, ids, w, sc, kept = moe.forward_channel_topk(
+            x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1, k2, ck["dn"], keep,
+            br=layer["br"], return_route=True, flags=PATH_FLAGS[path])
+    else:
+        y, lg, ids, w = moe.forward(x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1,
+                                    k2, br=layer["br"], return_route=True,
+                                    flags=PATH_FLAGS[path], shared=shared_args(layer))
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_dev.view(torch.int16)), "timed output differs"
     lg_h = lg.cpu().numpy()
@@ -321,7 +349,13 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
     n = synth.to_numpy
     Wg, Wu, Wd = (n(layer[k].index_select(0, idx)) for k in ("Wg", "Wu", "Wd"))
     rids = np.searchsorted(uniq, sids).astype(np.int32)
-    y_ref = oracle.experts(n(x)[sel], Wg, Wu, Wd, rids, ow[sel], nthreads=8)
+    if ck:
+        # the kept set equals the oracle's selection on the GPU's own scores
+        sc_h, kept_h = sc.cpu().numpy(), kept.cpu().numpy()
+        assert np.array_equal(oracle.channel_select(sc_h, keep), kept_h), "selection differs"
+        y_ref = oracle.experts_kept(n(x)[sel], Wg, Wu, Wd, rids, ow[sel], kept_h[sel])
+    else:
+        y_ref = oracle.experts(n(x)[sel], Wg, Wu, Wd, rids, ow[sel], nthreads=8)
     if layer.get("shared"):
         sh = {k: n(v) for k, v in layer["shared"].items()}
         y_ref = y_ref.astype(np.float64) + oracle.shared(n(x)[sel], sh["Sg"], sh["Su"], sh["Sd"],
@@ -471,10 +505,12 @@ def main():
     ratios = {}
     for cfgname, T in (("C2", 1), ("C3", 2), ("C3", 4), ("C3", 8), ("C3", 16), ("C3", 32),
                        ("C3", 64), ("C3", 128), ("C3", 256), ("C2h", 1), ("C3h", 8),
-                       ("C4", 4096), ("C4h", 4096), ("C2s", 1), ("C3s", 8), ("C4s", 4096)):
+                       ("C4", 4096), ("C4h", 4096), ("C2s", 1), ("C3s", 8), ("C4s", 4096),
+                       ("C2k", 1), ("C3k", 8)):
         a, b = find(cfgname, T, 4, 16), find(cfgname, T, 8, 8)
         if a and b:
-            tag = {"h": "_bf16_router", "s": "_shared_expert"}.get(cfgname[2:], "")
+            tag = {"h": "_bf16_router", "s": "_shared_expert",
+                   "k": "_channel_topk"}.get(cfgname[2:], "")
             ratios[f"b{T}_4:16_over_8:8{tag}"] = b["us_per_layer"] / a["us_per_layer"]
 
     us = head["us_per_layer"]

@@ -255,12 +255,14 @@ def down_column_norms(Wdown):
 
 
 def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep: int,
-                         br=None, return_route: bool = False, flags: int = 0):
+                         br=None, return_route: bool = False, flags: int = 0, out=None,
+                         workspace=None):
     """The layer with channel top-k inside the activated experts: of each
     token's k1*I channels only the ``keep`` highest-scoring (router weight x
     down-column norm x |activation|) are summed.  ``dnorm`` comes from
     ``down_column_norms``.  Returns y, or (y, logits, ids, w, scores, kept)
-    with ``return_route=True`` (scores [T, k1*I] fp32, kept [T, k1*I] bool)."""
+    with ``return_route=True`` (scores [T, k1*I] fp32, kept [T, k1*I] bool).
+    ``out`` and ``workspace`` as for ``forward``."""
     lib = load_library()
     _need_cuda("x", x)
     act = _dtype_code(x)
@@ -278,7 +280,7 @@ def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep
             or tuple(Wr.shape) != (E, H) or tuple(dnorm.shape) != (E, I):
         raise MoeError(1, "shape mismatch between x, Wr, Wgate, Wup, Wdown and dnorm")
     dev = x.device
-    y = torch.empty((T, H), dtype=x.dtype, device=dev)
+    y = out if out is not None else torch.empty((T, H), dtype=x.dtype, device=dev)
     lg = ids = w = sc = kept = None
     if return_route:
         lg = torch.empty((T, E), dtype=torch.float32, device=dev)
@@ -290,7 +292,11 @@ def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep
     if nbytes == 0 and T > 0:
         raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
     stream = _stream(dev)
-    ws = _workspace(dev, stream.value or 0, nbytes)
+    if workspace is not None:
+        _need_cuda("workspace", workspace, torch.uint8)
+        ws = workspace
+    else:
+        ws = _workspace(dev, stream.value or 0, nbytes)
     _check(lib.moe_forward_channel_topk(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
                                         _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(dnorm), keep,
                                         _ptr(y), _ptr(lg), _ptr(ids), _ptr(w), _ptr(sc),

@@ -423,9 +423,11 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
     return fail(MOE_EALIGN, "Sgate, Sup and Sdown need 16-byte alignment");
   if ((br && !aligned(br, 4)) || (logits_out && !aligned(logits_out, 4)) ||
       (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)) ||
-      (sh.sgw && !aligned(sh.sgw, 4)) || (ck.dn && !aligned(ck.dn, 4)) ||
-      (ck.scores_out && !aligned(ck.scores_out, 4)))
-    return fail(MOE_EALIGN, "br, sgate, dnorm and the route outputs need 4-byte alignment");
+      (sh.sgw && !aligned(sh.sgw, 4)))
+    return fail(MOE_EALIGN, "br, sgate and the route outputs need 4-byte alignment");
+  if ((ck.dn && !aligned(ck.dn, 16)) || (ck.scores_out && !aligned(ck.scores_out, 16)) ||
+      (ck.kept_out && !aligned(ck.kept_out, 8)))
+    return fail(MOE_EALIGN, "dnorm and scores_out need 16-byte, kept_out 8-byte alignment");
   const Layout L = layout(T, H, E, I, k1, sh.Is);
   const size_t need = workspace_bytes_for(T, H, E, I, k1, sh.Is);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)

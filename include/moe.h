@@ -214,6 +214,7 @@ size_t moe_forward_shared_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *
  *   Wdown  [E, H, I] w_dtype (MOE_F32 or MOE_BF16)               16-byte aligned
  *   dnorm  [E, I] fp32 out                                         4-byte aligned
+ *          (moe_forward_channel_topk reads it with 16-byte alignment)
  */
 int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
                           int32_t H, int32_t I, float *dnorm, void *stream);
@@ -234,10 +235,12 @@ int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
  *
  * keep = k1*I is the full layer (up to rounding), keep = 0 gives y = 0.
  * Arguments as moe_forward, plus:
- *   dnorm      [E, I] fp32 from moe_down_column_norms           4-byte aligned
+ *   dnorm      [E, I] fp32 from moe_down_column_norms          16-byte aligned
  *   keep       0 <= keep <= k1*I; k1*I <= 8192 (MOE_ENOTSUP beyond)
  *   scores_out [T, k1*I] fp32, or NULL: the scores the selection used
+ *                                                              16-byte aligned
  *   kept_out   [T, k1*I] uint8, or NULL: 1 for a kept channel, else 0
+ *                                                               8-byte aligned
  * It runs on the grouped path: MOE_FLAG_FORCE_FUSED and
  * MOE_FLAG_FORCE_PREFILL return MOE_ENOTSUP; MOE_FLAG_ROUTER_BF16 applies.
  * The workspace is moe_forward_workspace's.  The down projection still

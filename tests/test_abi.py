@@ -172,3 +172,4 @@ def test_channel_topk_argument_checks():
     assert fwd(flags=4) == 4                 # prefill path
     assert fwd(flags=1) == 4                 # fused path
     assert fwd(dn=2) == 2                    # misaligned dnorm
+    assert fwd(dn=20) == 2                   # dnorm needs 16-byte alignment
