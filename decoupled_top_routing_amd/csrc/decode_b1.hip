@@ -212,7 +212,8 @@ __device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, fl
 // One output row per wave: y[h] = sum over the activated experts, ascending,
 // of Wd[e_u, h, :] . a[u, :].
 template <typename WT, typename XT, int NCD>
-__device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int d) {
+__device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, uint32_t tag,
+                          int d) {
   constexpr int NW = Elem<WT>::kPer16B;
   constexpr int AB = kABytes<WT>;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
@@ -233,7 +234,96 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t tag, int 
   const int nch = a.I / NW;
   const int U = a.k1 + a.m;
   float acc = 0.0f;
-  for (int ub = 0; ub < U; ub += kPF) {
+  // Wd[e_s, h, :] . a[s, :] from the staged activations of slot s (one lane's share)
+  auto dot_slot = [&](const uint4 (&dqs)[NCD], int s, float v) {
+    const char *sa = reinterpret_cast<const char *>(L.a);
+#pragma unroll
+    for (int j = 0; j < NCD; ++j) {
+      const int ch = j * kWave + lane;
+      if (ch < nch) {
+        if constexpr (sizeof(WT) == 2) {
+          const uint4 aq = *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB);
+          v = dot2_bf16(dqs[j].x, aq.x, v);
+          v = dot2_bf16(dqs[j].y, aq.y, v);
+          v = dot2_bf16(dqs[j].z, aq.z, v);
+          v = dot2_bf16(dqs[j].w, aq.w, v);
+        } else {
+          float dv[NW], av[NW];
+          Elem<WT>::widen(dqs[j], dv);
+          Elem<float>::widen(
+              *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB), av);
+#pragma unroll
+          for (int k = 0; k < NW; ++k) v = __builtin_fmaf(dv[k], av[k], v);
+        }
+      }
+    }
+    return v;
+  };
+  if (U <= kPF) {
+    // One round: each expert (or shared piece) is staged and multiplied as
+    // soon as it completes, so only the last one to complete is left when it
+    // does.  Per-slot partial sums are added in slot order at the end, so y
+    // does not depend on the order of completion.
+    uint4 dq[kPF][NCD];
+#pragma unroll
+    for (int s = 0; s < kPF; ++s) {
+      if (s < U) {
+        const WT *drow = s < a.k1 ? Wd + ((int64_t)s_uniq[s] * a.H + h) * a.I
+                                  : Sd + (int64_t)h * a.Is + (int64_t)s_uniq[s] * a.I;
+#pragma unroll
+        for (int j = 0; j < NCD; ++j) {
+          const int ch = j * kWave + lane;
+          dq[s][j] = ch < nch ? ld16_stream(drow + ch * NW) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    float part[kPF];
+#pragma unroll
+    for (int s = 0; s < kPF; ++s) part[s] = 0.0f;
+    const uint64_t *cw = a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1;
+    const uint32_t all = (1u << U) - 1u;
+    const int row8 = a.I * AB / 8;  // 8-byte words of one slot's activations
+    uint32_t done = 0u;
+    while (done != all) {
+      if (wv == 0) {
+        // wait until at least one more of the slots not yet done is complete
+        const bool open = lane < U && !((done >> lane) & 1u);
+        uint64_t ready = 0;
+        uint32_t spins = 0;
+        while (true) {
+          const uint64_t w = open ? coh_ld(cw + lane) : 0ull;
+          ready = __ballot(open && (uint32_t)(w >> 32) == tag);
+          if (ready) break;
+          if (++spins > kSpinLimit) {
+            if (lane == 0) coh_st(err, 1);
+            ready = all & ~done;  // give up waiting; the call reports an error
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+        if (lane == 0) *s_new = (uint32_t)ready;
+      }
+      __syncthreads();
+      const uint32_t nw = *s_new;
+      // stage the newly complete slots' activations (device-coherent loads)
+      for (uint32_t m = nw; m; m &= m - 1) {
+        const int s = __builtin_ctz(m);
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(
+            static_cast<const char *>(a.abuf) + (int64_t)s * a.I * AB);
+        for (int i = tid; i < row8; i += kThreads) L.a[s * row8 + i] = coh_ld(src + i);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kPF; ++s)
+        if ((nw >> s) & 1u) part[s] = dot_slot(dq[s], s, part[s]);
+      done |= nw;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int s = 0; s < kPF; ++s)
+      if (s < U) acc = acc + part[s];
+  }
+  for (int ub = 0; U > kPF && ub < U; ub += kPF) {
     const int nu = min(kPF, U - ub);
     uint4 dq[kPF][NCD];
 #pragma unroll
@@ -300,6 +390,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
   __shared__ int s_e, s_last;
   __shared__ float s_wt;
   __shared__ float s_red[kWaves];
+  __shared__ uint32_t s_new;
   const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const uint32_t tag_epoch = (uint32_t)coh_ld(a.sync + kEpochWord);
   const uint32_t tag = call_tag(tag_epoch);
@@ -469,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     }
     return;
   }
-  down_rows<WT, XT, NCD>(a, L, s_uniq, tag, b - a.n_r - 1 - a.n_gu);
+  down_rows<WT, XT, NCD>(a, L, s_uniq, &s_new, tag, b - a.n_r - 1 - a.n_gu);
 }
 
 }  // namespace b1
