@@ -144,7 +144,7 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
   return MOE_OK;
 }
 
-enum class Path { Fused, Grouped, Prefill };
+enum class Path { Single, Fused, Grouped, Prefill };
 
 // The expert projections run as MFMA GEMMs from kPrefillMinAssign
 // assignments (T * k1) on, when the experts get two rows each on average;
@@ -313,9 +313,7 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   int32_t *ticket = sync + moe::kRouteTicketWord;
   const WT *Sg = static_cast<const WT *>(sh.Sg), *Su = static_cast<const WT *>(sh.Su),
            *Sd = static_cast<const WT *>(sh.Sd);
-  const int m = shared_pieces(I, sh.Is);
-  if (T == 1 && !ck.dn && (!Sg || m > 0) &&
-      moe::decode_b1_supported(H, I, k1, sizeof(WT) == 2, m)) {
+  if (path == Path::Single) {
     RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
                                                    k1, k2, Sg, Su, Sd, sh.Is, sh.sgw, y,
                                                    logits_out, ids_out, w_out, sync,
@@ -439,6 +437,11 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
   } else if ((rc = choose_path(T, H, E, I, k1, sh.Is, b16, flags, &path)) != MOE_OK) {
     return rc;
   }
+  // one token takes the one-launch kernel unless a path is forced
+  const int m = shared_pieces(I, sh.Is);
+  if (path == Path::Grouped && !(flags & MOE_FLAG_FORCE_GROUPED) && T == 1 && !ck.dn &&
+      (!sh.Sg || m > 0) && moe::decode_b1_supported(H, I, k1, b16, m))
+    path = Path::Single;
   Launches run((hipStream_t)stream);
   char *ws = static_cast<char *>(workspace);
   if (f32)

@@ -67,8 +67,11 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* moe_forward flags: force one of the execution paths (0 = choose by batch
- * size and shape).  All paths compute the same layer; they differ in kernels:
- *   FUSED   one launch per layer (router, route, experts), batches <= 8 tokens;
+ * size and shape: one token runs as a single launch whose workgroups hand the
+ * route and the activations over through the workspace; decode batches take
+ * GROUPED, large batches PREFILL).  All paths compute the same layer; they
+ * differ in kernels:
+ *   FUSED   an older single launch per layer, batches <= 8 tokens;
  *   GROUPED router, route, per-expert plan, gate/up, down and combine kernels
  *           (grouped GEMVs that read each activated expert once);
  *   PREFILL the same steps with the expert projections as bf16 MFMA grouped
