@@ -135,3 +135,26 @@ def test_edge_shapes_fp32(E, k1, k2, H, I, T):
     cfg = replace(synth.TINY, name=f"edge-E{E}", T=T, H=H, E=E, I=I)
     L = synth.make_layer(cfg)
     run_and_check(cfg, L, host_layer(L), k1, k2)
+
+
+@pytest.mark.parametrize("E,k1,k2,H,I,dtype", [
+    (1, 1, 1, 256, 64, "f32"),        # one expert: p = 1, w = 1
+    (1024, 2, 7, 256, 64, "f32"),     # the most experts: the route block's one-wave route
+    (300, 32, 64, 256, 64, "f32"),    # the most slots (k1 = 32): down rounds of 8
+    (33, 5, 9, 512, 72, "f32"),       # E and I not multiples of the tiles
+    (1024, 4, 16, 512, 64, "bf16"),   # bf16, the most experts
+    (128, 8, 8, 2048, 768, "bf16"),   # a full-size expert at 8:8
+])
+def test_one_launch_limits(E, k1, k2, H, I, dtype):
+    """One token on the single-launch kernel at the edges of the shapes it takes."""
+    from dataclasses import replace
+    cfg = replace(synth.TINY, name=f"b1-E{E}-k{k1}", T=1, H=H, E=E, I=I, dtype=dtype,
+                  rms_norm_x=dtype == "bf16", router_var_times_H=4.0 if dtype == "bf16" else 1.0)
+    L = synth.make_layer(cfg)
+    g = to_dev(L)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    moe.profile_launch(0, ev[0], ev[1])
+    moe.forward(g["x"], g["Wr"], g["Wg"], g["Wu"], g["Wd"], k1, k2)
+    torch.cuda.synchronize()
+    assert moe.profile_launch_name() == "b1_layer"
+    run_and_check(cfg, g, host_layer(L), k1, k2)
