@@ -243,6 +243,53 @@ struct BlockRoute {
   float M;
 };
 
+// Rank counting over keys in LDS (16-byte aligned, read at the same address
+// by every lane, so each read is a broadcast).  With kBatch16 the reads go in
+// batches of 16 keys issued together, one LDS round trip per batch instead
+// of one per 8 keys; each batch keeps 16 compare masks live in scalar
+// registers, so it is used only where the kernel has them to spare (a spill
+// to scratch on this path costs more than the batching saves).
+__device__ __forceinline__ void load16(const uint64_t *K, ulonglong2 (&q)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = *reinterpret_cast<const ulonglong2 *>(K + 2 * i);
+}
+__device__ __forceinline__ int above16(const ulonglong2 (&q)[8], uint64_t Ke) {
+  int c0 = 0, c1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    c0 += (q[i].x > Ke) + (q[i].y > Ke);
+    c1 += (q[i + 1].x > Ke) + (q[i + 1].y > Ke);
+  }
+  return c0 + c1;
+}
+// How many of the n keys at K exceed Ke (n a multiple of 8, or 16 with
+// kBatch16).
+template <bool kBatch16>
+__device__ __forceinline__ int count_above(const uint64_t *K, int n, uint64_t Ke) {
+  int c = 0;
+  if constexpr (kBatch16) {
+#pragma unroll 1
+    for (int j = 0; j < n; j += 16) {
+      ulonglong2 q[8];
+      load16(K + j, q);
+      c += above16(q, Ke);
+    }
+  } else {
+    int c1 = 0;
+    for (int j = 0; j < n; j += 8) {
+      const ulonglong2 q0 = *reinterpret_cast<const ulonglong2 *>(K + j);
+      const ulonglong2 q1 = *reinterpret_cast<const ulonglong2 *>(K + j + 2);
+      const ulonglong2 q2 = *reinterpret_cast<const ulonglong2 *>(K + j + 4);
+      const ulonglong2 q3 = *reinterpret_cast<const ulonglong2 *>(K + j + 6);
+      c += (q0.x > Ke) + (q0.y > Ke) + (q1.x > Ke) + (q1.y > Ke);
+      c1 += (q2.x > Ke) + (q2.y > Ke) + (q3.x > Ke) + (q3.y > Ke);
+    }
+    c += c1;
+  }
+  return c;
+}
+
+template <bool kBatch16 = false>
 __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
                                   int32_t *ids_out, float *w_out, BlockRoute &S,
                                   bool wbf16 = false) {
@@ -272,27 +319,20 @@ __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t
   }
   // element e is ranked by `split` threads, each over `chunk` keys of the
   // padded key array (keys past E are below every valid key, so they never
-  // count); 8 keys per step, all loads of a step in flight together
+  // count)
   const int split = min(kBlockThreads / epow, epow);
   const int e = tid & (epow - 1), part = tid >> lg;
   const int chunk = epow / split;
   if (e < E && part < split) {
     const uint64_t Ke = S.K[e];
-    const int j0 = part * chunk;
-    int c0 = 0, c1 = 0;
-    if (chunk >= 8) {
-      for (int j = j0; j < j0 + chunk; j += 8) {
-        const ulonglong2 q0 = *reinterpret_cast<const ulonglong2 *>(&S.K[j]);
-        const ulonglong2 q1 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 2]);
-        const ulonglong2 q2 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 4]);
-        const ulonglong2 q3 = *reinterpret_cast<const ulonglong2 *>(&S.K[j + 6]);
-        c0 += (q0.x > Ke) + (q0.y > Ke) + (q1.x > Ke) + (q1.y > Ke);
-        c1 += (q2.x > Ke) + (q2.y > Ke) + (q3.x > Ke) + (q3.y > Ke);
-      }
+    const uint64_t *Kp = S.K + part * chunk;
+    int cnt;
+    if (chunk >= 16) {
+      cnt = count_above<kBatch16>(Kp, chunk, Ke);
     } else {
-      for (int j = j0; j < j0 + chunk; ++j) c0 += S.K[j] > Ke ? 1 : 0;
+      cnt = 0;
+      for (int j = 0; j < chunk; ++j) cnt += Kp[j] > Ke ? 1 : 0;
     }
-    const int cnt = c0 + c1;
     if (cnt) atomicAdd(&S.rank[e], cnt);
   }
   __syncthreads();
@@ -387,12 +427,15 @@ __device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
 template <int V>
 __device__ void route_into_lds(const float *l, int E, int k1, int k2, int32_t *s_ids, float *s_w,
                                BlockRoute &S, bool wbf16 = false) {
-  if (E <= kBlockThreads && k1 <= kBlockThreads) {
-    route_token_block(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
-  } else {
-    if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, wbf16);
-    __syncthreads();
+  // V = 8 and 16 serve E > 256 only, so their kernels carry no block route
+  if constexpr (V * kWave <= kBlockThreads) {
+    if (E <= kBlockThreads && k1 <= kBlockThreads) {
+      route_token_block<(V <= 2)>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
+      return;
+    }
   }
+  if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, wbf16);
+  __syncthreads();
 }
 
 }  // namespace moe
