@@ -650,9 +650,20 @@ __global__ __launch_bounds__(256) void shared_prep_kernel(const XT *__restrict__
   const int lane = lane_id();
   float g = 1.0f;
   if (sgw) {
+    // x rows are 16-byte aligned (H % 8 == 0): one 16-byte chunk of x per
+    // step, several steps' loads in flight; sgate is only 4-byte aligned
+    constexpr int n = Elem<XT>::kPer16B;
     const XT *xr = x + t * H;
+    const int nc = H / n;
     float z = 0.0f;
-    for (int h = lane; h < H; h += kWave) z = __builtin_fmaf(Elem<XT>::load1(xr + h), sgw[h], z);
+#pragma unroll 4
+    for (int c = lane; c < nc; c += kWave) {
+      float xv[n];
+      Elem<XT>::widen(ld16(xr + (int64_t)c * n), xv);
+      const float *wp = sgw + (int64_t)c * n;
+#pragma unroll
+      for (int q = 0; q < n; ++q) z = __builtin_fmaf(xv[q], wp[q], z);
+    }
     z = wave_sum_dpp(z);
     g = 1.0f / (1.0f + __expf(-z));
   }
