@@ -134,12 +134,19 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r) {
 // Assignments of one expert appear in the order the atomic scatter gives;
 // each GEMM row is computed independently of its position, so y does not
 // depend on that order.
+constexpr int kPlanPer = 16;
+constexpr int kPlanStage = 32768;  // 128 KB of LDS
+
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__restrict__ ids,
                                                             int64_t n, int E,
                                                             int32_t *__restrict__ plan) {
   __shared__ int32_t cnt[kMaxExperts], uidx[kMaxExperts], fill[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t wsum[16][3];
+  // up to kPlanStage assignments are scattered in LDS and written out
+  // coalesced: scattered 4-byte global stores from one workgroup are slow
+  __shared__ int32_t s_list[kPlanStage];
+  const bool staged = n <= kPlanStage;
   int32_t *uniq = plan + 4;
   int32_t *off = uniq + E;
   int32_t *mt_off = off + E + 1;
@@ -150,7 +157,19 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
     fill[e] = 0;
   }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[ids[i]], 1);
+  // ids are read kPlanPer per thread at a time, all loads issued before the
+  // LDS atomics that consume them
+  for (int64_t b = 0; b < n; b += (int64_t)1024 * kPlanPer) {
+    int32_t ev[kPlanPer];
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      const int64_t i = b + (int64_t)q * 1024 + tid;
+      ev[q] = i < n ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q)
+      if (ev[q] >= 0) atomicAdd(&cnt[ev[q]], 1);
+  }
   __syncthreads();
   const int c = tid < E ? cnt[tid] : 0;
   int v[3] = {c > 0 ? 1 : 0, c, (c + GM - 1) / GM};
@@ -189,10 +208,28 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
     mt_off[U] = base[2] + inc[2];
   }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += 1024) {
-    const int e = ids[i];
-    const int pos = atomicAdd(&fill[e], 1);
-    list[s_off[uidx[e]] + pos] = (int32_t)i;
+  for (int64_t b = 0; b < n; b += (int64_t)1024 * kPlanPer) {
+    int32_t ev[kPlanPer];
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      const int64_t i = b + (int64_t)q * 1024 + tid;
+      ev[q] = i < n ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      if (ev[q] >= 0) {
+        const int pos = atomicAdd(&fill[ev[q]], 1);
+        const int32_t i = (int32_t)(b + (int64_t)q * 1024 + tid);
+        if (staged)
+          s_list[s_off[uidx[ev[q]]] + pos] = i;
+        else
+          list[s_off[uidx[ev[q]]] + pos] = i;
+      }
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < (int)n; i += 1024) list[i] = s_list[i];
   }
 }
 
