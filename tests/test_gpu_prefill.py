@@ -43,6 +43,14 @@ def test_prefill_against_grouped_shapes(prefill, T, flags):
                   flags=flags)
 
 
+def test_prefill_plan_beyond_lds_staging(prefill):
+    """4096 tokens at k1 = 9 are 36864 assignments, more than the 32768 the
+    plan kernel stages in LDS: its list is then scattered straight to global
+    memory (8:8 at 4096 tokens, exactly 32768, takes the staged branch)."""
+    L, Lh = prefill
+    run_and_check(synth.PREFILL, L, Lh, 9, 12, token_sample=token_sample(4096))
+
+
 def test_prefill_deterministic(prefill):
     """The plan's scatter order varies from call to call; the output may not."""
     L, _ = prefill
