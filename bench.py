@@ -10,18 +10,25 @@ replayed; HIP events on the capture stream time the replays.  The other cells
 (batch 1 and 8 at every k1:k2 pair, the 4096-token prefill, the E=512 layer
 at 1 and 64 tokens) are reported in "cells".
 
+The timed region of the headline is exactly --steps layer calls (whole ring
+replays, then one replay of a graph of the remaining calls); the spread is
+reported from at least 10 ring replays timed one by one.
+
 The roofline object is for the headline's dominant kernel: every launch of
 one call is bracketed with HIP events (moe_profile_launch) in an eager pass,
-the longest is the dominant one, and its events are then recorded around that
-launch in every call of a second timed eager pass over the ring.
+the longest is the dominant one; when a call is that one launch, the timed
+region gives its average duration.
 
-Prints one JSON line (see the repository's benchmark contract).
+The last line of stdout is one compact JSON object (the benchmark contract);
+every cell is printed to stderr as a JSON line and, with --cells-out, written
+to a file.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import os
 import sys
 import time
 from pathlib import Path
@@ -32,7 +39,7 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
 RING = 32
-PATH_FLAGS = {"auto": 0, "f": 1, "g": 2, "p": 4}
+PATH_FLAGS = {"auto": 0, "g": 2, "p": 4}
 TOPK_FRAC = 0.18  # channel top-k cells keep this share of a token's k1*I channels
 DEFAULT_CELLS = ",".join([
     "C2:1:4:16", "C2:1:8:8", "C2:1:4:4", "C2:1:4:128", "C2:1:3:16", "C2:1:2:16",
@@ -62,6 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=320)
     ap.add_argument("--ring", type=int, default=RING)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cells-out", default=None, help="write every cell as a JSON line here")
     ap.add_argument("--cells", default=DEFAULT_CELLS,
                     help="CONFIG:T:k1:k2[:path] list; the first is the headline; a "
                          "CONFIG ending in h runs that config's layers with the bf16 router, "
@@ -159,7 +167,6 @@ def kernel_work(name, cfg, T, k1, U, bias, wr_elt=4, shared=0):
         "gateup": (gu + T * H * elt, 4.0 * n * I * H),
         "down": (dn, 2.0 * n * I * H),
         "down_one_token": (dn + H * elt, 2.0 * n * I * H),
-        "fused_decode": (layer_bytes(cfg, T, U, bias, wr_elt), expert_flops(cfg, T, k1)),
         "router_mma": (router + T * E * 4, 2.0 * T * E * H),
         "gateup_mma": (gu + T * H * elt, 4.0 * n * I * H),
         "down_mma": (dn, 2.0 * n * I * H),
@@ -190,8 +197,10 @@ def shared_args(lay):
 
 
 # ------------------------------------------------------------------ timing
-def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
-    """Graph-capture one pass over the layers and time whole replays."""
+def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_replays=0):
+    """Graph-capture one pass over the layers; time exactly `steps` layer calls
+    (whole ring replays, then a graph of the first steps % ring calls), then
+    at least `min_replays` whole replays one by one for the spread."""
     dev = layers[0]["Wg"].device
     L = len(layers)
     stream = torch.cuda.Stream(device=dev)
@@ -204,13 +213,14 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
                      dtype=torch.uint8, device=dev)
     ids_list = []
 
-    def one_pass(record_ids=False):
-        for i, lay in enumerate(layers):
-            r = layer_call(moe, lay, xs[i], k1, k2, cfg, out=ys[i], workspace=ws,
+    def one_pass(n=L, record_ids=False):
+        for i in range(n):
+            r = layer_call(moe, layers[i], xs[i], k1, k2, cfg, out=ys[i], workspace=ws,
                            return_route=record_ids, flags=PATH_FLAGS[path])
             if record_ids:
                 ids_list.append(r[2].cpu().numpy())
 
+    n_full, rem = divmod(steps, L)
     with torch.cuda.stream(stream):
         one_pass(record_ids=True)           # eager, also collects the routes
         torch.cuda.synchronize()
@@ -218,23 +228,29 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             one_pass()
-        for _ in range(max(1, warmup // L)):
+        g_rem = None
+        if rem:
+            g_rem = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rem, stream=stream):
+                one_pass(rem)
+        for _ in range(max(1, -(-warmup // L))):
             g.replay()
         torch.cuda.synchronize()
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
-        n_rep = max(1, steps // L)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
-        for _ in range(n_rep):
+        for _ in range(n_full):
             g.replay()
+        if g_rem is not None:
+            g_rem.replay()
         stop.record(stream)
         stop.synchronize()
         total_ms = start.elapsed_time(stop)
         per_rep = []
-        for _ in range(min(20, n_rep)):
+        for _ in range(max(min_replays, min(20, n_full), 1)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -245,8 +261,8 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
         torch.cuda.synchronize()
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
-    del g
-    us = total_ms * 1e3 / (n_rep * L)
+    del g, g_rem
+    us = total_ms * 1e3 / steps
     U = unique_experts(ids_list)
     bias = layers[0]["br"] is not None
     per_rep.sort()
@@ -255,10 +271,12 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup):
     total = layer_bytes(cfg, T, U, bias, layers[0]["Wr"].element_size(), shb)
     flops = expert_flops(cfg, T, k1)
     return {
-        "T": T, "k1": k1, "k2": k2, "path": path, "layers": L, "steps": n_rep * L,
+        "T": T, "k1": k1, "k2": k2, "path": path, "layers": L, "steps": steps,
         "router": "bf16" if layers[0]["Wr"].dtype == torch.bfloat16 else "fp32",
         "shared_expert_channels": Is,
         "us_per_layer": us,
+        "replays": len(per_rep),
+        "us_median": per_rep[len(per_rep) // 2],
         "us_p10": per_rep[len(per_rep) // 10], "us_p90": per_rep[(9 * len(per_rep)) // 10],
         "tokens_per_s": T / (us * 1e-6),
         "unique_experts": U,
@@ -376,24 +394,73 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
     return err
 
 
-def cpu_baseline(oracle, synth, layer, k1, k2, budget_s=12.0):
-    """The oracle as it stands, on host copies of one ring layer, batch 1."""
+def host_cores():
+    """Cores this process may use: its affinity mask, capped by OMP_NUM_THREADS
+    when that is set (the CPU share of the machine)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(omp))) if omp.isdigit() and int(omp) > 0 else n
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(oracle, synth, layer, k1, k2, budget_s=8.0):
+    """The oracle as it stands, on host copies of one ring layer: single-token
+    calls on one core, then batches of tokens threaded over every core."""
     n = synth.to_numpy
     host = {k: n(layer[k]) for k in ("Wr", "Wg", "Wu", "Wd")}
     xs = n(layer["x"])
-    done, t0 = 0, time.perf_counter()
-    while True:
-        i = done % xs.shape[0]
-        oracle.forward(xs[i:i + 1], host["Wr"], host["Wg"], host["Wu"], host["Wd"], k1, k2,
-                       nthreads=1)
-        done += 1
-        el = time.perf_counter() - t0
-        if el > budget_s or done >= 4000:
-            break
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} single-token calls (batch 1, k1:k2={k1}:{k2}) of the C oracle on "
-                      f"host copies of one H=2048/E=128/I=768 bf16 layer, {el:.1f} s; the "
-                      f"oracle threads over tokens, so one token runs on one core"}
+
+    def run(batch, nthreads):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            i = (done // batch * batch) % (xs.shape[0] - batch + 1)
+            oracle.forward(xs[i:i + batch], host["Wr"], host["Wg"], host["Wu"], host["Wd"], k1,
+                           k2, nthreads=nthreads)
+            done += batch
+            el = time.perf_counter() - t0
+            if el > budget_s or done >= 20000:
+                return done / el, done, el
+
+    one, n1, t1 = run(1, 1)
+    cores = host_cores()
+    allc, na, ta = run(min(4 * cores, xs.shape[0]), cores)
+    return {"value": allc, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "one_core": one, "cpu_model": cpu_model(),
+            "precision": "route in exact fp32; logits, experts and combine accumulated in fp64",
+            "sample": f"batch-1 decode layer H=2048 E=128 I=768 bf16 k1:k2={k1}:{k2}: "
+                      f"{n1} single-token calls on 1 core in {t1:.1f} s, then {na} tokens in "
+                      f"batches threaded over {cores} cores in {ta:.1f} s"}
+
+
+def read_ceiling(moe, torch, nbytes=4 << 30):
+    """Read-only streaming rate (moe_hbm_read_probe) over a buffer 16x the
+    Infinity Cache: the best of a few grid sizes, 10 launches each."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(65536, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        moe.hbm_read_probe(buf, out, blocks)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            moe.hbm_read_probe(buf, out, blocks)
+        b.record()
+        b.synchronize()
+        gbs = nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, blocks)
+    del buf
+    return {"GBps": best[0], "blocks": best[1], "bytes": nbytes}
 
 
 def copy_calibration(torch, nbytes=256 << 20):
@@ -453,6 +520,16 @@ def main():
                       parts[4] if len(parts) > 4 else "auto"))
     sets = make_sets(synth, torch, {s[0] for s in specs}, args.ring)
 
+    cells_out = open(args.cells_out, "w") if args.cells_out else None
+
+    def emit(c):
+        line = json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()
+                           if not k.startswith("_")})
+        print(line, file=sys.stderr, flush=True)
+        if cells_out:
+            cells_out.write(line + "\n")
+            cells_out.flush()
+
     cells = []
     for idx, (name, T, k1, k2, path) in enumerate(specs):
         cfg, layers = sets[name]
@@ -463,10 +540,12 @@ def main():
         else:
             steps = args.steps if idx == 0 else min(args.steps, 50 * len(layers))
         c = time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps,
-                      args.warmup if idx == 0 else min(args.warmup, 4 * len(layers)))
+                      args.warmup if idx == 0 else min(args.warmup, 4 * len(layers)),
+                      min_replays=10 if idx == 0 else 0)
         c["config"] = name
         print(f"# {name} b{T} {k1}:{k2} [{path}]: {c['us_per_layer']:.2f} us/layer "
-              f"({c['us_p10']:.2f}-{c['us_p90']:.2f}), {c['tokens_per_s']:.0f} tok/s, "
+              f"(replays {c['us_p10']:.2f}-{c['us_median']:.2f}-{c['us_p90']:.2f}), "
+              f"{c['tokens_per_s']:.0f} tok/s, "
               f"{c['counted_GBps']:.0f} GB/s counted ({100 * c['hbm_frac_counted']:.1f}% of HBM), "
               f"{c['expert_tflops']:.1f} TFLOP/s, U={c['unique_experts']:.1f}",
               file=sys.stderr, flush=True)
@@ -478,6 +557,7 @@ def main():
         c["parity_normwise_err"] = check_parity(moe, torch, oracle, synth, layers[0], T, k1, k2,
                                                 path, c["_ys"][0],
                                                 n_tok=4 if name == "C5" else 32)
+        emit(c)
     print("# parity: every cell matches the oracle", file=sys.stderr, flush=True)
 
     head = cells[0]
@@ -501,10 +581,15 @@ def main():
           f"({timing}; eager event pair {eager_us:.2f} us)",
           file=sys.stderr, flush=True)
     calib = copy_calibration(torch)
+    ceiling = read_ceiling(moe, torch)
+    print(f"# read-only streaming ceiling {ceiling['GBps']:.0f} GB/s "
+          f"({ceiling['blocks']} workgroups); copy {calib['GBps_read_plus_write']:.0f} GB/s",
+          file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(oracle, synth, hlayers[0], hk1, hk2)
+        print(f"# cpu baseline {json.dumps(cpu)}", file=sys.stderr, flush=True)
 
     def find(cfgname, T, k1, k2):
         for (n_, T_, a_, b_, p_), c in zip(specs, cells):
@@ -514,34 +599,34 @@ def main():
 
     ratios = {}
     for cfgname, T in (("C2", 1), ("C3", 2), ("C3", 4), ("C3", 8), ("C3", 16), ("C3", 32),
-                       ("C3", 64), ("C3", 128), ("C3", 256), ("C2h", 1), ("C3h", 8),
-                       ("C4", 4096), ("C4h", 4096), ("C2s", 1), ("C3s", 8), ("C4s", 4096),
-                       ("C2k", 1), ("C3k", 8)):
+                       ("C3", 64), ("C4", 4096)):
         a, b = find(cfgname, T, 4, 16), find(cfgname, T, 8, 8)
         if a and b:
-            tag = {"h": "_bf16_router", "s": "_shared_expert",
-                   "k": "_channel_topk"}.get(cfgname[2:], "")
-            ratios[f"b{T}_4:16_over_8:8{tag}"] = b["us_per_layer"] / a["us_per_layer"]
+            ratios[f"b{T}"] = round(b["us_per_layer"] / a["us_per_layer"], 3)
+    c20, c10 = find("C5", 1, 5, 20), find("C5", 1, 10, 10)
+    c5 = find("C5", 1, 5, 5)
 
     us = head["us_per_layer"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
     roofline = {
-        "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": achieved / HBM_PEAK_GBS if achieved else None,
+        "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
         "traffic": traffic_record(dom["kernel"]),
-        "kernel": dom["kernel"], "us_per_launch": dom_us, "timing": timing,
-        "us_per_launch_eager_events": eager_us,
-        "algorithmic_bytes_per_launch": dom_bytes,
-        "launches": launches,
+        "kernel": dom["kernel"], "algorithmic_bytes": dom_bytes,
+        "us_per_launch": round(dom_us, 3), "timing": timing,
+        "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4) if achieved else None,
     }
+    if cpu:
+        cpu = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in cpu.items()}
     out = {
         "metric": "MoE-layer tokens/s + % HBM peak at batch 1/8, k1:k2 4:16 vs 8:8",
-        "value": head["tokens_per_s"],
+        "value": round(head["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": us / 1e3,
+        "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -551,16 +636,24 @@ def main():
             "workload": f"decode batch {hT}, H={hcfg.H} E={hcfg.E} I={hcfg.I} bf16 experts, "
                         f"k1:k2={hk1}:{hk2}, cold ring of {len(hlayers)} layers replayed from "
                         f"one HIP graph",
-            "global_batch": hT, "ring_layers": len(hlayers),
+            "global_batch": hT,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "copy_calibration": calib,
-        "cells": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()
-                   if not k.startswith("_")} for c in cells],
-        "ratios": ratios,
+        "replays": {"n": head["replays"], "us_median": round(head["us_median"], 3),
+                    "us_p10": round(head["us_p10"], 3), "us_p90": round(head["us_p90"], 3)},
+        "ratio_8:8_over_4:16": ratios,
+        "C5_b1_us": ({"10:10": round(c10["us_per_layer"], 2), "5:5": round(c5["us_per_layer"], 2),
+                      "5:20": round(c20["us_per_layer"], 2)} if c10 and c5 and c20 else None),
+        "read_ceiling_GBps": round(ceiling["GBps"], 1),
+        "cells": len(cells),
+        "cells_out": args.cells_out,
     }
-    print(json.dumps(out))
+    if cells_out:
+        cells_out.close()
+    line = json.dumps(out, separators=(",", ":"))
+    print(f"# summary line {len(line)} bytes", file=sys.stderr, flush=True)
+    print(line, flush=True)
     return 0
 
 

@@ -19,19 +19,20 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["route", "forward", "forward_channel_topk", "down_column_norms", "MoeError", "library_path", "load_library",
-           "F32", "BF16", "FORCE_FUSED", "FORCE_GROUPED", "FORCE_PREFILL", "ROUTER_BF16"]
+__all__ = ["route", "forward", "forward_channel_topk", "down_column_norms", "workspace_status",
+           "MoeError", "library_path", "load_library",
+           "F32", "BF16", "FORCE_GROUPED", "FORCE_PREFILL", "ROUTER_BF16"]
 
 PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libmoe.so"
 
 F32, BF16 = 0, 1
-FORCE_FUSED, FORCE_GROUPED, FORCE_PREFILL = 1, 2, 4
+FORCE_GROUPED, FORCE_PREFILL = 2, 4
 ROUTER_BF16 = 8
 ABI_VERSION = 1
 
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_EWORKSPACE",
-           4: "MOE_ENOTSUP", 5: "MOE_EHIP"}
+           4: "MOE_ENOTSUP", 5: "MOE_EHIP", 6: "MOE_EDEVICE"}
 
 _lib = None
 _lock = threading.Lock()
@@ -85,6 +86,12 @@ def load_library():
         lib.moe_profile_launch.restype = ctypes.c_int
         lib.moe_profile_launch.argtypes = [i32, P, P]
         lib.moe_profile_launch_name.restype = ctypes.c_char_p
+        lib.moe_workspace_status.restype = ctypes.c_int
+        lib.moe_workspace_status.argtypes = [P, P]
+        lib.moe_debug_withhold_route.restype = ctypes.c_int
+        lib.moe_debug_withhold_route.argtypes = [i32, u32]
+        lib.moe_hbm_read_probe.restype = ctypes.c_int
+        lib.moe_hbm_read_probe.argtypes = [P, ctypes.c_size_t, P, i32, P]
         if lib.moe_abi_version() != ABI_VERSION:
             raise MoeError(-1, f"libmoe ABI {lib.moe_abi_version()} != {ABI_VERSION}")
         _lib = lib
@@ -151,8 +158,10 @@ def profile_launch_name() -> str:
     return load_library().moe_profile_launch_name().decode()
 
 
-# One zero-filled workspace per (device, stream), grown on demand.  The
-# library leaves its synchronisation words at zero after every call.
+# One zero-filled workspace per (device, stream), grown on demand (a new one
+# is zero-filled again).  It can serve calls of any shape: the library keeps
+# its hand-over words at fixed places with call tags that do not repeat for
+# 2^31 calls.
 _workspaces: dict = {}
 
 
@@ -163,6 +172,42 @@ def _workspace(device, stream_ptr: int, nbytes: int) -> torch.Tensor:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def workspace_status(workspace=None, device=None):
+    """Wait for the current stream and read and reset the device status word of
+    ``workspace`` (default: this module's workspace for the current device and
+    stream); raises MoeError (MOE_EDEVICE) if a hand-over wait inside a kernel
+    gave up since the last check (moe_workspace_status)."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    stream = _stream(dev)
+    if workspace is None:
+        workspace = _workspaces.get((dev, stream.value or 0))
+        if workspace is None:
+            return
+    _need_cuda("workspace", workspace, torch.uint8)
+    _check(lib.moe_workspace_status(_ptr(workspace), stream))
+
+
+def debug_withhold_route(calls: int, spin_limit: int = 64):
+    """Test hook (moe_debug_withhold_route): the next ``calls`` one-token calls
+    on this thread do not publish their route; their waits give up after
+    ``spin_limit`` re-reads and set the device status word."""
+    _check(load_library().moe_debug_withhold_route(calls, spin_limit))
+
+
+def hbm_read_probe(buf: torch.Tensor, out: torch.Tensor, blocks: int):
+    """Measurement aid (moe_hbm_read_probe): stream-read every byte of the
+    contiguous device tensor ``buf`` once; ``out`` is a uint32/int32 device
+    tensor of at least ``blocks`` elements."""
+    lib = load_library()
+    _need_cuda("buf", buf)
+    _need_cuda("out", out)
+    if out.numel() < blocks or out.element_size() != 4:
+        raise MoeError(1, "out needs `blocks` 4-byte elements")
+    _check(lib.moe_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                  blocks, _stream(buf.device)))
 
 
 def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,

@@ -29,8 +29,8 @@ COMMON = [
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]
 
-SOURCES = ["route.hip", "decode.hip", "fused_decode.hip", "decode_b1.hip", "prefill.hip",
-           "channel_topk.hip", "moe_abi.cpp"]
+SOURCES = ["route.hip", "decode.hip", "decode_b1.hip", "prefill.hip",
+           "channel_topk.hip", "util.hip", "moe_abi.cpp"]
 
 
 def _compile(src: str) -> Path:

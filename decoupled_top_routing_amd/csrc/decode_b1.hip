@@ -60,9 +60,9 @@ namespace b1 {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRepP = 16;         // copies of the published route
+constexpr int kRepP = kB1RepP;    // copies of the published route
 constexpr int kPF = 8;            // activated experts whose down rows are in flight per wave
-constexpr int kCntStride = 16;    // 64-bit words between two counters (128 B)
+constexpr int kCntStride = kB1CntStride;  // 64-bit words between two counters (128 B)
 constexpr int kLdsBytes = 24576;  // staged channel activations of one D block
 
 struct Args {
@@ -89,7 +89,10 @@ struct Args {
   const float *sgw;   // shared gate vector [H], or NULL (factor 1)
   int m, Is;          // shared pieces (Is / I, 0 without a shared expert)
   int H, E, I, k1, k2, n_r, n_cb, n_gu, n_d;
+  uint32_t spin_limit;  // re-reads before a wait gives up
   bool router_bf16;   // bf16 router: bf16 Wr, logits and weights rounded to bf16
+  bool withhold_route;  // test hook: the route is never published, so every
+                        // wait for it gives up (outputs unspecified, error set)
 };
 
 // LDS of a block: the route block's arrays or a D block's staged activations
@@ -108,14 +111,16 @@ template <typename WT>
 constexpr int kABytes = sizeof(WT) == 2 ? 2 : 4;
 
 // Wait until the tagged words p[0..n) (n <= kWave, one per lane) carry tag;
-// lane i returns word i.  Bounded; SLEEP is the pause between two re-reads.
+// lane i returns word i.  At most `limit` re-reads; SLEEP is the pause
+// between two of them.
 template <int SLEEP = 1>
-__device__ uint64_t await_lane(const uint64_t *p, int n, uint32_t tag, int32_t *err) {
+__device__ uint64_t await_lane(const uint64_t *p, int n, uint32_t tag, int32_t *err,
+                               uint32_t limit) {
   const int lane = lane_id();
   uint64_t w = lane < n ? coh_ld(p + lane) : ((uint64_t)tag << 32);
   uint32_t spins = 0;
   while (__ballot((uint32_t)(w >> 32) != tag)) {
-    if (++spins > kSpinLimit) {
+    if (++spins > limit) {
       if (lane == 0) coh_st(err, 1);
       break;
     }
@@ -222,7 +227,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
   if (tid == 0) coh_st(a.started + d, (uint64_t)tag << 32);
   // the activated experts, ascending, then the shared pieces
   if (wv == 0) {
-    const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, 2 * a.k1, tag, err);
+    const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, 2 * a.k1, tag, err, a.spin_limit);
     if ((lane & 1) == 0 && lane < 2 * a.k1)
       s_uniq[lane >> 1] = min(max(__float_as_int(__uint_as_float((uint32_t)w)), 0), a.E - 1);
     if (lane < a.m) s_uniq[a.k1 + lane] = lane;
@@ -294,7 +299,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
           const uint64_t w = open ? coh_ld(cw + lane) : 0ull;
           ready = __ballot(open && (uint32_t)(w >> 32) == tag);
           if (ready) break;
-          if (++spins > kSpinLimit) {
+          if (++spins > a.spin_limit) {
             if (lane == 0) coh_st(err, 1);
             ready = all & ~done;  // give up waiting; the call reports an error
             break;
@@ -341,7 +346,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
     }
     if (ub == 0) {
       // every activated expert's and shared piece's activations are stored
-      if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, U, tag, err);
+      if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, U, tag, err, a.spin_limit);
       __syncthreads();
     }
     // stage this round's activations (device-coherent 8-byte loads)
@@ -449,13 +454,13 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     // route is published.
     if (tid <= a.k1 + a.m) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
     stage_tagged<kMaxExperts / kSyncThreads>(L.r.sl, a.E, [&](int i) { return a.tl + i; }, tag,
-                                             err);
+                                             err, a.spin_limit);
     route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S, a.router_bf16);
     for (int r = tid; r < a.k1; r += kThreads) {
       if (a.ids_out) a.ids_out[r] = L.r.s_ids[r];
       if (a.w_out) a.w_out[r] = L.r.s_w[r];
     }
-    if (tid < kWave) {
+    if (tid < kWave && !a.withhold_route) {
       const int n = a.k1;
       __builtin_amdgcn_s_waitcnt(0);
       // lane r holds slot r; u = its expert's place among the activated ones;
@@ -505,7 +510,8 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
       ubase = static_cast<const WT *>(a.Su) + off;
     } else {
       if (wv == 0) {
-        const uint64_t w = await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err);
+        const uint64_t w =
+            await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err, a.spin_limit);
         const uint64_t we = __shfl(w, 0), ww = __shfl(w, 1);
         if (lane == 0) {
           // a timed-out wait leaves any value here: keep the index in range
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     gateup_rows<WT, XT, NCH, CPW>(a, u, gbase, ubase, s_wt, (cb * kWaves + wv) * CPW);
     // a shared block counts itself only once the route is published: the
     // route block sets the counters before it publishes
-    if (shared && wv == 0) await_lane(a.tp + (item % kRepP) * a.tp_rep, 2, tag, err);
+    if (shared && wv == 0) await_lane(a.tp + (item % kRepP) * a.tp_rep, 2, tag, err, a.spin_limit);
     // every activation store of the block is complete, then count the block
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
       for (int i = tid; i < a.n_d; i += kThreads) {
         uint32_t spins = 0;
         while (coh_ld(a.started + i) != ((uint64_t)tag << 32)) {
-          if (++spins > kSpinLimit) {
+          if (++spins > a.spin_limit) {
             coh_st(err, 1);
             break;
           }
@@ -582,58 +588,50 @@ bool decode_b1_supported(int H, int I, int k1, bool bf16, int m) {
   if (!(nch == 1 || nch == 2 || nch == 4 || nch == 8)) return false;
   const int ab = bf16 ? 2 : 4;
   const int round_bytes = (k1 + m < b1::kPF ? k1 + m : b1::kPF) * I * ab;
+  // the fixed tagged region holds every word of these shapes
+  static_assert(3 * (kWave / 2) + kWave / 2 <= kB1TpRepWords, "route copy too small");
+  static_assert(kWave + 1 <= kB1MaxCounters, "too few counters");
+  if ((H + b1::kWaves - 1) / b1::kWaves > kB1MaxDownBlocks) return false;
   return I * esz / 16 <= 2 * kWave && round_bytes <= b1::kLdsBytes && (I * ab) % 8 == 0;
 }
 
-B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16, int m) {
-  B1Layout L;
-  auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
-  size_t o = 0;
-  L.tl = o;
-  o += r256((size_t)E * 8);
-  L.tp = o;
-  L.tp_rep_words = (int64_t)(((((size_t)(3 * k1 + m) * 8 + 4095) & ~(size_t)4095) + 1280) / 8);
-  o += r256(b1::kRepP * (size_t)L.tp_rep_words * 8);
-  L.cnt = o;
-  o += r256((size_t)(k1 + m + 1) * b1::kCntStride * 8);
-  L.started = o;
-  o += r256((size_t)((H + b1::kWaves - 1) / b1::kWaves) * 8);
-  L.abuf = o;
-  o += r256((size_t)(k1 + m) * I * (bf16 ? 2 : 4));
-  L.total = o;
-  return L;
+size_t decode_b1_abuf_bytes(int I, int k1, bool bf16, int m) {
+  return (((size_t)(k1 + m) * I * (bf16 ? 2 : 4)) + 255) & ~(size_t)255;
 }
 
+// The gate/up row's 16-byte chunks per lane follow from the router row's
+// (NCHR, fp32) and the weight dtype, so only those kernels are built; each
+// wave takes CPW = 8 / NCH channels, 8 chunks of each row in flight per lane.
 template <typename WT, typename XT, int NCHR, int V>
-static void launch_nch(b1::Args &a, int nch, int ncd, hipStream_t s) {
-  auto go = [&](auto kern, int cpw) {
-    a.n_cb = (a.I + b1::kWaves * cpw - 1) / (b1::kWaves * cpw);
-    a.n_gu = (a.k1 + a.m) * a.n_cb;
-    const int grid = a.n_r + 1 + a.n_gu + a.n_d;
-    kern<<<dim3((unsigned)grid), dim3(b1::kThreads), 0, s>>>(a);
-  };
-#define B1_GO(NCH, CPW)                                        \
-  do {                                                         \
-    if (ncd == 1)                                              \
-      go(b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 1>, CPW); \
-    else                                                       \
-      go(b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 2>, CPW); \
-  } while (0)
-  if (nch == 1) B1_GO(1, 8);
-  else if (nch == 2) B1_GO(2, 4);
-  else if (nch == 4) B1_GO(4, 2);
-  else B1_GO(8, 1);
-#undef B1_GO
+static void launch_nch(b1::Args &a, int ncd, hipStream_t s) {
+  constexpr int NCH = sizeof(WT) == 2 ? NCHR / 2 : NCHR;
+  static_assert(NCH >= 1 && NCH <= 8, "gate/up chunks per lane out of range");
+  constexpr int CPW = 8 / NCH;
+  a.n_cb = (a.I + b1::kWaves * CPW - 1) / (b1::kWaves * CPW);
+  a.n_gu = (a.k1 + a.m) * a.n_cb;
+  const int grid = a.n_r + 1 + a.n_gu + a.n_d;
+  if (ncd == 1)
+    b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 1><<<dim3((unsigned)grid), dim3(b1::kThreads), 0, s>>>(a);
+  else
+    b1::layer_kernel<WT, XT, NCHR, V, NCH, CPW, 2><<<dim3((unsigned)grid), dim3(b1::kThreads), 0, s>>>(a);
 }
 
 template <typename WT, typename XT, int V>
-static void launch_v(b1::Args &a, int nchr, int nch, int ncd, hipStream_t s) {
-  switch (nchr) {
-    case 1: launch_nch<WT, XT, 1, V>(a, nch, ncd, s); break;
-    case 2: launch_nch<WT, XT, 2, V>(a, nch, ncd, s); break;
-    case 4: launch_nch<WT, XT, 4, V>(a, nch, ncd, s); break;
-    case 8: launch_nch<WT, XT, 8, V>(a, nch, ncd, s); break;
-    default: launch_nch<WT, XT, 16, V>(a, nch, ncd, s); break;
+static void launch_v(b1::Args &a, int nchr, int ncd, hipStream_t s) {
+  if constexpr (sizeof(WT) == 2) {
+    switch (nchr) {
+      case 2: launch_nch<WT, XT, 2, V>(a, ncd, s); break;
+      case 4: launch_nch<WT, XT, 4, V>(a, ncd, s); break;
+      case 8: launch_nch<WT, XT, 8, V>(a, ncd, s); break;
+      default: launch_nch<WT, XT, 16, V>(a, ncd, s); break;
+    }
+  } else {
+    switch (nchr) {
+      case 1: launch_nch<WT, XT, 1, V>(a, ncd, s); break;
+      case 2: launch_nch<WT, XT, 2, V>(a, ncd, s); break;
+      case 4: launch_nch<WT, XT, 4, V>(a, ncd, s); break;
+      default: launch_nch<WT, XT, 8, V>(a, ncd, s); break;
+    }
   }
 }
 
@@ -642,10 +640,10 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
                             int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
                             int k2, const WT *Sg, const WT *Su, const WT *Sd, int Is,
                             const float *sgw, XT *y, float *logits_out, int32_t *ids_out,
-                            float *w_out, int32_t *sync, char *region, hipStream_t s) {
+                            float *w_out, int32_t *sync, char *region, void *abuf,
+                            uint32_t spin_limit, bool withhold_route, hipStream_t s) {
   constexpr int esz = sizeof(WT);
   const int m = Sg ? Is / I : 0;
-  const B1Layout Lb = decode_b1_layout(H, E, I, k1, esz == 2, m);
   b1::Args a;
   a.x = x;
   a.Wr = Wr;
@@ -665,12 +663,14 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
   a.ids_out = ids_out;
   a.w_out = w_out;
   a.sync = sync;
-  a.tl = reinterpret_cast<uint64_t *>(region + Lb.tl);
-  a.tp = reinterpret_cast<uint64_t *>(region + Lb.tp);
-  a.tp_rep = Lb.tp_rep_words;
-  a.cnt = reinterpret_cast<uint64_t *>(region + Lb.cnt);
-  a.started = reinterpret_cast<uint64_t *>(region + Lb.started);
-  a.abuf = region + Lb.abuf;
+  a.tl = reinterpret_cast<uint64_t *>(region + kB1Tl);
+  a.tp = reinterpret_cast<uint64_t *>(region + kB1Tp);
+  a.tp_rep = kB1TpRepWords;
+  a.cnt = reinterpret_cast<uint64_t *>(region + kB1Cnt);
+  a.started = reinterpret_cast<uint64_t *>(region + kB1Started);
+  a.abuf = abuf;
+  a.spin_limit = spin_limit;
+  a.withhold_route = withhold_route;
   a.H = H;
   a.E = E;
   a.I = I;
@@ -679,13 +679,13 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
   a.n_r = (E + b1::kWaves - 1) / b1::kWaves;
   a.n_d = (H + b1::kWaves - 1) / b1::kWaves;
   a.n_cb = a.n_gu = 0;
-  const int nchr = H / (4 * kWave), nch = b1_nch(H, esz);
+  const int nchr = H / (4 * kWave);
   const int ncd = (I * esz / 16 + kWave - 1) / kWave;
-  if (E <= 64) launch_v<WT, XT, 1>(a, nchr, nch, ncd, s);
-  else if (E <= 128) launch_v<WT, XT, 2>(a, nchr, nch, ncd, s);
-  else if (E <= 256) launch_v<WT, XT, 4>(a, nchr, nch, ncd, s);
-  else if (E <= 512) launch_v<WT, XT, 8>(a, nchr, nch, ncd, s);
-  else launch_v<WT, XT, 16>(a, nchr, nch, ncd, s);
+  if (E <= 64) launch_v<WT, XT, 1>(a, nchr, ncd, s);
+  else if (E <= 128) launch_v<WT, XT, 2>(a, nchr, ncd, s);
+  else if (E <= 256) launch_v<WT, XT, 4>(a, nchr, ncd, s);
+  else if (E <= 512) launch_v<WT, XT, 8>(a, nchr, ncd, s);
+  else launch_v<WT, XT, 16>(a, nchr, ncd, s);
   return hipGetLastError();
 }
 
@@ -695,7 +695,7 @@ hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16
                                                const WT *, int, int, int, const WT *,         \
                                                const WT *, const WT *, int, const float *,    \
                                                XT *, float *, int32_t *, float *, int32_t *,  \
-                                               char *, hipStream_t);
+                                               char *, void *, uint32_t, bool, hipStream_t);
 MOE_INST_B1(float, float)
 MOE_INST_B1(bf16_t, bf16_t)
 

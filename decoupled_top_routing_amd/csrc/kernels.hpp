@@ -20,19 +20,8 @@ constexpr size_t kSyncRegionBytes = 16384;
 // error word set by a wait that timed out
 constexpr int kEpochWord = 0;
 constexpr int kErrorWord = 32;
-
-// Byte offsets of the fused decode kernel's buffers in the workspace.
-struct DecodeLayout {
-  size_t sync, logits, abuf, total;
-};
-size_t fused_decode_workspace(int64_t T, int H, int E, int I, int k1, DecodeLayout *L);
-bool fused_decode_supported(int64_t T, int H, int E, int I, int k1, bool bf16);
-
-template <typename WT, typename XT>
-hipError_t launch_fused_decode(const XT *x, int64_t T, int H, const float *Wr, const float *br,
-                               int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
-                               int k2, XT *y, float *logits_out, int32_t *ids_out, float *w_out,
-                               char *ws, hipStream_t s);
+// re-reads before a hand-over wait gives up (and sets the error word)
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;
 
 hipError_t launch_route(const float *logits, int64_t T, int E, int k1, int k2, int32_t *ids,
                         float *w, int32_t *ids2, float *w2, hipStream_t s);
@@ -68,19 +57,37 @@ hipError_t launch_router_route(const XT *x, int H, const float *Wr, const float 
                                hipStream_t s);
 
 // ---- one token in one launch (router, route, gate/up and down)
-struct B1Layout {
-  size_t tl, tp, cnt, started, abuf, total;  // byte offsets in the path's region
-  int64_t tp_rep_words;
-};
+// Its tagged hand-over words sit at fixed places of a region of fixed size
+// that follows the sync region in every workspace (no other path writes
+// there): E tagged logits (up to kMaxExperts), kB1RepP copies of the
+// published route (kB1TpRepWords apart: 4 KiB + 1280 B, so that pollers
+// spread over memory channels), up to kB1MaxCounters completion counters
+// (kB1CntStride words apart) and a started word per down block (up to
+// kB1MaxDownBlocks).
+constexpr int kB1RepP = 16;
+constexpr int64_t kB1TpRepWords = (4096 + 1280) / 8;
+constexpr int kB1MaxCounters = 65;
+constexpr int kB1CntStride = 16;
+constexpr int kB1MaxDownBlocks = 1024;
+constexpr size_t kB1Tl = 0;
+constexpr size_t kB1Tp = kB1Tl + (size_t)kMaxExperts * 8;
+constexpr size_t kB1Cnt = kB1Tp + (size_t)kB1RepP * kB1TpRepWords * 8;
+constexpr size_t kB1Started = kB1Cnt + (size_t)kB1MaxCounters * kB1CntStride * 8;
+constexpr size_t kB1RegionBytes = (kB1Started + (size_t)kB1MaxDownBlocks * 8 + 255) & ~(size_t)255;
 // m = pieces of I channels of the shared expert (0 without one)
 bool decode_b1_supported(int H, int I, int k1, bool bf16, int m);
-B1Layout decode_b1_layout(int H, int E, int I, int k1, bool bf16, int m);
+// bytes of the channel activations [k1 + m, I] (bf16 or fp32)
+size_t decode_b1_abuf_bytes(int I, int k1, bool bf16, int m);
+// region: the fixed tagged region; abuf: decode_b1_abuf_bytes bytes.  A wait
+// gives up after spin_limit re-reads; withhold_route is a test hook that
+// keeps the route from being published, so the waits for it give up.
 template <typename WT, typename XT>
 hipError_t launch_decode_b1(const XT *x, int H, const void *Wr, bool router_bf16, const float *br,
                             int E, const WT *Wg, const WT *Wu, const WT *Wd, int I, int k1,
                             int k2, const WT *Sg, const WT *Su, const WT *Sd, int Is,
                             const float *sgw, XT *y, float *logits_out, int32_t *ids_out,
-                            float *w_out, int32_t *sync, char *region, hipStream_t s);
+                            float *w_out, int32_t *sync, char *region, void *abuf,
+                            uint32_t spin_limit, bool withhold_route, hipStream_t s);
 
 // ---- prefill (bf16 MFMA) path
 bool prefill_supported(int H, int I, bool bf16);

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kernels.hpp"
@@ -52,12 +53,16 @@ int shared_pieces(int32_t I, int32_t Is) { return Is > 0 && Is % I == 0 ? Is / I
 
 // Workspace layout of moe_forward (each segment 256-byte aligned).
 struct Layout {
-  size_t logits, ids, w, plan, abuf, zbuf, tagged, plan_s, gs, abuf_s, zbuf_s, total;
+  size_t logits, ids, w, plan, abuf, zbuf, abuf_b1, plan_s, gs, abuf_s, zbuf_s, total;
 };
+
+// Every workspace starts with the sync region, then the one-token kernel's
+// fixed tagged region; the per-call buffers follow.
+constexpr size_t kFixedBytes = moe::kSyncRegionBytes + moe::kB1RegionBytes;
 
 Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   Layout L;
-  size_t o = moe::kSyncRegionBytes;  // reserved: sync words of the fused path
+  size_t o = kFixedBytes;
   const size_t n_assign = (size_t)T * (size_t)k1;
   L.logits = o;
   o += round256((size_t)T * E * 4);
@@ -71,10 +76,8 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is
   o += round256(n_assign * (size_t)I * 4);
   L.zbuf = o;
   o += round256(n_assign * (size_t)H * 4);
-  L.tagged = o;
-  const int m = shared_pieces(I, Is);
-  o += round256(moe::decode_b1_layout(H, E, I, k1, true, m).total);
-  o += round256(moe::decode_b1_layout(H, E, I, k1, false, m).total);
+  L.abuf_b1 = o;
+  o += moe::decode_b1_abuf_bytes(I, k1, false, shared_pieces(I, Is));
   L.plan_s = L.gs = L.abuf_s = L.zbuf_s = o;
   if (Is > 0) {
     L.plan_s = o;
@@ -97,7 +100,7 @@ struct PrefillLayout {
 
 PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   PrefillLayout L;
-  size_t o = moe::kSyncRegionBytes;
+  size_t o = kFixedBytes;
   const size_t n = (size_t)T * (size_t)k1;
   L.logits = o;
   o += round256((size_t)T * E * 4);
@@ -132,9 +135,10 @@ PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   return L;
 }
 
-// Largest T accepted: keeps every element index of every tensor well inside
-// int64 and every grid dimension inside its hardware limit.
-constexpr int64_t kMaxT = int64_t(1) << 24;
+// Largest T accepted.  With the size limits of check_sizes, every launch of
+// every path stays inside the hardware's 32-bit grid size (work-items per
+// launch < 2^32) and every element index inside int64.
+constexpr int64_t kMaxT = int64_t(1) << 18;
 
 int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
   if (T < 0 || T > kMaxT) return fail(MOE_EINVAL, "T=%lld out of [0, %lld]", (long long)T, (long long)kMaxT);
@@ -144,7 +148,33 @@ int check_route_args(int64_t T, int32_t E, int32_t k1, int32_t k2) {
   return MOE_OK;
 }
 
-enum class Path { Single, Fused, Grouped, Prefill };
+// Work-items of the largest MFMA launch of the prefill path (a grouped GEMM
+// over n assignments of at most E experts, N columns of width 64 or 128).
+int64_t prefill_grid_items(int64_t n, int32_t E, int32_t N) {
+  const int64_t u = n < E ? n : E;
+  return ((n + 127) / 128 + u + 8) * ((N + 63) / 64) * 256;
+}
+
+// Size limits beyond the per-argument ranges: the per-expert launches
+// (E*H and E*I work-items, a few per element), the elementwise ones (T*H)
+// and the prefill GEMMs.
+int check_sizes(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
+  constexpr int64_t kGrid = int64_t(1) << 32;
+  if ((int64_t)E * H > (int64_t(1) << 25) || (int64_t)E * I > (int64_t(1) << 25))
+    return fail(MOE_EINVAL, "E*H=%lld and E*I=%lld must not exceed 2^25", (long long)E * H,
+                (long long)E * I);
+  if (T * H > (int64_t(1) << 28) || T * Is > (int64_t(1) << 28) || T * E > (int64_t(1) << 28))
+    return fail(MOE_EINVAL, "T*H, T*E and T*Is must not exceed 2^28 (T=%lld H=%d E=%d Is=%d)",
+                (long long)T, H, E, Is);
+  const int32_t N = H > I ? H : I;
+  if (prefill_grid_items(T * k1, E, N) >= kGrid ||
+      (Is > 0 && prefill_grid_items(T, 1, H > Is ? H : Is) >= kGrid))
+    return fail(MOE_EINVAL, "T*k1=%lld is too large for one call at H=%d I=%d", (long long)(T * k1),
+                H, I);
+  return MOE_OK;
+}
+
+enum class Path { Single, Grouped, Prefill };
 
 // The expert projections run as MFMA GEMMs from kPrefillMinAssign
 // assignments (T * k1) on, when the experts get two rows each on average;
@@ -153,18 +183,10 @@ enum class Path { Single, Fused, Grouped, Prefill };
 // and the E=512 layer at 640 assignments stays faster on the GEMV path).
 constexpr int64_t kPrefillMinAssign = 512;
 
-// The grouped multi-kernel path is the default: measured on MI355X it beats
-// the single-launch fused path at every decode batch (its gate/up and down
-// kernels sustain more bandwidth than the fused kernel's, which is limited
-// by register-bound occupancy); the fused path stays available on request.
+// The grouped multi-kernel path is the default below the prefill rule; one
+// token takes the single-launch kernel (decided by the caller).
 int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is, bool bf16,
                 uint32_t flags, Path *path) {
-  const bool fused_ok = Is == 0 && moe::fused_decode_supported(T, H, E, I, k1, bf16);
-  if (flags & MOE_FLAG_FORCE_FUSED) {
-    if (!fused_ok) return fail(MOE_ENOTSUP, "the fused path does not take these shapes");
-    *path = Path::Fused;
-    return MOE_OK;
-  }
   const bool prefill_ok =
       moe::prefill_supported(H, I, bf16) && (Is == 0 || moe::prefill_supported(H, Is, bf16));
   if (flags & MOE_FLAG_FORCE_PREFILL) {
@@ -185,12 +207,9 @@ int choose_path(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t 
 }
 
 size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
-  moe::DecodeLayout D;
-  size_t a = moe::fused_decode_workspace(T, H, E, I, k1, &D);
   const size_t b = layout(T, H, E, I, k1, Is).total;
   const size_t c = prefill_layout(T, H, E, I, k1, Is).total;
-  if (b > a) a = b;
-  return c > a ? c : a;
+  return c > b ? c : b;
 }
 
 // ---- launches of one moe_forward call, with the profiling aid of
@@ -198,11 +217,17 @@ size_t workspace_bytes_for(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k
 thread_local int g_prof_launch = -1;
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 thread_local char g_prof_name[64] = "";
+// test hook of moe_debug_withhold_route: one-token calls left on this thread
+// that withhold their route, and the wait limit they use
+thread_local int g_withhold_calls = 0;
+thread_local uint32_t g_withhold_spin = 0;
 
 struct Launches {
   hipStream_t s;
   int n, prof;
   hipEvent_t start, stop;
+  uint32_t spin_limit = moe::kDefaultSpinLimit;
+  bool withhold_route = false;
   explicit Launches(hipStream_t st) : s(st), n(0), prof(g_prof_launch), start(g_prof_start),
                                       stop(g_prof_stop) {
     g_prof_launch = -1;  // one call only
@@ -296,12 +321,6 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
                              reinterpret_cast<const uint16_t *>(Wd), I, k1, k2, sh,
                              reinterpret_cast<uint16_t *>(y), logits_out, ids_out, w_out, ws, run);
   }
-  if (path == Path::Fused) {
-    RUN("fused_decode", (moe::launch_fused_decode<WT, XT>(x, T, H, Wr32, br, E, Wg, Wu, Wd, I, k1,
-                                                          k2, y, logits_out, ids_out, w_out, ws,
-                                                          s)));
-    return MOE_OK;
-  }
   float *logits = reinterpret_cast<float *>(ws + L.logits);
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
   float *w = reinterpret_cast<float *>(ws + L.w);
@@ -314,10 +333,16 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   const WT *Sg = static_cast<const WT *>(sh.Sg), *Su = static_cast<const WT *>(sh.Su),
            *Sd = static_cast<const WT *>(sh.Sd);
   if (path == Path::Single) {
+    if (g_withhold_calls > 0) {
+      --g_withhold_calls;
+      run.withhold_route = true;
+      run.spin_limit = g_withhold_spin;
+    }
     RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
                                                    k1, k2, Sg, Su, Sd, sh.Is, sh.sgw, y,
                                                    logits_out, ids_out, w_out, sync,
-                                                   ws + L.tagged, s)));
+                                                   ws + moe::kSyncRegionBytes, ws + L.abuf_b1,
+                                                   run.spin_limit, run.withhold_route, s)));
     return MOE_OK;
   }
   if (T == 1 && !router_bf16 && moe::router_route_supported(H)) {
@@ -371,6 +396,33 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
 
 #undef RUN
 
+// MOE_DEBUG set (and not "0") in the environment: every forward call waits
+// for its work and checks the device status word (not under graph capture).
+bool debug_checks() {
+  static const bool on = [] {
+    const char *v = getenv("MOE_DEBUG");
+    return v != nullptr && *v != 0 && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+// Wait for the stream, read the error word of the workspace's sync region
+// and reset it: MOE_EDEVICE if a hand-over wait gave up since the last check.
+int take_device_status(char *ws, hipStream_t s) {
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws + 4 * moe::kErrorWord, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "read of the device status word");
+  if (v == 0) return MOE_OK;
+  const int32_t zero = 0;
+  e = hipMemcpyAsync(ws + 4 * moe::kErrorWord, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reset of the device status word");
+  return fail(MOE_EDEVICE,
+              "a hand-over wait inside the layer kernel gave up: the outputs of a call on this "
+              "workspace since the last check are unspecified");
+}
+
 // moe_forward and moe_forward_shared: argument checks, then the path.
 int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
                  const float *br, int32_t E, const void *Wgate, const void *Wup,
@@ -386,7 +438,8 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
     return fail(MOE_EINVAL, "H*I=%lld exceeds 2^31", (long long)H * I);
   if (sh.Sg && (sh.Is < 8 || sh.Is % 8 != 0 || (int64_t)H * sh.Is > (int64_t(1) << 31)))
     return fail(MOE_EINVAL, "Is=%d must be a positive multiple of 8 with H*Is <= 2^31", sh.Is);
-  const uint32_t paths = MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
+  if ((rc = check_sizes(T, H, E, I, k1, sh.Sg ? sh.Is : 0)) != MOE_OK) return rc;
+  const uint32_t paths = MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_PREFILL;
   if (flags & ~(paths | MOE_FLAG_ROUTER_BF16))
     return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
   if (__builtin_popcount(flags & paths) > 1)
@@ -400,16 +453,12 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
     return fail(MOE_ENOTSUP, "the bf16 router takes bf16 activations and weights");
   if (router_bf16 && br)
     return fail(MOE_EINVAL, "the bf16 router takes no bias (br must be NULL)");
-  if (router_bf16 && (flags & MOE_FLAG_FORCE_FUSED))
-    return fail(MOE_ENOTSUP, "the fused path has no bf16 router");
-  if (sh.Sg && (flags & MOE_FLAG_FORCE_FUSED))
-    return fail(MOE_ENOTSUP, "the fused path has no shared expert");
   if (ck.dn) {
     if (!moe::channel_select_supported(k1, I))
       return fail(MOE_ENOTSUP, "channel top-k takes k1*I <= 8192 (got %lld)", (long long)k1 * I);
     if (ck.keep < 0 || (int64_t)ck.keep > (int64_t)k1 * I)
       return fail(MOE_EINVAL, "keep=%d out of [0, k1*I=%lld]", ck.keep, (long long)k1 * I);
-    if (flags & (MOE_FLAG_FORCE_FUSED | MOE_FLAG_FORCE_PREFILL))
+    if (flags & MOE_FLAG_FORCE_PREFILL)
       return fail(MOE_ENOTSUP, "channel top-k runs on the grouped path only");
   }
   if (T == 0) return MOE_OK;
@@ -445,15 +494,18 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
   Launches run((hipStream_t)stream);
   char *ws = static_cast<char *>(workspace);
   if (f32)
-    return forward_typed<float, float>(
+    rc = forward_typed<float, float>(
         static_cast<const float *>(x), T, H, Wr, false, br, E, static_cast<const float *>(Wgate),
         static_cast<const float *>(Wup), static_cast<const float *>(Wdown), I, k1, k2, sh, ck,
         static_cast<float *>(y), logits_out, ids_out, w_out, path, ws, L, run);
-  return forward_typed<moe::bf16_t, moe::bf16_t>(
-      static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
-      static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
-      static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, sh, ck, static_cast<moe::bf16_t *>(y),
-      logits_out, ids_out, w_out, path, ws, L, run);
+  else
+    rc = forward_typed<moe::bf16_t, moe::bf16_t>(
+        static_cast<const moe::bf16_t *>(x), T, H, Wr, router_bf16, br, E,
+        static_cast<const moe::bf16_t *>(Wgate), static_cast<const moe::bf16_t *>(Wup),
+        static_cast<const moe::bf16_t *>(Wdown), I, k1, k2, sh, ck,
+        static_cast<moe::bf16_t *>(y), logits_out, ids_out, w_out, path, ws, L, run);
+  if (rc == MOE_OK && debug_checks()) rc = take_device_status(ws, (hipStream_t)stream);
+  return rc;
 }
 
 }  // namespace
@@ -470,6 +522,7 @@ const char *moe_status_str(int status) {
     case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ENOTSUP: return "unsupported dtype combination";
     case MOE_EHIP: return "HIP runtime error";
+    case MOE_EDEVICE: return "a device-side wait gave up; outputs unspecified";
     default: return "unknown status";
   }
 }
@@ -579,5 +632,19 @@ int moe_profile_launch(int32_t launch, void *start, void *stop) {
 }
 
 const char *moe_profile_launch_name(void) { return g_prof_name; }
+
+int moe_workspace_status(void *workspace, void *stream) {
+  if (!workspace) return fail(MOE_EINVAL, "NULL workspace");
+  if (!aligned(workspace, 256)) return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+  return take_device_status(static_cast<char *>(workspace), (hipStream_t)stream);
+}
+
+int moe_debug_withhold_route(int32_t calls, uint32_t spin_limit) {
+  if (calls < 0 || spin_limit < 1)
+    return fail(MOE_EINVAL, "calls=%d must be >= 0 and spin_limit=%u >= 1", calls, spin_limit);
+  g_withhold_calls = calls;
+  g_withhold_spin = spin_limit;
+  return MOE_OK;
+}
 
 }  // extern "C"

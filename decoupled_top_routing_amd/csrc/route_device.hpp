@@ -1,7 +1,7 @@
 // Device-side route of one token: fp32 softmax with a specified exp, ranking
 // and the Eq. 2 weights ("Paper of the Week #3 - Half the FLOPs Is Not Half
 // the Time", section "The Receipt", Eq. 2; section "Ship It - Code of the
-// Week").  Used by the route kernel and by the fused decode kernel.
+// Week").  Used by the route kernels and by the one-token layer kernel.
 #pragma once
 
 #include "common.hpp"

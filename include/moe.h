@@ -40,7 +40,10 @@
  *    the caller's next synchronisation, as usual for HIP;
  *  - logits must be finite (a precondition: with a non-finite logit the
  *    outputs for that token are unspecified);
- *  - entry points never throw and are safe to call from several host threads.
+ *  - entry points never throw and are safe to call from several host threads;
+ *  - with MOE_DEBUG set in the environment (to anything but "0"), every
+ *    moe_forward* call also waits for its work and returns the device status
+ *    of moe_workspace_status (so it cannot be captured in a HIP graph).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -60,8 +63,9 @@ typedef enum {
     MOE_EINVAL = 1,     /* a size or k argument out of range, or a NULL pointer */
     MOE_EALIGN = 2,     /* a pointer without the required alignment */
     MOE_EWORKSPACE = 3, /* workspace NULL, misaligned or too small */
-    MOE_ENOTSUP = 4,    /* unsupported dtype combination */
-    MOE_EHIP = 5        /* a HIP runtime call failed */
+    MOE_ENOTSUP = 4,    /* unsupported dtype combination or shape for a path */
+    MOE_EHIP = 5,       /* a HIP runtime call failed */
+    MOE_EDEVICE = 6     /* a wait inside a kernel gave up (moe_workspace_status) */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -71,14 +75,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * route and the activations over through the workspace; decode batches take
  * GROUPED, large batches PREFILL).  All paths compute the same layer; they
  * differ in kernels:
- *   FUSED   an older single launch per layer, batches <= 8 tokens;
  *   GROUPED router, route, per-expert plan, gate/up, down and combine kernels
- *           (grouped GEMVs that read each activated expert once);
+ *           (grouped GEMVs that read each activated expert once); with one
+ *           token it replaces the single launch;
  *   PREFILL the same steps with the expert projections as bf16 MFMA grouped
  *           GEMMs (chosen from 512 assignments T*k1 on, when the activated
  *           experts average two rows or more).
- * A forced path that cannot take the call's shapes returns MOE_ENOTSUP. */
-#define MOE_FLAG_FORCE_FUSED 1u
+ * A forced path that cannot take the call's shapes returns MOE_ENOTSUP.  Bit
+ * value 1 is not a flag (MOE_EINVAL). */
 #define MOE_FLAG_FORCE_GROUPED 2u
 #define MOE_FLAG_FORCE_PREFILL 4u
 
@@ -95,8 +99,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * logits_out and w_out still receive fp32 arrays, holding the bf16 values.
  * At k1 = k2 this is the stock renormalising bf16 router.  It needs the
  * (BF16, BF16) dtype pair (MOE_ENOTSUP otherwise) and combines with
- * MOE_FLAG_FORCE_GROUPED or MOE_FLAG_FORCE_PREFILL; with
- * MOE_FLAG_FORCE_FUSED it returns MOE_ENOTSUP. */
+ * MOE_FLAG_FORCE_GROUPED or MOE_FLAG_FORCE_PREFILL. */
 #define MOE_FLAG_ROUTER_BF16 8u
 
 /* Version of this ABI (MOE_ABI_VERSION). */
@@ -116,8 +119,8 @@ const char *moe_last_error_str(void);
  *   logits  [T, E] fp32, finite.                   4-byte aligned
  *   ids     [T, k1] int32 out: expert indices in rank order
  *   weights [T, k1] fp32 out: Eq. 2 weights in the same order
- *   1 <= E <= 1024;  1 <= k1 <= E;  k2 >= k1 (k2 > E behaves as k2 = E).
- *   T = 0 returns MOE_OK and launches nothing.
+ *   1 <= E <= 1024;  1 <= k1 <= E;  k2 >= k1 (k2 > E behaves as k2 = E);
+ *   0 <= T <= 2^18.  T = 0 returns MOE_OK and launches nothing.
  */
 int moe_route(const float *logits, int64_t T, int32_t E, int32_t k1,
               int32_t k2, int32_t *ids, float *weights, void *stream);
@@ -148,16 +151,23 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *   logits_out [T,E] fp32, ids_out [T,k1] int32, w_out [T,k1] fp32: optional
  *          copies of the route (NULL to skip), 4-byte aligned
  *   workspace: device memory of at least moe_forward_workspace(...) bytes,
- *          256-byte aligned, ZERO-FILLED before its first use; the library
- *          leaves its synchronisation words at zero after every call, so one
- *          zero fill at allocation lasts for the workspace's lifetime.  Calls
- *          that run concurrently need separate workspaces.
+ *          256-byte aligned, ZERO-FILLED before its first use.  It carries
+ *          state from call to call, so one zero fill at allocation lasts for
+ *          its lifetime, whatever the shapes of later calls: an epoch word
+ *          that advances on every one-token call (the source of the tags of
+ *          its hand-over words, which sit at fixed places of a region of
+ *          their own, so a stale word cannot carry the current tag until 2^31
+ *          calls have passed), the error word read by moe_workspace_status,
+ *          and counters that return to zero after every call.  Calls that
+ *          run concurrently need separate workspaces.
  *   flags: 0 or one MOE_FLAG_FORCE_* value, optionally with
  *          MOE_FLAG_ROUTER_BF16.
  *
  *   Supported dtype pairs (act, w): (F32, F32) and (BF16, BF16); accumulation
  *   is fp32.  1 <= E <= 1024; H and I multiples of 8; 1 <= k1 <= E;
- *   k2 >= k1.  T = 0 returns MOE_OK and launches nothing.
+ *   k2 >= k1; 0 <= T <= 2^18; E*H and E*I at most 2^25; T*H and T*E at most
+ *   2^28 (and T*k1 small enough for the prefill GEMM grids; MOE_EINVAL
+ *   otherwise).  T = 0 returns MOE_OK and launches nothing.
  *   Identical inputs give bitwise identical logits, ids, weights and y.
  */
 int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
@@ -185,8 +195,8 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
  *   Is     shared channels: a positive multiple of 8, H * Is <= 2^31
  *   sgate  [H] fp32 gate vector, or NULL                            4-byte aligned
  * Every other argument, and the route outputs, as for moe_forward (the
- * route is unchanged by the shared expert).  The workspace size comes from
- * moe_forward_shared_workspace.  MOE_FLAG_FORCE_FUSED returns MOE_ENOTSUP;
+ * route is unchanged by the shared expert; T*Is at most 2^28).  The
+ * workspace size comes from moe_forward_shared_workspace.
  * MOE_FLAG_FORCE_PREFILL also needs Is % 64 == 0.  For one token with
  * Is % I == 0 the shared expert runs inside the single launch of the layer,
  * streaming while the token is routed.
@@ -244,8 +254,8 @@ int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
  *                                                              16-byte aligned
  *   kept_out   [T, k1*I] uint8, or NULL: 1 for a kept channel, else 0
  *                                                               8-byte aligned
- * It runs on the grouped path: MOE_FLAG_FORCE_FUSED and
- * MOE_FLAG_FORCE_PREFILL return MOE_ENOTSUP; MOE_FLAG_ROUTER_BF16 applies.
+ * It runs on the grouped path: MOE_FLAG_FORCE_PREFILL returns MOE_ENOTSUP;
+ * MOE_FLAG_ROUTER_BF16 applies.
  * The workspace is moe_forward_workspace's.  The down projection still
  * reads whole down rows (the [E, H, I] layout puts a column's elements 2*I
  * bytes apart), so the selection changes y, not the bytes read.
@@ -273,6 +283,47 @@ int moe_forward_channel_topk(const void *x, int32_t act_dtype, int64_t T,
  */
 int moe_profile_launch(int32_t launch, void *start, void *stop);
 const char *moe_profile_launch_name(void);
+
+/*
+ * moe_workspace_status -- the device status of a workspace.  The one-token
+ * kernel's workgroups hand the route and the activations to one another
+ * through tagged words of the workspace; every such wait is bounded, and one
+ * that gives up (a precondition broken, or a fault elsewhere on the device)
+ * lets its kernel run to the end with unspecified outputs and sets an error
+ * word in the workspace.  The pages do not cover this (their router runs
+ * in the framework's own kernels); it is this library's contract.
+ *
+ * Waits for `stream`, reads the error word and resets it: MOE_EDEVICE if a
+ * wait gave up in any call on this workspace since the last check, else
+ * MOE_OK.  A synchronous host call: not for use under graph capture.
+ *   workspace  the moe_forward* workspace (256-byte aligned)
+ */
+int moe_workspace_status(void *workspace, void *stream);
+
+/*
+ * moe_debug_withhold_route -- test hook for the status above.  The next
+ * `calls` calls on the calling thread that run the one-token kernel do not
+ * publish their route, so every wait for it gives up after `spin_limit`
+ * re-reads (>= 1); their kernels still run to the end, reading only in-range
+ * expert rows, and their outputs are unspecified.  calls = 0 disarms.
+ */
+int moe_debug_withhold_route(int32_t calls, uint32_t spin_limit);
+
+/*
+ * moe_hbm_read_probe -- measurement aid: the read-only streaming ceiling.
+ * Loads every 16-byte chunk of buf once with the streaming loads the expert
+ * kernels use and writes one word per workgroup to out (an xor of what it
+ * read, so the loads are live).  Timing a launch over a buffer much larger
+ * than the device's last-level cache gives the read bandwidth a kernel can
+ * reach, the ceiling for the decode kernels beside the HBM peak.
+ *   buf     device buffer, 16-byte aligned; bytes a positive multiple of 16
+ *   out     [blocks] uint32 device buffer, 4-byte aligned
+ *   blocks  workgroups of 256 threads, 1..65536
+ * Returns MOE_EINVAL / MOE_EALIGN on bad arguments, MOE_EHIP on a failed
+ * launch.
+ */
+int moe_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int32_t blocks,
+                       void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,6 @@
 """Comparison helpers for the GPU parity tests (HIP path against the oracle)."""
+import os
+
 import numpy as np
 import torch
 
@@ -6,6 +8,10 @@ import oracle
 from decoupled_top_routing_amd import synth
 
 DEV = "cuda:0"
+
+# host threads for the oracle (it threads over tokens); at most 16, the CPU
+# share of one GPU on the boxes these tests run on
+NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 # Output tolerances, normwise per token: max_h |y - y_ref| / max_h |y_ref|.
 TOL_F32 = 1e-5   # fp32 activations and weights
@@ -77,7 +83,8 @@ def run_and_check(cfg, L, Lh, k1, k2, flags=0, token_sample=None, tol=None):
     against the oracle's experts and combine on that route, within the dtype's
     tolerance; (iv) an independent oracle route from x picks the same experts
     except on near-ties.  token_sample limits (i), (iii) and (iv) to those
-    tokens; Lh may omit the expert weights (see expert_subset)."""
+    tokens; Lh may omit the expert weights (see expert_subset).  Returns
+    (y, error, number of tokens whose y was checked)."""
     import decoupled_top_routing_amd as moe
     g = to_dev(L) if L["Wg"].device.type == "cpu" else L
     print(f"{cfg.name} T={g['x'].shape[0]} k1={k1} k2={k2} flags={flags}", flush=True)
@@ -88,11 +95,11 @@ def run_and_check(cfg, L, Lh, k1, k2, flags=0, token_sample=None, tol=None):
     T = lg_h.shape[0]
     sel = np.arange(T) if token_sample is None else np.asarray(token_sample)
     x_h = Lh["x"][sel]
-    ref_l = oracle.logits(x_h, Lh["Wr"], Lh["br"], nthreads=8)
+    ref_l = oracle.logits(x_h, Lh["Wr"], Lh["br"], nthreads=NTHREADS)
     assert normwise_err(lg_h[sel], ref_l) <= 1e-5
     oids, ow = check_route_exact(ids, w, lg_h, k1, k2, f"{cfg.name} ({k1},{k2})")
     Wg, Wu, Wd, sids = expert_subset(g, Lh, oids[sel])
-    y_ref = oracle.experts(x_h, Wg, Wu, Wd, sids, ow[sel], nthreads=8)
+    y_ref = oracle.experts(x_h, Wg, Wu, Wd, sids, ow[sel], nthreads=NTHREADS)
     err = normwise_err(to_f64(y)[sel], y_ref)
     tol = tol if tol is not None else (TOL_F32 if cfg.dtype == "f32" else TOL_BF16)
     assert err <= tol, f"normwise error {err} > {tol}"
@@ -100,4 +107,4 @@ def run_and_check(cfg, L, Lh, k1, k2, flags=0, token_sample=None, tol=None):
     ties = near_tie_tokens(oracle.softmax(ref_l), k1)
     differ = (np.sort(iids, 1) != np.sort(oids[sel], 1)).any(1)
     assert not (differ & ~ties).any(), "experts differ away from a near-tie"
-    return y, err
+    return y, err, len(sel)

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = moe.load_library()
-    for code in range(6):
+    for code in range(7):
         assert lib.moe_status_str(code)
     assert lib.moe_status_str(99) == b"unknown status"
 
@@ -59,6 +59,7 @@ def _route(lib, T, E, k1, k2, ptr=8):
     (1, 16, 17, 17, 1),       # k1 > E
     (1, 16, 4, 3, 1),         # k2 < k1
     (-1, 16, 2, 4, 1),        # T < 0
+    ((1 << 18) + 1, 16, 2, 4, 1),   # T above the limit that keeps T*256 work-items in range
 ])
 def test_route_rejects_bad_arguments(T, E, k1, k2, code):
     lib = moe.load_library()
@@ -96,9 +97,14 @@ def _fwd(lib, **kw):
     (dict(ws=None), 3), (dict(ws=128), 3), (dict(wsb=1024), 3),
     (dict(x=None), 1), (dict(flags=3), 1), (dict(flags=16), 1),
     (dict(flags=4, act=0, wt=0), 4), (dict(flags=4, I=776), 4), (dict(flags=4, H=2056), 4),
-    # the bf16 router: bf16 pair only, no bias, not on the fused path
-    (dict(flags=8, act=0, wt=0), 4), (dict(flags=8, br=16), 1), (dict(flags=9), 4),
-    (dict(flags=8 | 3), 1), (dict(flags=8 | 32), 1),
+    # bit value 1 is not a flag (it was a retired path)
+    (dict(flags=1), 1), (dict(flags=9), 1),
+    # the bf16 router: bf16 pair only, no bias
+    (dict(flags=8, act=0, wt=0), 4), (dict(flags=8, br=16), 1),
+    (dict(flags=8 | 6), 1), (dict(flags=8 | 32), 1),
+    # sizes whose launch grids would pass 2^32 work-items
+    (dict(T=(1 << 18) + 1), 1), (dict(T=1 << 18, H=2048), 1), (dict(E=1024, H=65536), 1),
+    (dict(E=1024, I=65536), 1),
 ])
 def test_forward_rejects_bad_arguments(kw, code):
     lib = moe.load_library()
@@ -126,8 +132,9 @@ def _fwd_shared(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(Sg=None), 1), (dict(Sd=None), 1), (dict(Is=4), 1), (dict(Is=772), 1),
     (dict(Sg=24), 2), (dict(Sd=8), 2), (dict(sg=2), 2),
-    (dict(flags=1), 4),                   # the fused path has no shared expert
+    (dict(flags=1), 1),                   # not a flag
     (dict(flags=4, Is=72), 4),            # the prefill path needs Is % 64 == 0
+    (dict(T=1 << 17, Is=4096), 1),        # T*Is above 2^28
     (dict(k2=3), 1), (dict(ws=None), 3),
 ])
 def test_forward_shared_rejects_bad_arguments(kw, code):
@@ -170,6 +177,29 @@ def test_channel_topk_argument_checks():
     assert fwd(keep=4 * 768 + 1) == 1
     assert fwd(k1=11, keep=10) == 4          # k1*I > 8192
     assert fwd(flags=4) == 4                 # prefill path
-    assert fwd(flags=1) == 4                 # fused path
+    assert fwd(flags=1) == 1                 # not a flag
     assert fwd(dn=2) == 2                    # misaligned dnorm
     assert fwd(dn=20) == 2                   # dnorm needs 16-byte alignment
+
+
+def test_workspace_status_argument_checks():
+    lib = moe.load_library()
+    assert lib.moe_workspace_status(None, None) == 1
+    assert lib.moe_workspace_status(ctypes.c_void_p(128), None) == 3
+
+
+def test_withhold_route_hook_argument_checks():
+    lib = moe.load_library()
+    assert lib.moe_debug_withhold_route(-1, 64) == 1
+    assert lib.moe_debug_withhold_route(1, 0) == 1
+    assert lib.moe_debug_withhold_route(0, 1) == 0     # disarmed
+
+
+def test_workspace_size_is_the_same_for_calls_of_any_shape_prefix():
+    """The sync region and the one-token kernel's tagged region sit at fixed
+    places: a workspace for one shape starts with the same fixed part as one
+    for any other, so calls of different shapes can share it."""
+    lib = moe.load_library()
+    small = lib.moe_forward_workspace(1, 256, 16, 64, 2, 0, 0)
+    big = lib.moe_forward_workspace(1, 4096, 1024, 1024, 32, 1, 1)
+    assert 0 < small < big

@@ -23,7 +23,7 @@ def tiny():
     return L, host_layer(L)
 
 
-PATHS = [0, moe.FORCE_FUSED, moe.FORCE_GROUPED]
+PATHS = [0, moe.FORCE_GROUPED]
 
 
 @pytest.mark.parametrize("k1,k2", synth.TINY.k_pairs)
@@ -49,7 +49,7 @@ def test_a3b_decode(a3b, k1, k2, T):
     run_and_check(cfg, Lt, Lht, k1, k2)
 
 
-@pytest.mark.parametrize("flags", [moe.FORCE_FUSED, moe.FORCE_GROUPED])
+@pytest.mark.parametrize("flags", [moe.FORCE_GROUPED, moe.FORCE_PREFILL])
 @pytest.mark.parametrize("k1,k2", [(8, 8), (4, 16)])
 @pytest.mark.parametrize("T", [1, 8])
 def test_a3b_decode_each_path(a3b, k1, k2, flags, T):
@@ -125,7 +125,7 @@ def test_zero_tokens(a3b):
     (8, 8, 8, 64, 16, 5),      # every expert active: the dense mixture
     (16, 3, 40, 136, 24, 17),  # k2 > E, ragged sizes
     (1024, 2, 7, 64, 8, 9),    # the most experts
-    (16, 2, 4, 256, 64, 64),   # the largest batch on the fused decode path
+    (16, 2, 4, 256, 64, 64),   # 64 tokens: the route kernel's in-kernel plan limit
     (16, 2, 4, 256, 64, 65),   # the smallest batch past it
     (512, 10, 20, 512, 136, 40),  # many unique experts, down rows of 34 chunks
     (33, 5, 9, 1024, 64, 13),  # router rows of 4 chunks per lane

@@ -14,13 +14,6 @@ from parity import DEV, host_layer, run_and_check, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def token_sample(T, n=96, seed=11):
-    """n distinct tokens including the first and the last."""
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
-    return np.array(sorted(s))
-
-
 @pytest.fixture(scope="module")
 def prefill():
     L = to_dev(synth.make_layer(synth.PREFILL))
@@ -29,9 +22,11 @@ def prefill():
 
 @pytest.mark.parametrize("k1,k2", synth.PREFILL.k_pairs)
 def test_prefill_4096(prefill, k1, k2):
-    """The default path at 4096 tokens is the prefill path."""
+    """The default path at 4096 tokens is the prefill path; y is checked on
+    every token (every row of the plan's permutation and every M tile)."""
     L, Lh = prefill
-    run_and_check(synth.PREFILL, L, Lh, k1, k2, token_sample=token_sample(4096))
+    _, _, n = run_and_check(synth.PREFILL, L, Lh, k1, k2)
+    assert n == 4096
 
 
 @pytest.mark.parametrize("T", [1, 63, 300])
@@ -48,7 +43,8 @@ def test_prefill_plan_beyond_lds_staging(prefill):
     plan kernel stages in LDS: its list is then scattered straight to global
     memory (8:8 at 4096 tokens, exactly 32768, takes the staged branch)."""
     L, Lh = prefill
-    run_and_check(synth.PREFILL, L, Lh, 9, 12, token_sample=token_sample(4096))
+    _, _, n = run_and_check(synth.PREFILL, L, Lh, 9, 12)
+    assert n == 4096
 
 
 def test_prefill_deterministic(prefill):
