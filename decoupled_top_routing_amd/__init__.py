@@ -90,6 +90,11 @@ def load_library():
         lib.moe_workspace_status.argtypes = [P, P]
         lib.moe_debug_withhold_route.restype = ctypes.c_int
         lib.moe_debug_withhold_route.argtypes = [i32, u32]
+        lib.moe_forward_noalloc.restype = ctypes.c_int
+        lib.moe_forward_noalloc.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32, i32,
+                                            i32, P, P, P, P, u32, P]
+        lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        lib.moe_noalloc_scratch_bytes.argtypes = []
         lib.moe_hbm_read_probe.restype = ctypes.c_int
         lib.moe_hbm_read_probe.argtypes = [P, ctypes.c_size_t, P, i32, P]
         if lib.moe_abi_version() != ABI_VERSION:
@@ -212,7 +217,7 @@ def hbm_read_probe(buf: torch.Tensor, out: torch.Tensor, blocks: int):
 
 def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
             return_route: bool = False, flags: int = 0, out=None, workspace=None,
-            shared=None):
+            shared=None, noalloc: bool = False):
     """The whole routed MoE layer.
 
     x [T,H] (fp32 or bf16), Wr [E,H] fp32, br [E] fp32 or None, Wgate and Wup
@@ -265,10 +270,17 @@ def forward(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, br=None,
         lg = torch.empty((T, E), dtype=torch.float32, device=dev)
         ids = torch.empty((T, k1), dtype=torch.int32, device=dev)
         w = torch.empty((T, k1), dtype=torch.float32, device=dev)
+    stream = _stream(dev)
+    if noalloc:
+        if shared is not None or workspace is not None:
+            raise MoeError(1, "noalloc takes neither a shared expert nor a workspace")
+        _check(lib.moe_forward_noalloc(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
+                                       _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(y), _ptr(lg),
+                                       _ptr(ids), _ptr(w), flags, stream))
+        return (y, lg, ids, w) if return_route else y
     nbytes = lib.moe_forward_shared_workspace(T, H, E, I, k1, Is, act, act)
     if nbytes == 0 and T > 0:
         raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
-    stream = _stream(dev)
     if workspace is not None:
         _need_cuda("workspace", workspace, torch.uint8)
         ws = workspace

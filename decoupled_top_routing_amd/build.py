@@ -30,7 +30,7 @@ COMMON = [
 ]
 
 SOURCES = ["route.hip", "decode.hip", "decode_b1.hip", "prefill.hip",
-           "channel_topk.hip", "util.hip", "moe_abi.cpp"]
+           "channel_topk.hip", "util.hip", "noalloc.hip", "moe_abi.cpp"]
 
 
 def _compile(src: str) -> Path:

@@ -121,6 +121,12 @@ hipError_t launch_channel_select(float *abuf, int64_t T, int k1, int I, const in
                                  const float *dn, int keep, float *scores_out, uint8_t *kept_out,
                                  hipStream_t s);
 
+// ---- the device scratch of moe_forward_noalloc (noalloc.hip)
+size_t noalloc_scratch_bytes();
+// The current device's scratch address; the first call on a device takes it
+// with hipGetSymbolAddress and zero-fills its first zero_prefix bytes on s.
+hipError_t noalloc_scratch(void **ptr, size_t zero_prefix, hipStream_t s);
+
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
 

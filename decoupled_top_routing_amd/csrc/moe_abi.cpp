@@ -553,7 +553,7 @@ size_t moe_forward_shared_workspace(int64_t T, int32_t H, int32_t E, int32_t I, 
   (void)act_dtype;
   (void)w_dtype;
   if (T < 0 || T > kMaxT || E < 1 || E > MOE_MAX_EXPERTS || k1 < 1 || k1 > E || H < 8 ||
-      I < 8 || Is < 0 || (Is > 0 && Is < 8))
+      I < 8 || Is < 0 || (Is > 0 && Is < 8) || check_sizes(T, H, E, I, k1, Is) != MOE_OK)
     return 0;
   return workspace_bytes_for(T, H, E, I, k1, Is);
 }
@@ -632,6 +632,33 @@ int moe_profile_launch(int32_t launch, void *start, void *stop) {
 }
 
 const char *moe_profile_launch_name(void) { return g_prof_name; }
+
+int moe_forward_noalloc(const void *x, int32_t act_dtype, int64_t T, int32_t H, const void *Wr,
+                        const float *br, int32_t E, const void *Wgate, const void *Wup,
+                        const void *Wdown, int32_t w_dtype, int32_t I, int32_t k1, int32_t k2,
+                        void *y, float *logits_out, int32_t *ids_out, float *w_out,
+                        uint32_t flags, void *stream) {
+  // argument errors (and T = 0) are returned by moe_forward's checks before
+  // the scratch is touched: those sizes need no workspace
+  const size_t need = moe_forward_workspace(T, H, E, I, k1, act_dtype, w_dtype);
+  if (T == 0 || need == 0)
+    return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
+                        Shared{}, ChannelTopk{}, y, logits_out, ids_out, w_out, flags, nullptr, 0,
+                        stream);
+  const size_t have = moe::noalloc_scratch_bytes();
+  if (need > have)
+    return fail(MOE_EWORKSPACE,
+                "these sizes need %zu bytes of scratch; moe_forward_noalloc holds %zu "
+                "(call moe_forward with a workspace)", need, have);
+  void *ws = nullptr;
+  const hipError_t e = moe::noalloc_scratch(&ws, kFixedBytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "device scratch of moe_forward_noalloc");
+  return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
+                      Shared{}, ChannelTopk{}, y, logits_out, ids_out, w_out, flags, ws, have,
+                      stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return moe::noalloc_scratch_bytes(); }
 
 int moe_workspace_status(void *workspace, void *stream) {
   if (!workspace) return fail(MOE_EINVAL, "NULL workspace");

@@ -32,7 +32,9 @@
  * Conventions for every entry point:
  *  - all tensors are row-major and contiguous, in device memory of the
  *    current HIP device, owned by the caller; the library keeps no pointer
- *    after returning and allocates no device memory;
+ *    after returning and allocates no device memory (its one device buffer
+ *    is the fixed scratch array of moe_forward_noalloc, which each device the
+ *    library runs on holds until the process ends);
  *  - `stream` is a hipStream_t (NULL = the null stream); all work is enqueued
  *    on it with no host synchronisation; outputs are overwritten;
  *  - argument errors are returned before anything is launched; a failed launch
@@ -177,6 +179,34 @@ int moe_forward(const void *x, int32_t act_dtype, int64_t T, int32_t H,
                 float *logits_out, int32_t *ids_out, float *w_out,
                 uint32_t flags, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * moe_forward_noalloc -- moe_forward without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid allocation, harnesses without an allocator).  It computes
+ * exactly what moe_forward computes, with the same kernels and paths, using
+ * a fixed device array of moe_noalloc_scratch_bytes() bytes (32 MiB) in
+ * place of the workspace; it calls no hipMalloc, hipFree or other
+ * allocating routine.  Sizes whose moe_forward_workspace exceeds the array
+ * return MOE_EWORKSPACE before anything is launched (the array holds the
+ * decode shapes: e.g. up to 256 tokens of an H=2048, E=128, I=768, k1=8
+ * layer, or 64 tokens of an H=4096, E=512, I=1024, k1=10 one).
+ *
+ * The array is shared by every call on a device and keeps the last call's
+ * contents; the first call on a device clears the part that must start at
+ * zero (a fill kernel on that call's stream).  Calls that overlap on one
+ * device (several streams or threads) race on it and must be serialised by
+ * the caller.  Arguments, outputs and errors as for moe_forward.
+ */
+int moe_forward_noalloc(const void *x, int32_t act_dtype, int64_t T, int32_t H,
+                        const void *Wr, const float *br, int32_t E,
+                        const void *Wgate, const void *Wup, const void *Wdown,
+                        int32_t w_dtype, int32_t I, int32_t k1, int32_t k2, void *y,
+                        float *logits_out, int32_t *ids_out, float *w_out,
+                        uint32_t flags, void *stream);
+
+/* moe_noalloc_scratch_bytes -- size of moe_forward_noalloc's device array. */
+size_t moe_noalloc_scratch_bytes(void);
 
 /*
  * moe_forward_shared -- moe_forward plus a shared expert, which runs on every
