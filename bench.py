@@ -115,6 +115,7 @@ def make_sets(synth, torch, names, ring):
             import decoupled_top_routing_amd as moe
             cfg, layers = sets[n[:2]]
             sets[n] = (cfg, [dict(lay, topk={"dn": moe.down_column_norms(lay["Wd"]),
+                                             "cols": moe.down_columns(lay["Wd"]),
                                              "frac": TOPK_FRAC})
                              for lay in layers])
     torch.cuda.synchronize()
@@ -182,7 +183,8 @@ def layer_call(moe, lay, x, k1, k2, cfg, **kw):
         keep = int(round(ck["frac"] * k1 * cfg.I))
         rr = kw.pop("return_route", False)
         r = moe.forward_channel_topk(x, lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
-                                     ck["dn"], keep, br=lay["br"], return_route=rr, **kw)
+                                     ck["dn"], keep, br=lay["br"], return_route=rr,
+                                     Wdown_cols=ck["cols"], **kw)
         return r[:4] if rr else r
     return moe.forward(x, lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2, br=lay["br"],
                        shared=shared_args(lay), **kw)
@@ -209,8 +211,10 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
     lib = moe.load_library()
     act = 1 if cfg.dtype == "bf16" else 0
     Is = layers[0]["shared"]["Sg"].shape[0] if layers[0].get("shared") else 0
-    ws = torch.zeros(lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act),
-                     dtype=torch.uint8, device=dev)
+    nws = (lib.moe_forward_channel_topk_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act)
+           if layers[0].get("topk") else
+           lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act))
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     ids_list = []
 
     def one_pass(n=L, record_ids=False):
@@ -304,8 +308,10 @@ def profile_launches(moe, torch, cfg, layers, T, k1, k2, path, n_calls):
     lib = moe.load_library()
     act = 1 if cfg.dtype == "bf16" else 0
     Is = layers[0]["shared"]["Sg"].shape[0] if layers[0].get("shared") else 0
-    ws = torch.zeros(lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act),
-                     dtype=torch.uint8, device=layers[0]["Wg"].device)
+    nws = (lib.moe_forward_channel_topk_workspace(T, cfg.H, cfg.E, cfg.I, k1, act, act)
+           if layers[0].get("topk") else
+           lib.moe_forward_shared_workspace(T, cfg.H, cfg.E, cfg.I, k1, Is, act, act))
+    ws = torch.zeros(nws, dtype=torch.uint8, device=layers[0]["Wg"].device)
 
     def call(i):
         j = i % len(layers)
@@ -357,7 +363,7 @@ def check_parity(moe, torch, oracle, synth, layer, T, k1, k2, path, y_dev, n_tok
         keep = int(round(ck["frac"] * k1 * layer["Wg"].shape[1]))
         y, lg, ids, w, sc, kept = moe.forward_channel_topk(
             x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1, k2, ck["dn"], keep,
-            br=layer["br"], return_route=True, flags=PATH_FLAGS[path])
+            br=layer["br"], return_route=True, flags=PATH_FLAGS[path], Wdown_cols=ck["cols"])
     else:
         y, lg, ids, w = moe.forward(x, layer["Wr"], layer["Wg"], layer["Wu"], layer["Wd"], k1,
                                     k2, br=layer["br"], return_route=True,

@@ -19,7 +19,8 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["route", "forward", "forward_channel_topk", "down_column_norms", "workspace_status",
+__all__ = ["route", "forward", "forward_channel_topk", "down_column_norms", "down_columns",
+           "workspace_status",
            "MoeError", "library_path", "load_library",
            "F32", "BF16", "FORCE_GROUPED", "FORCE_PREFILL", "ROUTER_BF16"]
 
@@ -29,7 +30,7 @@ LIB_PATH = PKG / "libmoe.so"
 F32, BF16 = 0, 1
 FORCE_GROUPED, FORCE_PREFILL = 2, 4
 ROUTER_BF16 = 8
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_EWORKSPACE",
            4: "MOE_ENOTSUP", 5: "MOE_EHIP", 6: "MOE_EDEVICE"}
@@ -79,8 +80,12 @@ def load_library():
         lib.moe_down_column_norms.argtypes = [P, i32, i32, i32, i32, P, P]
         lib.moe_forward_channel_topk.restype = ctypes.c_int
         lib.moe_forward_channel_topk.argtypes = [P, i32, i64, i32, P, P, i32, P, P, P, i32, i32,
-                                                 i32, i32, P, i32, P, P, P, P, P, P, u32, P,
+                                                 i32, i32, P, i32, P, P, P, P, P, P, P, u32, P,
                                                  ctypes.c_size_t, P]
+        lib.moe_forward_channel_topk_workspace.restype = ctypes.c_size_t
+        lib.moe_forward_channel_topk_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+        lib.moe_down_columns.restype = ctypes.c_int
+        lib.moe_down_columns.argtypes = [P, i32, i32, i32, i32, P, P]
         lib.moe_forward_shared_workspace.restype = ctypes.c_size_t
         lib.moe_forward_shared_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
         lib.moe_profile_launch.restype = ctypes.c_int
@@ -311,15 +316,28 @@ def down_column_norms(Wdown):
     return dn
 
 
+def down_columns(Wdown):
+    """The column copy [E, I, H] of Wdown [E, H, I] (moe_down_columns): each
+    channel's down column as one contiguous row."""
+    lib = load_library()
+    _need_cuda("Wdown", Wdown)
+    E, H, I = Wdown.shape
+    cols = torch.empty((E, I, H), dtype=Wdown.dtype, device=Wdown.device)
+    _check(lib.moe_down_columns(_ptr(Wdown), _dtype_code(Wdown), E, H, I, _ptr(cols),
+                                _stream(Wdown.device)))
+    return cols
+
+
 def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep: int,
                          br=None, return_route: bool = False, flags: int = 0, out=None,
-                         workspace=None):
+                         workspace=None, Wdown_cols=None):
     """The layer with channel top-k inside the activated experts: of each
     token's k1*I channels only the ``keep`` highest-scoring (router weight x
     down-column norm x |activation|) are summed.  ``dnorm`` comes from
-    ``down_column_norms``.  Returns y, or (y, logits, ids, w, scores, kept)
-    with ``return_route=True`` (scores [T, k1*I] fp32, kept [T, k1*I] bool).
-    ``out`` and ``workspace`` as for ``forward``."""
+    ``down_column_norms``; with ``Wdown_cols`` (from ``down_columns``) the down
+    projection reads only the kept channels' columns.  Returns y, or (y,
+    logits, ids, w, scores, kept) with ``return_route=True`` (scores [T, k1*I]
+    fp32, kept [T, k1*I] bool).  ``out`` and ``workspace`` as for ``forward``."""
     lib = load_library()
     _need_cuda("x", x)
     act = _dtype_code(x)
@@ -336,6 +354,10 @@ def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep
     if H2 != H or Wup.shape != Wgate.shape or tuple(Wdown.shape) != (E, H, I) \
             or tuple(Wr.shape) != (E, H) or tuple(dnorm.shape) != (E, I):
         raise MoeError(1, "shape mismatch between x, Wr, Wgate, Wup, Wdown and dnorm")
+    if Wdown_cols is not None:
+        _need_cuda("Wdown_cols", Wdown_cols, x.dtype)
+        if tuple(Wdown_cols.shape) != (E, I, H):
+            raise MoeError(1, "Wdown_cols must be [E, I, H]")
     dev = x.device
     y = out if out is not None else torch.empty((T, H), dtype=x.dtype, device=dev)
     lg = ids = w = sc = kept = None
@@ -345,7 +367,7 @@ def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep
         w = torch.empty((T, k1), dtype=torch.float32, device=dev)
         sc = torch.empty((T, k1 * I), dtype=torch.float32, device=dev)
         kept = torch.empty((T, k1 * I), dtype=torch.uint8, device=dev)
-    nbytes = lib.moe_forward_workspace(T, H, E, I, k1, act, act)
+    nbytes = lib.moe_forward_channel_topk_workspace(T, H, E, I, k1, act, act)
     if nbytes == 0 and T > 0:
         raise MoeError(1, f"invalid sizes T={T} H={H} E={E} I={I} k1={k1}")
     stream = _stream(dev)
@@ -356,8 +378,9 @@ def forward_channel_topk(x, Wr, Wgate, Wup, Wdown, k1: int, k2: int, dnorm, keep
         ws = _workspace(dev, stream.value or 0, nbytes)
     _check(lib.moe_forward_channel_topk(_ptr(x), act, T, H, _ptr(Wr), _ptr(br), E, _ptr(Wgate),
                                         _ptr(Wup), _ptr(Wdown), act, I, k1, k2, _ptr(dnorm), keep,
-                                        _ptr(y), _ptr(lg), _ptr(ids), _ptr(w), _ptr(sc),
-                                        _ptr(kept), flags, _ptr(ws), ws.numel(), stream))
+                                        _ptr(Wdown_cols), _ptr(y), _ptr(lg), _ptr(ids), _ptr(w),
+                                        _ptr(sc), _ptr(kept), flags, _ptr(ws), ws.numel(),
+                                        stream))
     if return_route:
         return y, lg, ids, w, sc, kept.bool()
     return y

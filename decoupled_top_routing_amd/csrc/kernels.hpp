@@ -116,10 +116,23 @@ bool channel_select_supported(int k1, int I);
 template <typename WT>
 hipError_t launch_down_column_norms(const WT *Wd, int E, int H, int I, float *dn, hipStream_t s);
 // zeroes every activation of abuf [T*k1, I] outside each token's top-keep
-// channels by score dn[e, c] * |a|; optional scores and kept flags [T, k1*I]
+// channels by score dn[e, c] * |a|; optional scores and kept flags [T, k1*I],
+// and the kept list [T, keep] of (row e*I + c of the column copy, activation)
+// in flat-channel order
 hipError_t launch_channel_select(float *abuf, int64_t T, int k1, int I, const int32_t *ids,
                                  const float *dn, int keep, float *scores_out, uint8_t *kept_out,
-                                 hipStream_t s);
+                                 uint2 *kept_list, hipStream_t s);
+// the column copy WdT [E, I, H] of Wd [E, H, I]
+template <typename WT>
+hipError_t launch_down_columns(const WT *Wd, int E, int H, int I, WT *WdT, hipStream_t s);
+// h-slices (one 16-byte chunk per lane) and list groups of the kept-channel
+// down projection; its partial sums take T * groups * H floats
+int kept_slices(int H, int esz);
+int kept_groups(int64_t T, int H, int keep, int esz);
+// y = the kept channels' columns scaled by their activations, from the list
+template <typename WT, typename XT>
+hipError_t launch_kept_down(const WT *WdT, int64_t T, int H, const uint2 *kept_list, int keep,
+                            float *part, XT *y, hipStream_t s);
 
 // ---- the device scratch of moe_forward_noalloc (noalloc.hip)
 size_t noalloc_scratch_bytes();

@@ -45,7 +45,25 @@ struct ChannelTopk {
   int32_t keep = 0;
   float *scores_out = nullptr;
   uint8_t *kept_out = nullptr;
+  const void *cols = nullptr;  // column copy of the down weights, or NULL
 };
+
+// Extra workspace of channel top-k with the column copy: the kept list
+// [T, keep] of 8-byte entries and the kept-down partial sums [T, groups, H].
+struct TopkLayout {
+  size_t list, part, total;
+};
+TopkLayout topk_layout(size_t base, int64_t T, int32_t H, int32_t I, int32_t k1, int esz) {
+  TopkLayout L;
+  size_t o = base;
+  L.list = o;
+  o += round256((size_t)T * k1 * I * 8);
+  L.part = o;
+  const int G = moe::kept_groups(T, H, k1 * I, esz);
+  o += round256((size_t)T * G * H * 4);
+  L.total = o;
+  return L;
+}
 
 // pieces of I channels the one-launch kernel splits the shared expert into
 // (0: none, or Is not a multiple of I)
@@ -380,9 +398,23 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   }
   RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s,
                                             Sg, Su, sh.Is, plan_s, gs, abuf_s)));
-  if (ck.dn)
+  if (ck.dn) {
+    uint2 *kept_list = nullptr;
+    float *part = nullptr;
+    if (ck.cols) {
+      const TopkLayout K = topk_layout(L.total, T, H, I, k1, (int)sizeof(WT));
+      kept_list = reinterpret_cast<uint2 *>(ws + K.list);
+      part = reinterpret_cast<float *>(ws + K.part);
+    }
     RUN("channel_select", moe::launch_channel_select(abuf, T, k1, I, ids, ck.dn, ck.keep,
-                                                     ck.scores_out, ck.kept_out, s));
+                                                     ck.scores_out, ck.kept_out, kept_list, s));
+    if (ck.cols) {
+      // the down projection reads only the kept channels' columns
+      RUN("kept_down", (moe::launch_kept_down<WT, XT>(static_cast<const WT *>(ck.cols), T, H,
+                                                      kept_list, ck.keep, part, y, s)));
+      return MOE_OK;
+    }
+  }
   const int ncd = (int)((I * sizeof(WT) / 16 + 63) / 64);
   if (T == 1 && ncd <= 2 && !Sg) {
     RUN("down_one_token", (moe::launch_down_one_token<WT, XT>(Wd, H, I, plan, E, abuf, y, s)));
@@ -472,11 +504,17 @@ int forward_impl(const void *x, int32_t act_dtype, int64_t T, int32_t H, const v
       (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)) ||
       (sh.sgw && !aligned(sh.sgw, 4)))
     return fail(MOE_EALIGN, "br, sgate and the route outputs need 4-byte alignment");
+  if (ck.cols && !aligned(ck.cols, 16))
+    return fail(MOE_EALIGN, "Wdown_cols needs 16-byte alignment");
   if ((ck.dn && !aligned(ck.dn, 16)) || (ck.scores_out && !aligned(ck.scores_out, 16)) ||
       (ck.kept_out && !aligned(ck.kept_out, 8)))
     return fail(MOE_EALIGN, "dnorm and scores_out need 16-byte, kept_out 8-byte alignment");
   const Layout L = layout(T, H, E, I, k1, sh.Is);
-  const size_t need = workspace_bytes_for(T, H, E, I, k1, sh.Is);
+  size_t need = workspace_bytes_for(T, H, E, I, k1, sh.Is);
+  if (ck.cols) {
+    const size_t t = topk_layout(L.total, T, H, I, k1, f32 ? 4 : 2).total;
+    if (t > need) need = t;
+  }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                 need, workspace_bytes, workspace);
@@ -605,19 +643,49 @@ int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E, int32_t
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down column norms");
 }
 
+int moe_down_columns(const void *Wdown, int32_t w_dtype, int32_t E, int32_t H, int32_t I,
+                     void *Wdown_cols, void *stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || H < 1 || I < 1 || (int64_t)H * I > (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "E=%d H=%d I=%d out of range", E, H, I);
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16)
+    return fail(MOE_ENOTSUP, "weight dtype %d not supported", w_dtype);
+  if (!Wdown || !Wdown_cols) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned(Wdown, 16) || !aligned(Wdown_cols, 16))
+    return fail(MOE_EALIGN, "Wdown and Wdown_cols need 16-byte alignment");
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e =
+      w_dtype == MOE_F32
+          ? moe::launch_down_columns(static_cast<const float *>(Wdown), E, H, I,
+                                     static_cast<float *>(Wdown_cols), s)
+          : moe::launch_down_columns(static_cast<const moe::bf16_t *>(Wdown), E, H, I,
+                                     static_cast<moe::bf16_t *>(Wdown_cols), s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "down columns");
+}
+
+size_t moe_forward_channel_topk_workspace(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1,
+                                          int32_t act_dtype, int32_t w_dtype) {
+  const size_t base = moe_forward_workspace(T, H, E, I, k1, act_dtype, w_dtype);
+  if (base == 0) return 0;
+  const Layout L = layout(T, H, E, I, k1, 0);
+  const size_t t = topk_layout(L.total, T, H, I, k1, w_dtype == MOE_F32 ? 4 : 2).total;
+  return t > base ? t : base;
+}
+
 int moe_forward_channel_topk(const void *x, int32_t act_dtype, int64_t T, int32_t H,
                              const void *Wr, const float *br, int32_t E, const void *Wgate,
                              const void *Wup, const void *Wdown, int32_t w_dtype, int32_t I,
-                             int32_t k1, int32_t k2, const float *dnorm, int32_t keep, void *y,
-                             float *logits_out, int32_t *ids_out, float *w_out,
-                             float *scores_out, uint8_t *kept_out, uint32_t flags,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+                             int32_t k1, int32_t k2, const float *dnorm, int32_t keep,
+                             const void *Wdown_cols, void *y, float *logits_out,
+                             int32_t *ids_out, float *w_out, float *scores_out,
+                             uint8_t *kept_out, uint32_t flags, void *workspace,
+                             size_t workspace_bytes, void *stream) {
   if (!dnorm) return fail(MOE_EINVAL, "NULL dnorm");
   ChannelTopk ck;
   ck.dn = dnorm;
   ck.keep = keep;
   ck.scores_out = scores_out;
   ck.kept_out = kept_out;
+  ck.cols = Wdown_cols;
   return forward_impl(x, act_dtype, T, H, Wr, br, E, Wgate, Wup, Wdown, w_dtype, I, k1, k2,
                       Shared{}, ck, y, logits_out, ids_out, w_out, flags, workspace,
                       workspace_bytes, stream);

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 
 typedef enum {
@@ -263,6 +263,20 @@ int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
                           int32_t H, int32_t I, float *dnorm, void *stream);
 
 /*
+ * moe_down_columns -- the column copy of the down weights,
+ * Wdown_cols[e, c, :] = Wdown[e, :, c]: each channel's down column as one
+ * contiguous row ("Channel Selection for Mixture-of-Experts Decoding Needs No
+ * Calibration Data", section 2: a channel owns one down column; section 5.2
+ * reads only the selected channels' weights).  Made once per weight set, like
+ * moe_down_column_norms; an input of moe_forward_channel_topk.
+ *
+ *   Wdown       [E, H, I] w_dtype (MOE_F32 or MOE_BF16)          16-byte aligned
+ *   Wdown_cols  [E, I, H] w_dtype out                            16-byte aligned
+ */
+int moe_down_columns(const void *Wdown, int32_t w_dtype, int32_t E, int32_t H, int32_t I,
+                     void *Wdown_cols, void *stream);
+
+/*
  * moe_forward_channel_topk -- moe_forward with channel selection inside the
  * activated experts ("Channel Selection ...", section 5.2; section 2: a
  * channel owns one gate row, one up row and one down column).  After the
@@ -280,25 +294,34 @@ int moe_down_column_norms(const void *Wdown, int32_t w_dtype, int32_t E,
  * Arguments as moe_forward, plus:
  *   dnorm      [E, I] fp32 from moe_down_column_norms          16-byte aligned
  *   keep       0 <= keep <= k1*I; k1*I <= 8192 (MOE_ENOTSUP beyond)
+ *   Wdown_cols [E, I, H] from moe_down_columns, or NULL        16-byte aligned
+ *              With it the down projection reads only the kept channels'
+ *              columns (keep rows of H values per token, summed in a fixed
+ *              order: flat-channel order within fixed groups, then the
+ *              groups' sums in a fixed tree); without it, every down row is
+ *              read with the unkept activations set to zero.
  *   scores_out [T, k1*I] fp32, or NULL: the scores the selection used
  *                                                              16-byte aligned
  *   kept_out   [T, k1*I] uint8, or NULL: 1 for a kept channel, else 0
  *                                                               8-byte aligned
  * It runs on the grouped path: MOE_FLAG_FORCE_PREFILL returns MOE_ENOTSUP;
- * MOE_FLAG_ROUTER_BF16 applies.
- * The workspace is moe_forward_workspace's.  The down projection still
- * reads whole down rows (the [E, H, I] layout puts a column's elements 2*I
- * bytes apart), so the selection changes y, not the bytes read.
+ * MOE_FLAG_ROUTER_BF16 applies.  The workspace size comes from
+ * moe_forward_channel_topk_workspace.
  */
 int moe_forward_channel_topk(const void *x, int32_t act_dtype, int64_t T,
                              int32_t H, const void *Wr, const float *br,
                              int32_t E, const void *Wgate, const void *Wup,
                              const void *Wdown, int32_t w_dtype, int32_t I,
                              int32_t k1, int32_t k2, const float *dnorm,
-                             int32_t keep, void *y, float *logits_out,
-                             int32_t *ids_out, float *w_out, float *scores_out,
-                             uint8_t *kept_out, uint32_t flags, void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             int32_t keep, const void *Wdown_cols, void *y,
+                             float *logits_out, int32_t *ids_out, float *w_out,
+                             float *scores_out, uint8_t *kept_out, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_forward_channel_topk_workspace -- bytes of workspace
+ * moe_forward_channel_topk needs (a multiple of 256); 0 for invalid sizes. */
+size_t moe_forward_channel_topk_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
+                                          int32_t k1, int32_t act_dtype, int32_t w_dtype);
 
 /*
  * moe_profile_launch -- profiling aid; changes no output.  Arms the NEXT

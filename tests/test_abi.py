@@ -165,11 +165,12 @@ def test_channel_topk_argument_checks():
     assert lib.moe_down_column_norms(v(16), 7, 128, 2048, 768, v(16), None) == 4
 
     def fwd(**kw):
-        a = dict(k1=4, keep=100, dn=16, flags=0)
+        a = dict(k1=4, keep=100, dn=16, flags=0, cols=None)
         a.update(kw)
         return lib.moe_forward_channel_topk(v(16), 1, 1, 2048, v(16), None, 128, v(16), v(16),
                                             v(16), 1, 768, a["k1"], 16,
                                             None if a["dn"] is None else v(a["dn"]), a["keep"],
+                                            None if a["cols"] is None else v(a["cols"]),
                                             v(16), None, None, None, None, None, a["flags"],
                                             v(256), 1 << 30, None)
     assert fwd(dn=None) == 1
@@ -180,6 +181,17 @@ def test_channel_topk_argument_checks():
     assert fwd(flags=1) == 1                 # not a flag
     assert fwd(dn=2) == 2                    # misaligned dnorm
     assert fwd(dn=20) == 2                   # dnorm needs 16-byte alignment
+    assert fwd(cols=24) == 2                 # the column copy needs 16-byte alignment
+    # the column copy: E out of range, misaligned, unsupported dtype
+    assert lib.moe_down_columns(v(16), 1, 0, 2048, 768, v(16), None) == 1
+    assert lib.moe_down_columns(v(16), 1, 128, 2048, 768, v(8), None) == 2
+    assert lib.moe_down_columns(v(16), 7, 128, 2048, 768, v(16), None) == 4
+    # its workspace holds the kept list and the partial sums beyond the grouped
+    # path's buffers: never smaller than moe_forward's, and 0 for invalid sizes
+    for T in (1, 8, 64):
+        assert lib.moe_forward_channel_topk_workspace(T, 2048, 128, 768, 4, 1, 1) >= \
+            lib.moe_forward_workspace(T, 2048, 128, 768, 4, 1, 1)
+    assert lib.moe_forward_channel_topk_workspace(1, 2048, 128, 768, 0, 1, 1) == 0
 
 
 def test_workspace_status_argument_checks():
