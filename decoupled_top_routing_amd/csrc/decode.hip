@@ -16,10 +16,17 @@
 //  down_kernel   : one work item = (unique expert, block of output rows):
 //                  stream the down rows once, z[t,r,h] = Wd[e,h,:] . a[t,r,:];
 //  combine_kernel: y[t,h] = sum of z[t,r,h] over the token's slots, in order.
+//
+// Batches of at most kIdsMax assignments skip the plan: every gate/up and
+// down block reads the batch's ids and finds its own expert and assignments,
+// and the down launch also does the combine (the block that completes a
+// block of output rows sums them), so such a batch runs as two launches
+// after the route.
 #include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "sync.hpp"
 
 namespace moe {
 
@@ -119,6 +126,53 @@ hipError_t launch_plan(const int32_t *ids, int64_t n_assign, int E, int32_t *pla
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- ids map
+// Work items without a plan, for n <= kIdsMax = 64 assignments: there are
+// min(n, E) keys per launch group, as many as a plan would have unique
+// experts at most.  With n <= E key q is assignment q, and the item is live
+// when q is the first assignment routed to its expert; otherwise key q is
+// expert q, live when any assignment is routed to it.  Every wave reads the
+// ids (one per lane) and one ballot marks the assignments of the item's
+// expert, so a block finds its work in one round trip and no barrier.
+
+// The assignments of a work item: n entries of lst, or the n set bits of
+// mask (ascending) when lst is NULL.
+struct Items {
+  const int32_t *lst;
+  uint64_t mask;
+  int n;
+  __device__ __forceinline__ int take(int i, uint64_t &rest) const {
+    if (lst) return lst[i];
+    const int a = __builtin_ctzll(rest);
+    rest &= rest - 1ull;
+    return a;
+  }
+};
+
+// The item of `key` (n == 0: not live) and its expert in *e_out.
+__device__ __forceinline__ Items ids_item(const int32_t *__restrict__ ids, int n, int E, int key,
+                                          int *e_out) {
+  const int lane = lane_id();
+  const bool by_asg = n <= E;
+  const int e = by_asg ? ids[key] : key;
+  *e_out = e;
+  const int ei = lane < n ? ids[lane] : -1;
+  const uint64_t m = __ballot(ei == e);
+  const bool live = by_asg ? __builtin_ctzll(m) == key : m != 0ull;
+  return Items{nullptr, m, live ? (int)__popcll(m) : 0};
+}
+
+// The item of unique expert u of a plan (n == 0: u >= U).
+__device__ __forceinline__ Items plan_item(const int32_t *__restrict__ plan, int E, int u,
+                                           int *e_out) {
+  if (u >= plan[0]) return Items{nullptr, 0ull, 0};
+  const int32_t *uniq = plan + 4;
+  const int32_t *off = uniq + E;
+  *e_out = uniq[u];
+  const int lb = off[u];
+  return Items{off + E + 1 + lb, 0ull, off[u + 1] - lb};
+}
+
 // ---------------------------------------------------------------- gate/up
 // One workgroup = (unique expert u, block of 4*CPW channels); each wave owns
 // CPW channels and issues the loads of all its gate and up rows (2*CPW*NCH
@@ -139,6 +193,8 @@ struct GuGroup {
   int E, k1;
   const float *w;
   float *abuf;
+  const int32_t *ids;  // non-NULL: work items from the ids (ids_item), no plan
+  int n;               // assignments in ids
 };
 
 // NT assignments (list entries asg) against a wave's CPW gate and up rows
@@ -239,12 +295,9 @@ __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, i
   const int n_cb = (I + kGuWaves * CPW - 1) / (kGuWaves * CPW);
   const int u = bid / n_cb;
   const int cb = bid - u * n_cb;
-  if (u >= plan[0]) return;
-  const int32_t *uniq = plan + 4;
-  const int32_t *off = uniq + E;
-  const int32_t *list = off + E + 1;
-  const int e = uniq[u];
-  const int lb = off[u], ln = off[u + 1] - lb;
+  int e = 0;
+  const Items it = G.ids ? ids_item(G.ids, G.n, E, u, &e) : plan_item(plan, E, u, &e);
+  if (it.n == 0) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int c0 = (cb * kGuWaves + wv) * CPW;
   uint4 gq[CPW][NCH], uq[CPW][NCH];
@@ -260,8 +313,11 @@ __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, i
     }
   }
   // one token at a time (two at a time measured slower: register pressure)
-  for (int i = 0; i < ln; ++i)
-    gateup_tokens<1, WT, XT, NCH, CPW>(x, H, I, k1, list + lb + i, w, abuf, gq, uq, c0);
+  uint64_t rest = it.mask;
+  for (int i = 0; i < it.n; ++i) {
+    const int32_t asg = it.take(i, rest);
+    gateup_tokens<1, WT, XT, NCH, CPW>(x, H, I, k1, &asg, w, abuf, gq, uq, c0);
+  }
 }
 
 // Any H (a multiple of 8): one channel per wave, chunks walked in a loop.
@@ -315,14 +371,22 @@ __global__ __launch_bounds__(256) void gateup_any_kernel(const XT *__restrict__ 
 }
 
 template <typename WT, typename XT>
+bool gateup_takes_ids(int H) {
+  const int nch = (H * (int)sizeof(WT)) % (16 * kWave) == 0 ? (int)(H * sizeof(WT) / 16 / kWave) : 0;
+  return nch == 1 || nch == 2 || nch == 4 || nch == 8;
+}
+
+template <typename WT, typename XT>
 hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
                          float *abuf, hipStream_t s, const WT *Sg, const WT *Su, int Is,
-                         const int32_t *plan_s, const float *gs, float *abuf_s) {
+                         const int32_t *plan_s, const float *gs, float *abuf_s,
+                         const int32_t *ids) {
   const int64_t umax = n_assign < E ? n_assign : E;
   const int nch = (H * (int)sizeof(WT)) % (16 * kWave) == 0 ? (int)(H * sizeof(WT) / 16 / kWave) : 0;
-  const GuGroup<WT> gr{Wg, Wu, I, plan, E, k1, w, abuf};
-  const GuGroup<WT> gsh{Sg, Su, Is, plan_s, 1, 1, gs, abuf_s};
+  if (ids && (n_assign > kIdsMax || !gateup_takes_ids<WT, XT>(H))) return hipErrorInvalidValue;
+  const GuGroup<WT> gr{Wg, Wu, I, plan, E, k1, w, abuf, ids, (int)(ids ? n_assign : 0)};
+  const GuGroup<WT> gsh{Sg, Su, Is, plan_s, 1, 1, gs, abuf_s, nullptr, 0};
   const GuGroup<WT> g0 = Sg ? gsh : gr;
   auto go = [&](auto nch_c, auto cpw_c) {
     constexpr int NCH = decltype(nch_c)::value, CPW = decltype(cpw_c)::value;
@@ -351,8 +415,10 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
 // One workgroup = (unique expert u, block of 4*RPW rows of Wd[e]); each wave
 // loads its RPW rows (NCD 16-byte chunks per lane per row) up front, then for
 // every assignment routed to u writes z[asg, h] = Wd[e,h,:] . a[asg,:].
+// Four rows per wave measured faster than two and than eight from 2 to 64
+// tokens (H=2048, I=768 bf16).
 constexpr int kDnWaves = 4;
-constexpr int kRPW = 2;
+constexpr int kRPW = 4;
 constexpr int kDnRB = kDnWaves * kRPW;
 
 // One group of experts in a down launch (see GuGroup, whose block order it
@@ -366,6 +432,8 @@ struct DnGroup {
   int E;
   const float *abuf;
   float *zbuf;
+  const int32_t *ids;  // non-NULL: work items from the ids (ids_item), no plan
+  int n;               // assignments in ids
 };
 
 // NT assignments against a wave's kRPW down rows already in registers:
@@ -434,12 +502,9 @@ __global__ __launch_bounds__(256) void down_kernel(int H, DnGroup<WT> g0, DnGrou
   const int n_hb = (H + kDnRB - 1) / kDnRB;
   const int u = bid / n_hb;
   const int hb = bid - u * n_hb;
-  if (u >= plan[0]) return;
-  const int32_t *uniq = plan + 4;
-  const int32_t *off = uniq + E;
-  const int32_t *list = off + E + 1;
-  const int e = uniq[u];
-  const int lb = off[u], ln = off[u + 1] - lb;
+  int e = 0;
+  const Items it = G.ids ? ids_item(G.ids, G.n, E, u, &e) : plan_item(plan, E, u, &e);
+  if (it.n == 0) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int nch = I / NW;
   const int h0 = hb * kDnRB + wv * kRPW;
@@ -454,7 +519,11 @@ __global__ __launch_bounds__(256) void down_kernel(int H, DnGroup<WT> g0, DnGrou
     }
   }
   // one token at a time (two at a time measured slower: register pressure)
-  for (int i = 0; i < ln; ++i) down_tokens<1, WT, NCD>(H, I, list + lb + i, abuf, zbuf, dq, h0);
+  uint64_t rest = it.mask;
+  for (int i = 0; i < it.n; ++i) {
+    const int32_t asg = it.take(i, rest);
+    down_tokens<1, WT, NCD>(H, I, &asg, abuf, zbuf, dq, h0);
+  }
 }
 
 // Any I: one row per wave, chunks walked in a loop.
@@ -500,16 +569,30 @@ __global__ __launch_bounds__(256) void down_any_kernel(int H, DnGroup<WT> g0, Dn
 }
 
 template <typename WT>
-hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
-                       const float *abuf, float *zbuf, hipStream_t s, const WT *Sd, int Is,
-                       const int32_t *plan_s, const float *abuf_s, float *zbuf_s) {
-  const int64_t umax = n_assign < E ? n_assign : E;
-  const int n_hb = (H + kDnRB - 1) / kDnRB;
+static int down_ncd(int I, bool shared, int Is) {
   auto ncd_of = [](int i) { return (int)((i * sizeof(WT) / 16 + kWave - 1) / kWave); };
   // one NCD for both groups: the wider one (chunks past a row's end are masked)
-  const int ncd = Sd ? max(ncd_of(I), ncd_of(Is)) : ncd_of(I);
-  const DnGroup<WT> gr{Wd, I, plan, E, abuf, zbuf};
-  const DnGroup<WT> gsh{Sd, Is, plan_s, 1, abuf_s, zbuf_s};
+  return shared ? max(ncd_of(I), ncd_of(Is)) : ncd_of(I);
+}
+
+template <typename WT>
+bool down_takes_ids(int I, int Is) {
+  const int ncd = down_ncd<WT>(I, Is > 0, Is);
+  return ncd >= 1 && ncd <= 4;
+}
+
+template <typename WT>
+hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,
+                       const float *abuf, float *zbuf, hipStream_t s, const WT *Sd, int Is,
+                       const int32_t *plan_s, const float *abuf_s, float *zbuf_s,
+                       const int32_t *ids) {
+  const int64_t umax = n_assign < E ? n_assign : E;
+  const int n_hb = (H + kDnRB - 1) / kDnRB;
+  const int ncd = down_ncd<WT>(I, Sd != nullptr, Is);
+  if (ids && (n_assign > kIdsMax || !down_takes_ids<WT>(I, Sd ? Is : 0)))
+    return hipErrorInvalidValue;
+  const DnGroup<WT> gr{Wd, I, plan, E, abuf, zbuf, ids, (int)(ids ? n_assign : 0)};
+  const DnGroup<WT> gsh{Sd, Is, plan_s, 1, abuf_s, zbuf_s, nullptr, 0};
   const DnGroup<WT> g0 = Sd ? gsh : gr;
   const unsigned n_r = (unsigned)(umax * n_hb), n_sh = Sd ? (unsigned)n_hb : 0u;
   const unsigned n0 = Sd ? n_sh : n_r;
@@ -689,10 +772,13 @@ hipError_t launch_shared_prep(const XT *x, int64_t T, int H, const float *sgw, i
                                             const int32_t *, int, int64_t, int,           \
                                             const float *, float *, hipStream_t,          \
                                             const WT *, const WT *, int, const int32_t *, \
-                                            const float *, float *);                      \
-  template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t, \
+                                            const float *, float *, const int32_t *);     \
+  template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t,  \
                                       const float *, float *, hipStream_t, const WT *, int, \
-                                      const int32_t *, const float *, float *);           \
+                                      const int32_t *, const float *, float *,              \
+                                      const int32_t *);                                     \
+  template bool gateup_takes_ids<WT, XT>(int);                                              \
+  template bool down_takes_ids<WT>(int, int);                                               \
   template hipError_t launch_combine<XT>(const float *, const float *, int64_t, int, int, XT *, \
                                          hipStream_t);                                        \
   template hipError_t launch_shared_prep<XT>(const XT *, int64_t, int, const float *, int32_t *, \

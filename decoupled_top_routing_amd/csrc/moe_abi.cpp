@@ -350,12 +350,16 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   int32_t *ticket = sync + moe::kRouteTicketWord;
   const WT *Sg = static_cast<const WT *>(sh.Sg), *Su = static_cast<const WT *>(sh.Su),
            *Sd = static_cast<const WT *>(sh.Sd);
+  // the launches with a bounded wait inside: the one-token kernel and the
+  // small-batch router + route
+  const bool batch_route = path != Path::Single && !router_bf16 &&
+                           moe::router_route_batch_supported(T, H);
+  if ((path == Path::Single || batch_route) && g_withhold_calls > 0) {
+    --g_withhold_calls;
+    run.withhold_route = true;
+    run.spin_limit = g_withhold_spin;
+  }
   if (path == Path::Single) {
-    if (g_withhold_calls > 0) {
-      --g_withhold_calls;
-      run.withhold_route = true;
-      run.spin_limit = g_withhold_spin;
-    }
     RUN("b1_layer", (moe::launch_decode_b1<WT, XT>(x, H, Wr, router_bf16, br, E, Wg, Wu, Wd, I,
                                                    k1, k2, Sg, Su, Sd, sh.Is, sh.sgw, y,
                                                    logits_out, ids_out, w_out, sync,
@@ -363,7 +367,27 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
                                                    run.spin_limit, run.withhold_route, s)));
     return MOE_OK;
   }
-  if (T == 1 && !router_bf16 && moe::router_route_supported(H)) {
+  // 2..kIdsMax assignments of two or more tokens: no plan; up to
+  // kRouteBatchMax tokens: router and route in one launch
+  const bool by_ids = T >= 2 && n_assign <= moe::kIdsMax && moe::gateup_takes_ids<WT, XT>(H) &&
+                      moe::down_takes_ids<WT>(I, Sg ? sh.Is : 0);
+  if (batch_route) {
+    RUN("router_route", moe::launch_router_route_batch<XT>(x, T, H, Wr32, br, E, k1, k2, logits,
+                                                           logits_out, ids, w, ids_out, w_out,
+                                                           sync, run.spin_limit,
+                                                           run.withhold_route, s));
+    if (!by_ids) RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
+  } else if (by_ids) {
+    if (router_bf16) {
+      if constexpr (sizeof(XT) == 2)
+        RUN("router", moe::launch_router_bf16(x, T, H, static_cast<const moe::bf16_t *>(Wr), E,
+                                              logits, logits_out, s));
+    } else {
+      RUN("router", moe::launch_router<XT>(x, T, H, Wr32, br, E, logits, logits_out, s));
+    }
+    RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
+                                        nullptr, router_bf16, s));
+  } else if (T == 1 && !router_bf16 && moe::router_route_supported(H)) {
     RUN("router_route", moe::launch_router_route<XT>(x, H, Wr32, br, E, k1, k2, logits,
                                                      logits_out, ids, w, ids_out, w_out, plan,
                                                      ticket, s));
@@ -397,7 +421,8 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
     RUN("shared_prep", moe::launch_shared_prep<XT>(x, T, H, sh.sgw, plan_s, nullptr, gs, s));
   }
   RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s,
-                                            Sg, Su, sh.Is, plan_s, gs, abuf_s)));
+                                            Sg, Su, sh.Is, plan_s, gs, abuf_s,
+                                            by_ids ? ids : nullptr)));
   if (ck.dn) {
     uint2 *kept_list = nullptr;
     float *part = nullptr;
@@ -421,7 +446,7 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
     return MOE_OK;
   }
   RUN("down", moe::launch_down<WT>(Wd, H, I, plan, E, n_assign, abuf, zbuf, s, Sd, sh.Is, plan_s,
-                                   abuf_s, zbuf_s));
+                                   abuf_s, zbuf_s, by_ids ? ids : nullptr));
   RUN("combine", moe::launch_combine<XT>(zbuf, zbuf_s, T, H, k1, y, s));
   return MOE_OK;
 }
@@ -440,14 +465,16 @@ bool debug_checks() {
 
 // Wait for the stream, read the error word of the workspace's sync region
 // and reset it: MOE_EDEVICE if a hand-over wait gave up since the last check.
+// A wait that gave up can leave a count of the sync region off zero, so the
+// reset clears every word of the region but the epoch.
 int take_device_status(char *ws, hipStream_t s) {
   int32_t v = 0;
   hipError_t e = hipMemcpyAsync(&v, ws + 4 * moe::kErrorWord, sizeof v, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "read of the device status word");
   if (v == 0) return MOE_OK;
-  const int32_t zero = 0;
-  e = hipMemcpyAsync(ws + 4 * moe::kErrorWord, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+  static const int32_t zeros[moe::kSyncRegionBytes / 4] = {};
+  e = hipMemcpyAsync(ws + 4, zeros, moe::kSyncRegionBytes - 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "reset of the device status word");
   return fail(MOE_EDEVICE,

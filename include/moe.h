@@ -340,25 +340,33 @@ const char *moe_profile_launch_name(void);
 /*
  * moe_workspace_status -- the device status of a workspace.  The one-token
  * kernel's workgroups hand the route and the activations to one another
- * through tagged words of the workspace; every such wait is bounded, and one
- * that gives up (a precondition broken, or a fault elsewhere on the device)
- * lets its kernel run to the end with unspecified outputs and sets an error
- * word in the workspace.  The pages do not cover this (their router runs
- * in the framework's own kernels); it is this library's contract.
+ * through tagged words of the workspace, and the router + route launch of
+ * 2..64 tokens makes its route blocks wait for every token's logits; every
+ * such wait is bounded, and one that gives up (a precondition broken, or a
+ * fault elsewhere on the device) lets its kernel run to the end with
+ * unspecified outputs and sets an error word in the workspace.  The pages do
+ * not cover this (their router runs in the framework's own kernels); it is
+ * this library's contract.
  *
  * Waits for `stream`, reads the error word and resets it: MOE_EDEVICE if a
  * wait gave up in any call on this workspace since the last check, else
- * MOE_OK.  A synchronous host call: not for use under graph capture.
+ * MOE_OK.  With MOE_EDEVICE it also clears the workspace's other
+ * synchronisation counts, which a wait that gave up may have left set.  A
+ * synchronous host call: not for use under graph capture.
  *   workspace  the moe_forward* workspace (256-byte aligned)
  */
 int moe_workspace_status(void *workspace, void *stream);
 
 /*
  * moe_debug_withhold_route -- test hook for the status above.  The next
- * `calls` calls on the calling thread that run the one-token kernel do not
- * publish their route, so every wait for it gives up after `spin_limit`
- * re-reads (>= 1); their kernels still run to the end, reading only in-range
- * expert rows, and their outputs are unspecified.  calls = 0 disarms.
+ * `calls` calls on the calling thread that run a launch with such a wait
+ * (the one-token kernel, or the router + route launch of 2..64 tokens with
+ * an fp32 router weight) withhold their hand-over: the one-token kernel does
+ * not publish its route, and the router + route launch never releases the
+ * blocks that wait for every token's logits.  Every such wait gives up
+ * after `spin_limit` re-reads (>= 1); the kernels still run to the end,
+ * reading only in-range expert rows, and the outputs are unspecified.
+ * calls = 0 disarms.
  */
 int moe_debug_withhold_route(int32_t calls, uint32_t spin_limit);
 

@@ -72,9 +72,12 @@ def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
             y = moe.forward(lay["x"][:T], lay["Wr"], lay["Wg"], lay["Wu"], lay["Wd"], k1, k2,
                             br=lay["br"], flags=fl, workspace=ws)
             torch.cuda.synchronize()
-            words = ws[:16384].view(torch.int32).cpu()
-            # word 0 is the workspace's epoch; every counter and the error
-            # word must be back at zero
+            words = ws[:16384].view(torch.int32).cpu().clone()
+            # word 0 is the workspace's epoch and word 1088 the sense of the
+            # small-batch route barrier (it flips every call, 0 or 1); every
+            # counter and the error word must be back at zero
+            assert int(words[1088]) in (0, 1), name
+            words[1088] = 0
             assert int(words[1:].abs().sum()) == 0, f"sync words left set ({name})"
             yb = y.float().cpu()
             if rep == 0:

@@ -1,11 +1,12 @@
 """The device status word of a workspace (moe_workspace_status).
 
-The one-token kernel's workgroups hand the route over through tagged words;
-every wait is bounded.  The test hook moe_debug_withhold_route keeps a call's
-route from being published, so every wait for it gives up after a few
-re-reads: the kernel still runs to the end (reading only in-range expert
-rows), and the status call must report MOE_EDEVICE once, then reset.
-Calls after it must be exact again.
+The one-token kernel's workgroups hand the route over through tagged words,
+and the router + route launch of 2..64 tokens makes its route blocks wait
+for every token's logits; every wait is bounded.  The test hook
+moe_debug_withhold_route keeps a call's hand-over from happening, so every
+wait for it gives up after a few re-reads: the kernels still run to the end
+(reading only in-range expert rows), and the status call must report
+MOE_EDEVICE once, then reset.  Calls after it must be exact again.
 """
 import os
 import subprocess
@@ -43,21 +44,29 @@ def test_status_is_clear_after_normal_calls(tiny):
     moe.workspace_status(ws)          # raises on MOE_EDEVICE
 
 
-@pytest.mark.parametrize("layer", ["tiny", "a3b"])
-def test_withheld_route_is_reported_once(tiny, layer):
+@pytest.fixture(scope="module")
+def a3b():
+    L = synth.make_layer(synth.DECODE_B1, T=32)
+    return to_dev(L), host_layer(L)
+
+
+# (layer, tokens): one token runs the one-token kernel; 8 and 32 tokens run
+# the router + route launch (8 x 4 assignments without a plan, 32 x 4 with one)
+@pytest.mark.parametrize("layer,T", [("tiny", 1), ("tiny", 8), ("a3b", 1), ("a3b", 8),
+                                     ("a3b", 32)])
+def test_withheld_route_is_reported_once(tiny, a3b, layer, T):
     if layer == "tiny":
         g, Lh = tiny
         cfg, k1, k2 = synth.TINY, 2, 4
     else:
-        L = synth.make_layer(synth.DECODE_B1)
-        g, Lh = to_dev(L), host_layer(L)
+        g, Lh = a3b
         cfg, k1, k2 = synth.DECODE_B1, 4, 16
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
-    x1 = g["x"][:1]
+    x1 = g["x"][:T]
     args = (x1, g["Wr"], g["Wg"], g["Wu"], g["Wd"], k1, k2)
     y0 = moe.forward(*args, br=g["br"], workspace=ws)
     moe.workspace_status(ws)
-    print(f"{cfg.name}: withholding the route of one call", flush=True)
+    print(f"{cfg.name} T={T}: withholding the route of one call", flush=True)
     moe.debug_withhold_route(1, 64)
     moe.forward(*args, br=g["br"], workspace=ws)
     with pytest.raises(moe.MoeError) as ei:
@@ -70,8 +79,8 @@ def test_withheld_route_is_reported_once(tiny, layer):
     assert torch.equal(y0.view(torch.int16) if y0.dtype == torch.bfloat16 else y0,
                        y1.view(torch.int16) if y1.dtype == torch.bfloat16 else y1)
     moe.workspace_status(ws)
-    Lt = dict(g, x=g["x"][:1])
-    Lht = dict(Lh, x=Lh["x"][:1])
+    Lt = dict(g, x=g["x"][:T])
+    Lht = dict(Lh, x=Lh["x"][:T])
     run_and_check(cfg, Lt, Lht, k1, k2)
 
 
