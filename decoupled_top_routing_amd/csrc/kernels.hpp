@@ -23,9 +23,6 @@ constexpr int kErrorWord = 32;
 // re-reads before a hand-over wait gives up (and sets the error word)
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;
 
-hipError_t launch_route(const float *logits, int64_t T, int E, int k1, int k2, int32_t *ids,
-                        float *w, int32_t *ids2, float *w2, hipStream_t s);
-
 template <typename XT>
 hipError_t launch_router(const XT *x, int64_t T, int H, const float *Wr, const float *br, int E,
                          float *logits, float *logits2, hipStream_t s);

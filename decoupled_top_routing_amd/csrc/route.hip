@@ -7,7 +7,7 @@
 //  - section "The Receipt", Eq. 2: w_i = p_i / (sum of the top-k2 p) for the
 //    top-k1 experts; k2 >= E means the weights are the probabilities.
 //
-// One wavefront routes one token (route_device.hpp).  The softmax arithmetic
+// One workgroup routes one token (route_device.hpp).  The softmax arithmetic
 // is pinned down so that the ids and weights are reproducible bit for bit.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -17,19 +17,6 @@
 #pragma clang fp contract(off)
 
 namespace moe {
-
-template <int V>
-__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int64_t T,
-                                                    int E, int k1, int k2,
-                                                    int32_t *__restrict__ ids,
-                                                    float *__restrict__ w,
-                                                    int32_t *__restrict__ ids2,
-                                                    float *__restrict__ w2) {
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  route_token<V>(logits + t * E, E, k1, k2, ids + t * k1, w + t * k1,
-                 ids2 ? ids2 + t * k1 : nullptr, w2 ? w2 + t * k1 : nullptr);
-}
 
 // One workgroup per token.  With `plan`, the last block to finish (ticket)
 // also builds the batch plan (T*k1 <= 64); the ids it reads were stored
@@ -90,22 +77,6 @@ hipError_t launch_route_plan(const float *logits, int64_t T, int E, int k1, int 
     route_plan_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
   else
     route_plan_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2, plan, ticket, wbf16);
-  return hipGetLastError();
-}
-
-hipError_t launch_route(const float *logits, int64_t T, int E, int k1, int k2, int32_t *ids,
-                        float *w, int32_t *ids2, float *w2, hipStream_t s) {
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (E <= 64)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2);
-  else if (E <= 128)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2);
-  else if (E <= 256)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2);
-  else if (E <= 512)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2);
-  else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k1, k2, ids, w, ids2, w2);
   return hipGetLastError();
 }
 

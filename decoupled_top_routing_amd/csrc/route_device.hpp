@@ -50,196 +50,50 @@ __device__ __forceinline__ float exp_nonpos(float d) {
   return __builtin_ldexpf(q, (int)n);
 }
 
-// Route one token with the calling wavefront.  V = values per lane, with
-// 64 * V >= E; lane L holds experts [L*V, L*V + V) ("blocked" layout, so a
-// lower lane always holds lower indices).
-//
+// The route of one token, shared by every route below:
 //  1. m = max of the logits (exact);
 //  2. e = exp_nonpos(l - m), 0 for the padding;
-//  3. S = pairwise sum of e over 64*V slots: a lane-local adjacent-pair tree,
-//     then the pairwise tree over lanes (wave_sum_dpp).  fp32 addition is
-//     commutative, so the lane order inside a node does not matter, and zero
-//     padding of a power-of-two tree leaves its sum unchanged: S equals the
-//     pairwise sum over the next power of two >= E;
+//  3. S = pairwise sum of e over the next power of two >= E (zero padded):
+//     each 64-expert chunk by the wave sum (wave_sum_dpp is the pairwise
+//     tree over the lanes in order), then the pairwise tree over the chunk
+//     sums.  fp32 addition is commutative, so the order inside a node does
+//     not matter, and zero padding leaves a power-of-two tree's sum
+//     unchanged;
 //  4. p = e / S (IEEE division);
 //  5. ranking by (p descending, index ascending) with key = bits of p + 1
-//     (p >= 0, so the bits order like the values; padding has key 0): for
-//     E <= 256 every expert's rank is counted directly, otherwise R rounds
-//     take the largest remaining key (lowest lane, lowest slot on ties).
-//     Only the first R = min(k2, E) ranks are read (k1 when k2 >= E: no mass
-//     needed);
+//     (p >= 0, so the bits order like the values; padding has key 0), packed
+//     with the index so that one unsigned compare orders the experts; only
+//     the first R = min(k2, E) ranks are needed (k1 when k2 >= E: no mass);
 //  6. M = p_(0) + p_(1) + ... left to right over the min(k2, E) ranked values;
 //     w_r = p_(r) / M, or p_(r) when k2 >= E;
 //  7. with wbf16 (the router run on a bf16 model, where the method casts the
 //     weights to the logits' dtype), w_r is then rounded to bf16.
-// Rank r is held by lane r % 64 in slot r / 64 until the end.
-// COHERENT: read the logits with device-coherent loads (they were written by
-// other workgroups of the same kernel).  ids and w may point to LDS.
-template <int V, bool COHERENT = false>
-__device__ void route_token(const float *__restrict__ l, int E, int k1, int k2,
-                            int32_t *__restrict__ ids, float *__restrict__ w,
-                            int32_t *__restrict__ ids2, float *__restrict__ w2,
-                            bool wbf16 = false) {
-#pragma clang fp contract(off)
-  const int lane = lane_id();
-  float ex[V];
-  float lmax = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int e = lane * V + j;
-    float lv = -INFINITY;
-    if (e < E)
-      lv = COHERENT ? __hip_atomic_load(const_cast<float *>(l + e), __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT)
-                    : l[e];
-    ex[j] = lv;
-    lmax = fmaxf(lmax, ex[j]);
-  }
-  const float m = wave_max_dpp(lmax);
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int e = lane * V + j;
-    ex[j] = e < E ? exp_nonpos(ex[j] - m) : 0.0f;
-  }
-  float s[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) s[j] = ex[j];
-#pragma unroll
-  for (int step = 1; step < V; step <<= 1) {
-#pragma unroll
-    for (int j = 0; j + step < V; j += 2 * step) s[j] = s[j] + s[j + step];
-  }
-  // the DPP sum is the pairwise tree over the 64 lanes (see wave_sum_dpp)
-  const float S = wave_sum_dpp(s[0]);
-
-  uint32_t key[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int e = lane * V + j;
-    key[j] = e < E ? __float_as_uint(ex[j] / S) + 1u : 0u;
-  }
-
-  const bool renorm = k2 < E;
-  const int R = renorm ? k2 : k1;
-  float M = 0.0f;
-  int32_t my_id[V];
-  float my_p[V];
-#pragma unroll
-  for (int q = 0; q < V; ++q) {
-    my_id[q] = 0;
-    my_p[q] = 0.0f;
-  }
-  auto keep = [&](int r, int id, float pr) {
-    if (r < k1 && lane == (r & (kWave - 1))) {
-      const int q = r / kWave;
-#pragma unroll
-      for (int qq = 0; qq < V; ++qq)
-        if (qq == q) {
-          my_id[qq] = id;
-          my_p[qq] = pr;
-        }
-    }
-  };
-  if constexpr (V <= 4) {
-    // Rank of each expert = number of experts ahead of it in the order (p
-    // descending, index ascending); keys are distinct, so the ranks are a
-    // permutation.  Each lane counts against every key, broadcast with
-    // readlane: independent instructions instead of a chain of reductions.
-    // key and index packed so one unsigned compare orders by (p desc, index
-    // asc): padding (key 0) sorts after every expert (key >= 1)
-    uint64_t K[V];
-    int rank[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      K[j] = ((uint64_t)key[j] << 11) | (uint64_t)(2047 - (lane * V + j));
-      rank[j] = 0;
-    }
-#pragma unroll 4
-    for (int L = 0; L < kWave; ++L) {
-#pragma unroll
-      for (int s2 = 0; s2 < V; ++s2) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)K[s2], L);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(K[s2] >> 32), L);
-        const uint64_t kk = ((uint64_t)hi << 32) | lo;
-#pragma unroll
-        for (int j = 0; j < V; ++j) rank[j] += kk > K[j] ? 1 : 0;
-      }
-    }
-    // walk the ranks in order: the lane holding rank r hands over its expert
-    for (int r = 0; r < R; ++r) {
-      int sid = -1;
-      uint32_t skey = 0u;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const bool m = rank[j] == r;
-        sid = m ? lane * V + j : sid;
-        skey = m ? key[j] : skey;
-      }
-      const uint64_t mask = __ballot(sid >= 0);
-      const int win = __ffsll((unsigned long long)mask) - 1;
-      const int id = __builtin_amdgcn_readlane(sid, win);
-      const float pr = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)skey, win) - 1u);
-      if (renorm) M = M + pr;
-      keep(r, id, pr);
-    }
-  } else {
-    // R rounds: each lane offers its best untaken expert, the wave takes the
-    // largest key, and the lowest lane holding it wins.
-    for (int r = 0; r < R; ++r) {
-      uint32_t best = 0u;
-      int bj = 0;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        if (key[j] > best) {
-          best = key[j];
-          bj = j;
-        }
-      }
-      const uint32_t kmax = wave_max_u32_dpp(best);
-      const uint64_t mask = __ballot(best == kmax);
-      const int win = __ffsll((unsigned long long)mask) - 1;
-      if (lane == win) {
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-          if (j == bj) key[j] = 0u;
-      }
-      const int id = __builtin_amdgcn_readlane(lane * V + bj, win);
-      const float pr = __uint_as_float(kmax - 1u);
-      if (renorm) M = M + pr;
-      keep(r, id, pr);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < V; ++q) {
-    const int r = q * kWave + lane;
-    if (r < k1) {
-      float wr = renorm ? my_p[q] / M : my_p[q];
-      if (wbf16) wr = round_bf16(wr);
-      ids[r] = my_id[q];
-      w[r] = wr;
-      if (ids2) ids2[r] = my_id[q];
-      if (w2) w2[r] = wr;
-    }
-  }
-}
 
 constexpr int kBlockThreads = 256;
 constexpr int kBlockWaves = kBlockThreads / kWave;
 
-// One token (E <= 256) routed by the whole block, with the arithmetic of
-// route_token: exact max; e = exp_nonpos(l - max); S = the pairwise tree
-// (each wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
+// One token (E <= 256) routed by the whole block, with the arithmetic
+// above: exact max; e = exp_nonpos(l - max); S = the pairwise tree (each
+// wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
 // (p descending, index ascending) counted in parallel (element e by
 // min(256 / P, P) threads, P = next_pow2(E), each over a slice of the keys);
 // the mass summed in rank order by one thread; w = p / M or p, rounded to
 // bf16 with wbf16.
 
 struct BlockRoute {
-  alignas(16) uint64_t K[kBlockThreads];
-  int32_t rank[kBlockThreads];
-  float sp[kBlockThreads];
-  int32_t sid[kBlockThreads];
+  union {
+    struct {
+      alignas(16) uint64_t K[kBlockThreads];
+      int32_t rank[kBlockThreads];
+      float sp[kBlockThreads];
+      int32_t sid[kBlockThreads];
+    };
+    alignas(16) uint64_t KL[kMaxExperts];  // E > 256: keys of the selected experts
+  };
+  uint32_t key[kMaxExperts];  // E > 256: every expert's key
   float red[kBlockWaves];
+  float chunk[kMaxExperts / kWave];
+  int32_t n;
   float M;
 };
 
@@ -374,6 +228,142 @@ __device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t
   __syncthreads();
 }
 
+// One token (256 < E <= 1024) routed by the whole block, with the
+// arithmetic above: exact max; e = exp_nonpos(l - max); S = the pairwise
+// tree (each 64-expert chunk by the wave sum, then the tree over
+// the 16 chunk sums, zero past E); p = e / S; key = bits of p + 1.  The
+// selection costs the same for every k2: the first wave finds the top
+// kTauBits bits of the R-th largest key (R = min(k2, E), or k1 when k2 >=
+// E) bit by bit from the top, each step one count of the keys at or above a
+// candidate (V keys per lane, one ballot each, no barrier).  Every key at or
+// above that prefix is a candidate (at least R of them, the R largest among
+// them); only the candidates are ranked (by (p descending, index
+// ascending), counted against each other), and the mass summed in rank order
+// by one thread.  Candidates beyond R are keys within a factor 1 + 2^-5 of
+// the R-th largest: few, unless many probabilities (nearly) tie, which costs
+// time and not exactness.
+// ids and w (LDS, kMaxExperts entries) receive the R selected in rank order,
+// w first holding p; on return ids[0..k1) and w[0..k1) hold the route.
+// V = 64-expert chunks the first wave holds (64 V >= E).
+constexpr int kTauBits = 12;
+
+template <int V>
+__device__ void route_token_block_large(const float *l, int E, int k1, int k2, int32_t *ids,
+                                        float *w, BlockRoute &S, bool wbf16 = false) {
+#pragma clang fp contract(off)
+  constexpr int J = kMaxExperts / kBlockThreads;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  // thread t holds experts t, t + 256, t + 512, t + 768
+  float lv[J];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = j * kBlockThreads + tid;
+    lv[j] = e < E ? l[e] : -INFINITY;
+    tmax = fmaxf(tmax, lv[j]);
+  }
+  const float wm = wave_max_dpp(tmax);
+  if (lane == 0) S.red[wv] = wm;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]));
+  float ex[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = j * kBlockThreads + tid;
+    ex[j] = e < E ? exp_nonpos(lv[j] - m) : 0.0f;
+    // chunk 4j + wv is experts [64 (4j + wv), +64), one per lane in order
+    const float cs = wave_sum_dpp(ex[j]);
+    if (lane == 0) S.chunk[j * kBlockWaves + wv] = cs;
+  }
+  __syncthreads();
+  float c8[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) c8[q] = S.chunk[2 * q] + S.chunk[2 * q + 1];
+  const float sum = ((c8[0] + c8[1]) + (c8[2] + c8[3])) + ((c8[4] + c8[5]) + (c8[6] + c8[7]));
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = j * kBlockThreads + tid;
+    S.key[e] = e < E ? __float_as_uint(ex[j] / sum) + 1u : 0u;
+  }
+  __syncthreads();
+  const bool renorm = k2 < E;
+  const int R = renorm ? k2 : k1;
+  if (wv == 0) {
+    // the first wave holds expert q * 64 + lane in key[q]
+    uint32_t key[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) key[q] = S.key[q * kWave + lane];
+    // all V compares are issued before the first scalar popcount reads a
+    // result (interleaved, each popcount stalled the wave on its compare)
+    auto count_ge = [&](uint32_t c) {
+      uint64_t bal[V];
+#pragma unroll
+      for (int q = 0; q < V; ++q) bal[q] = __ballot(key[q] >= c);
+      __builtin_amdgcn_sched_barrier(0);
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < V; ++q) n += __popcll(bal[q]);
+      return n;
+    };
+    // keys are at most bits(1.0f) + 1 < 2^30: the top kTauBits bits of the
+    // R-th largest key, from the top
+    uint32_t tau = 0u;
+    for (int b = 29; b >= 30 - kTauBits; --b) {
+      const uint32_t c = tau | (1u << b);
+      if (count_ge(c) >= R) tau = c;
+    }
+    // the candidates: every key >= tau (at least R of them, every one of
+    // the R largest among them)
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pos = 0;
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const bool cand = key[q] >= tau;
+      const uint64_t cm = __ballot(cand);
+      if (cand)
+        S.KL[pos + __popcll(cm & below)] =
+            ((uint64_t)key[q] << 11) | (uint64_t)(2047 - (q * kWave + lane));
+      pos += __popcll(cm);
+    }
+    if (lane == 0) S.n = pos;
+  }
+  __syncthreads();
+  // rank the candidates against each other; the first R ranks are the route
+  const int nc = S.n;
+  for (int i = tid; i < nc; i += kBlockThreads) {
+    const uint64_t Ki = S.KL[i];
+    int r = 0;
+    for (int q = 0; q < nc; ++q) r += S.KL[q] > Ki ? 1 : 0;
+    if (r < R) {
+      w[r] = __uint_as_float((uint32_t)(Ki >> 11) - 1u);
+      ids[r] = 2047 - (int)(Ki & 2047u);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = 0.0f;
+    if (renorm) {
+      int r = 0;
+      for (; r + 8 <= R; r += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = w[r + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) M = M + v[q];
+      }
+      for (; r < R; ++r) M = M + w[r];
+    }
+    S.M = M;
+  }
+  __syncthreads();
+  for (int r = tid; r < k1; r += kBlockThreads) {
+    float wr = renorm ? w[r] / S.M : w[r];
+    if (wbf16) wr = round_bf16(wr);
+    w[r] = wr;
+  }
+  __syncthreads();
+}
+
 // Every store of this block is complete (s_waitcnt), then thread 0 takes a
 // ticket; true in the whole block that takes the last of n tickets, which
 // also puts the ticket word back to zero.
@@ -421,21 +411,17 @@ __device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
   }
 }
 
-// Route one token into LDS (s_ids, s_w: rank order), by the whole block
-// (E <= 256, k1 <= 256) or by its first wave; wbf16 rounds the weights to
-// bf16.
+// Route one token into LDS (s_ids, s_w: rank order, kMaxExperts entries
+// each) with the whole block; wbf16 rounds the weights to bf16.  V = E / 64
+// rounded up to a power of two: V <= 4 is the direct rank count, V = 8 and
+// 16 the selection whose cost does not depend on k2.
 template <int V>
 __device__ void route_into_lds(const float *l, int E, int k1, int k2, int32_t *s_ids, float *s_w,
                                BlockRoute &S, bool wbf16 = false) {
-  // V = 8 and 16 serve E > 256 only, so their kernels carry no block route
-  if constexpr (V * kWave <= kBlockThreads) {
-    if (E <= kBlockThreads && k1 <= kBlockThreads) {
-      route_token_block<(V <= 2)>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
-      return;
-    }
-  }
-  if (threadIdx.x < kWave) route_token<V>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, wbf16);
-  __syncthreads();
+  if constexpr (V * kWave <= kBlockThreads)
+    route_token_block<(V <= 2)>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
+  else
+    route_token_block_large<V>(l, E, k1, k2, s_ids, s_w, S, wbf16);
 }
 
 }  // namespace moe

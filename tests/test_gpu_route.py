@@ -51,11 +51,11 @@ def test_route_ties_and_near_ties():
     """Tied probabilities resolve to the lower index; quantised logits make
     many exact ties, including across the k1 and k2 boundaries."""
     rng = np.random.default_rng(5)
-    for E in (16, 128, 512):
+    for E in (16, 128, 512, 1024):
         l = np.round(rng.standard_normal((512, E)) * 2).astype(np.float32)
         l[:64] = 0.0                                    # all equal
         l[64:128, ::2] = 1.0                            # half tied at the top
-        for k1, k2 in ((1, 1), (2, 4), (4, 16), (8, 8), (5, 20)):
+        for k1, k2 in ((1, 1), (2, 4), (4, 16), (8, 8), (5, 20), (70, 80), (3, 1000)):
             if k2 <= E:
                 ids, w = run(l, k1, k2)
                 check_route_exact(ids, w, l, k1, k2, f"ties E={E}")
