@@ -72,179 +72,58 @@ __device__ __forceinline__ float exp_nonpos(float d) {
 constexpr int kBlockThreads = 256;
 constexpr int kBlockWaves = kBlockThreads / kWave;
 
-// One token (E <= 256) routed by the whole block, with the arithmetic
-// above: exact max; e = exp_nonpos(l - max); S = the pairwise tree (each
-// wave's 64 experts, then (w0 + w1) + (w2 + w3)); p = e / S; ranks by
-// (p descending, index ascending) counted in parallel (element e by
-// min(256 / P, P) threads, P = next_pow2(E), each over a slice of the keys);
-// the mass summed in rank order by one thread; w = p / M or p, rounded to
-// bf16 with wbf16.
-
+// LDS of a block route.
 struct BlockRoute {
-  union {
-    struct {
-      alignas(16) uint64_t K[kBlockThreads];
-      int32_t rank[kBlockThreads];
-      float sp[kBlockThreads];
-      int32_t sid[kBlockThreads];
-    };
-    alignas(16) uint64_t KL[kMaxExperts];  // E > 256: keys of the selected experts
-  };
-  uint32_t key[kMaxExperts];  // E > 256: every expert's key
+  alignas(16) uint64_t KL[kMaxExperts];  // the candidates' packed keys
+  uint32_t key[kMaxExperts];             // E > 256: every expert's key
   float red[kBlockWaves];
   float chunk[kMaxExperts / kWave];
   int32_t n;
   float M;
 };
 
-// Rank counting over keys in LDS (16-byte aligned, read at the same address
-// by every lane, so each read is a broadcast).  With kBatch16 the reads go in
-// batches of 16 keys issued together, one LDS round trip per batch instead
-// of one per 8 keys; each batch keeps 16 compare masks live in scalar
-// registers, so it is used only where the kernel has them to spare (a spill
-// to scratch on this path costs more than the batching saves).
-__device__ __forceinline__ void load16(const uint64_t *K, ulonglong2 (&q)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = *reinterpret_cast<const ulonglong2 *>(K + 2 * i);
-}
-__device__ __forceinline__ int above16(const ulonglong2 (&q)[8], uint64_t Ke) {
-  int c0 = 0, c1 = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    c0 += (q[i].x > Ke) + (q[i].y > Ke);
-    c1 += (q[i + 1].x > Ke) + (q[i + 1].y > Ke);
-  }
-  return c0 + c1;
-}
-// How many of the n keys at K exceed Ke (n a multiple of 8, or 16 with
-// kBatch16).
-template <bool kBatch16>
-__device__ __forceinline__ int count_above(const uint64_t *K, int n, uint64_t Ke) {
-  int c = 0;
-  if constexpr (kBatch16) {
-#pragma unroll 1
-    for (int j = 0; j < n; j += 16) {
-      ulonglong2 q[8];
-      load16(K + j, q);
-      c += above16(q, Ke);
-    }
-  } else {
-    int c1 = 0;
-    for (int j = 0; j < n; j += 8) {
-      const ulonglong2 q0 = *reinterpret_cast<const ulonglong2 *>(K + j);
-      const ulonglong2 q1 = *reinterpret_cast<const ulonglong2 *>(K + j + 2);
-      const ulonglong2 q2 = *reinterpret_cast<const ulonglong2 *>(K + j + 4);
-      const ulonglong2 q3 = *reinterpret_cast<const ulonglong2 *>(K + j + 6);
-      c += (q0.x > Ke) + (q0.y > Ke) + (q1.x > Ke) + (q1.y > Ke);
-      c1 += (q2.x > Ke) + (q2.y > Ke) + (q3.x > Ke) + (q3.y > Ke);
-    }
-    c += c1;
-  }
-  return c;
-}
-
-template <bool kBatch16 = false>
-__device__ void route_token_block(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
-                                  int32_t *ids_out, float *w_out, BlockRoute &S,
-                                  bool wbf16 = false) {
+// The route from nc candidates in S.KL (packed keys, the R largest among
+// them) by the whole block: each candidate's rank counted against the
+// others, the first R ranks stored (w holding p), the mass summed in rank
+// order by thread 0, then w = p / M (or p), rounded to bf16 with wbf16.
+__device__ __forceinline__ void block_rank(BlockRoute &S, int nc, int R, int k1, bool renorm,
+                                           bool wbf16, int32_t *ids, float *w) {
 #pragma clang fp contract(off)
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const bool valid = tid < E;
-  const float lv = valid ? l[tid] : -INFINITY;
-  const float wm = wave_max_dpp(lv);
-  if (lane == 0) S.red[wv] = wm;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]));
-  const float ex = valid ? exp_nonpos(lv - m) : 0.0f;
-  const float ws = wave_sum_dpp(ex);
-  __syncthreads();
-  if (lane == 0) S.red[wv] = ws;
-  __syncthreads();
-  const float sum = (S.red[0] + S.red[1]) + (S.red[2] + S.red[3]);
-  const float p = ex / sum;
-  const uint32_t key = valid ? __float_as_uint(p) + 1u : 0u;
-  S.K[tid] = ((uint64_t)key << 11) | (uint64_t)(2047 - tid);
-  S.rank[tid] = 0;
-  __syncthreads();
-  int epow = 1, lg = 0;
-  while (epow < E) {
-    epow <<= 1;
-    ++lg;
-  }
-  // element e is ranked by `split` threads, each over `chunk` keys of the
-  // padded key array (keys past E are below every valid key, so they never
-  // count)
-  const int split = min(kBlockThreads / epow, epow);
-  const int e = tid & (epow - 1), part = tid >> lg;
-  const int chunk = epow / split;
-  if (e < E && part < split) {
-    const uint64_t Ke = S.K[e];
-    const uint64_t *Kp = S.K + part * chunk;
-    int cnt;
-    if (chunk >= 16) {
-      cnt = count_above<kBatch16>(Kp, chunk, Ke);
-    } else {
-      cnt = 0;
-      for (int j = 0; j < chunk; ++j) cnt += Kp[j] > Ke ? 1 : 0;
-    }
-    if (cnt) atomicAdd(&S.rank[e], cnt);
-  }
-  __syncthreads();
-  const bool renorm = k2 < E;
-  const int R = renorm ? k2 : k1;
-  if (valid) {
-    const int r = S.rank[tid];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nc; i += kBlockThreads) {
+    const uint64_t Ki = S.KL[i];
+    int r = 0;
+    for (int q = 0; q < nc; ++q) r += S.KL[q] > Ki ? 1 : 0;
     if (r < R) {
-      S.sp[r] = p;
-      S.sid[r] = tid;
+      w[r] = __uint_as_float((uint32_t)(Ki >> 11) - 1u);
+      ids[r] = 2047 - (int)(Ki & 2047u);
     }
   }
   __syncthreads();
   if (tid == 0) {
-    // left to right in rank order; the loads run ahead of the adds
     float M = 0.0f;
     if (renorm) {
       int r = 0;
       for (; r + 8 <= R; r += 8) {
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = S.sp[r + q];
+        for (int q = 0; q < 8; ++q) v[q] = w[r + q];
 #pragma unroll
         for (int q = 0; q < 8; ++q) M = M + v[q];
       }
-      for (; r < R; ++r) M = M + S.sp[r];
+      for (; r < R; ++r) M = M + w[r];
     }
     S.M = M;
   }
   __syncthreads();
-  if (tid < k1) {
-    float wr = renorm ? S.sp[tid] / S.M : S.sp[tid];
+  for (int r = tid; r < k1; r += kBlockThreads) {
+    float wr = renorm ? w[r] / S.M : w[r];
     if (wbf16) wr = round_bf16(wr);
-    ids[tid] = S.sid[tid];
-    w[tid] = wr;
-    if (ids_out) ids_out[tid] = S.sid[tid];
-    if (w_out) w_out[tid] = wr;
+    w[r] = wr;
   }
   __syncthreads();
 }
 
-// One token (256 < E <= 1024) routed by the whole block, with the
-// arithmetic above: exact max; e = exp_nonpos(l - max); S = the pairwise
-// tree (each 64-expert chunk by the wave sum, then the tree over
-// the 16 chunk sums, zero past E); p = e / S; key = bits of p + 1.  The
-// selection costs the same for every k2: the first wave finds the top
-// kTauBits bits of the R-th largest key (R = min(k2, E), or k1 when k2 >=
-// E) bit by bit from the top, each step one count of the keys at or above a
-// candidate (V keys per lane, one ballot each, no barrier).  Every key at or
-// above that prefix is a candidate (at least R of them, the R largest among
-// them); only the candidates are ranked (by (p descending, index
-// ascending), counted against each other), and the mass summed in rank order
-// by one thread.  Candidates beyond R are keys within a factor 1 + 2^-5 of
-// the R-th largest: few, unless many probabilities (nearly) tie, which costs
-// time and not exactness.
-// ids and w (LDS, kMaxExperts entries) receive the R selected in rank order,
-// w first holding p; on return ids[0..k1) and w[0..k1) hold the route.
-// V = 64-expert chunks the first wave holds (64 V >= E).
 constexpr int kTauBits = 12;
 
 template <int V>
@@ -328,40 +207,7 @@ __device__ void route_token_block_large(const float *l, int E, int k1, int k2, i
     if (lane == 0) S.n = pos;
   }
   __syncthreads();
-  // rank the candidates against each other; the first R ranks are the route
-  const int nc = S.n;
-  for (int i = tid; i < nc; i += kBlockThreads) {
-    const uint64_t Ki = S.KL[i];
-    int r = 0;
-    for (int q = 0; q < nc; ++q) r += S.KL[q] > Ki ? 1 : 0;
-    if (r < R) {
-      w[r] = __uint_as_float((uint32_t)(Ki >> 11) - 1u);
-      ids[r] = 2047 - (int)(Ki & 2047u);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float M = 0.0f;
-    if (renorm) {
-      int r = 0;
-      for (; r + 8 <= R; r += 8) {
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = w[r + q];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) M = M + v[q];
-      }
-      for (; r < R; ++r) M = M + w[r];
-    }
-    S.M = M;
-  }
-  __syncthreads();
-  for (int r = tid; r < k1; r += kBlockThreads) {
-    float wr = renorm ? w[r] / S.M : w[r];
-    if (wbf16) wr = round_bf16(wr);
-    w[r] = wr;
-  }
-  __syncthreads();
+  block_rank(S, S.n, R, k1, renorm, wbf16, ids, w);
 }
 
 // Every store of this block is complete (s_waitcnt), then thread 0 takes a
@@ -411,17 +257,135 @@ __device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
   }
 }
 
+// One token (E <= 256) routed by one wave, with the arithmetic above: lane
+// L holds experts q * 64 + L in slot q < V (index order (q, L), so a
+// ballot's lower lanes are the lower indices); exact max; e =
+// exp_nonpos(l - max); S = the pairwise tree (each chunk q by the wave sum,
+// then the tree over the V chunk sums); p = e / S.  The selection is that of
+// route_token_block_large: the top kTauBits bits of the R-th largest key,
+// the candidates at or above them ranked against each other, the mass
+// summed in rank order.  With at most 64 candidates the wave ranks them
+// itself (one per lane) and ids and w (LDS, kMaxExperts entries) receive the
+// route in rank order, with no barrier (the wave's LDS accesses are ordered
+// by waiting for them); with more, the candidates stay in S.KL for
+// block_rank.  Returns the number of candidates (in every lane).
+template <int V>
+__device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
+                                BlockRoute &S, bool wbf16 = false) {
+#pragma clang fp contract(off)
+  const int lane = lane_id();
+  float ex[V];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    const int e = q * kWave + lane;
+    ex[q] = e < E ? l[e] : -INFINITY;
+    tmax = fmaxf(tmax, ex[q]);
+  }
+  const float m = wave_max_dpp(tmax);
+  float cs[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    const int e = q * kWave + lane;
+    ex[q] = e < E ? exp_nonpos(ex[q] - m) : 0.0f;
+    cs[q] = wave_sum_dpp(ex[q]);
+  }
+#pragma unroll
+  for (int step = 1; step < V; step <<= 1)
+#pragma unroll
+    for (int q = 0; q + step < V; q += 2 * step) cs[q] = cs[q] + cs[q + step];
+  const float sum = cs[0];
+  uint32_t key[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    const int e = q * kWave + lane;
+    key[q] = e < E ? __float_as_uint(ex[q] / sum) + 1u : 0u;
+  }
+  const bool renorm = k2 < E;
+  const int R = renorm ? k2 : k1;
+  auto count_ge = [&](uint32_t c) {
+    uint64_t bal[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) bal[q] = __ballot(key[q] >= c);
+    __builtin_amdgcn_sched_barrier(0);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < V; ++q) n += __popcll(bal[q]);
+    return n;
+  };
+  uint32_t tau = 0u;
+  for (int b = 29; b >= 30 - kTauBits; --b) {
+    const uint32_t c = tau | (1u << b);
+    if (count_ge(c) >= R) tau = c;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nc = 0;
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    const bool cand = key[q] >= tau;
+    const uint64_t cm = __ballot(cand);
+    if (cand)
+      S.KL[nc + __popcll(cm & below)] =
+          ((uint64_t)key[q] << 11) | (uint64_t)(2047 - (q * kWave + lane));
+    nc += __popcll(cm);
+  }
+  if (lane == 0) S.n = nc;
+  if (nc > kWave) return nc;  // ranked by the block
+  // lane i ranks candidate i against the others (LDS reads at one address
+  // for the whole wave)
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < nc) {
+    const uint64_t Ki = S.KL[lane];
+    int r = 0;
+    for (int q = 0; q < nc; ++q) r += S.KL[q] > Ki ? 1 : 0;
+    if (r < R) {
+      w[r] = __uint_as_float((uint32_t)(Ki >> 11) - 1u);
+      ids[r] = 2047 - (int)(Ki & 2047u);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  float M = 0.0f;
+  if (renorm) {
+    // every lane sums the same values in the same order
+    int q = 0;
+    for (; q + 8 <= R; q += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = w[q + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = M + v[u];
+    }
+    for (; q < R; ++q) M = M + w[q];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  for (int q = lane; q < k1; q += kWave) {
+    float wr = renorm ? w[q] / M : w[q];
+    if (wbf16) wr = round_bf16(wr);
+    w[q] = wr;
+  }
+  return nc;
+}
+
 // Route one token into LDS (s_ids, s_w: rank order, kMaxExperts entries
 // each) with the whole block; wbf16 rounds the weights to bf16.  V = E / 64
-// rounded up to a power of two: V <= 4 is the direct rank count, V = 8 and
-// 16 the selection whose cost does not depend on k2.
+// rounded up to a power of two: V <= 4 routes in one wave, V = 8 and 16 with
+// the block.
 template <int V>
 __device__ void route_into_lds(const float *l, int E, int k1, int k2, int32_t *s_ids, float *s_w,
                                BlockRoute &S, bool wbf16 = false) {
-  if constexpr (V * kWave <= kBlockThreads)
-    route_token_block<(V <= 2)>(l, E, k1, k2, s_ids, s_w, nullptr, nullptr, S, wbf16);
-  else
+  if constexpr (V * kWave <= kBlockThreads) {
+    if (threadIdx.x < kWave) route_token_wave<V>(l, E, k1, k2, s_ids, s_w, S, wbf16);
+    __syncthreads();
+    if (S.n > kWave) {
+      const bool renorm = k2 < E;
+      block_rank(S, S.n, renorm ? k2 : k1, k1, renorm, wbf16, s_ids, s_w);
+    }
+  } else {
     route_token_block_large<V>(l, E, k1, k2, s_ids, s_w, S, wbf16);
+  }
 }
 
 }  // namespace moe
