@@ -67,6 +67,24 @@ struct Loader {
 #pragma unroll
     for (int j = 0; j < NB; ++j) *reinterpret_cast<uint4 *>(&T.b[buf][row(j)][q]) = rb[j];
   }
+  // the same through an explicit register stage (several slices in flight)
+  struct Stage {
+    uint4 a[NA], b[NB];
+  };
+  __device__ void fetch(int k0, Stage &r) const {
+    const int q = (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) r.a[i] = ld16(arow[i] + k0 + q);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) r.b[j] = ld16_stream(brow[j] + k0 + q);
+  }
+  __device__ static void store(Tile<BM, BN> &T, int buf, const Stage &r) {
+    const int q = (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4 *>(&T.a[buf][row(i)][q]) = r.a[i];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) *reinterpret_cast<uint4 *>(&T.b[buf][row(j)][q]) = r.b[j];
+  }
 };
 
 // acc[i][j] += A(wave rows i) * B(wave cols j)^T over one K slice in LDS;
@@ -110,6 +128,53 @@ __device__ void mma_k_loop(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm, i
     if (kk + 1 < nk) ld.store(T, buf ^ 1);
     __syncthreads();
   }
+}
+
+// The K loop for a K known at compile time (NK slices), fully unrolled: the
+// slices stream through a ring of kStages register stages into the two LDS
+// buffers, so that while slice k is multiplied out of LDS the loads of
+// slices k+1 .. k+kStages are in flight, and slice k+1 is written to the
+// other buffer once it has arrived.  Unrolled, every wait for a stage's
+// loads leaves the younger stages' loads outstanding (in a rolled loop the
+// compiler waited for every load at each store, which left one slice in
+// flight whatever the ring).
+constexpr int kStages = 3;
+
+template <int BM, int BN, int NK>
+__device__ __forceinline__ void mma_k_loop_fixed(Tile<BM, BN> &T, Loader<BM, BN> &ld, int wm,
+                                                 int wn, f32x16_t (&acc)[BM / 64][BN / 64]) {
+  using Stage = typename Loader<BM, BN>::Stage;
+  Stage ring[kStages];
+#pragma unroll
+  for (int q = 0; q < kStages; ++q)
+    if (q < NK) ld.fetch(q * BK, ring[q]);
+  Loader<BM, BN>::store(T, 0, ring[0]);
+  if (kStages < NK) ld.fetch(kStages * BK, ring[0]);
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    mma_slice<BM, BN>(T, kk & 1, wm, wn, acc);
+    if (kk + 1 < NK) Loader<BM, BN>::store(T, (kk + 1) & 1, ring[(kk + 1) % kStages]);
+    if (kk + 1 + kStages < NK) ld.fetch((kk + 1 + kStages) * BK, ring[(kk + 1) % kStages]);
+    __syncthreads();
+  }
+}
+
+// K loop of the expert GEMMs: NK > 0 slices unrolled, NK = 0 the
+// double-buffered loop over any K (a kernel instantiation per NK keeps each
+// one's registers to itself).
+template <int NK, int BM, int BN>
+__device__ __forceinline__ void mma_k_any(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm,
+                                          int wn, f32x16_t (&acc)[BM / 64][BN / 64]) {
+  if constexpr (NK > 0)
+    mma_k_loop_fixed<BM, BN, NK>(T, ld, wm, wn, acc);
+  else
+    mma_k_loop<BM, BN>(T, ld, K, wm, wn, acc);
+}
+
+// the K of the measured layers get an unrolled loop
+__host__ __device__ constexpr int unrolled_nk(int K) {
+  return (K == 768 || K == 1024 || K == 2048 || K == 4096) ? K / BK : 0;
 }
 
 template <int MI, int NI>
@@ -267,7 +332,8 @@ __device__ bool tile_of(int b, const int32_t *mt_off, int U, int n_mt, int NT, i
 // and up: rows [64g, 64g+32) = Wg[e, c0+32g ..], rows [64g+32, 64g+64) =
 // Wu[e, c0+32g ..]; wave (wm, wn) then holds the gate and the up value of
 // the same (row, channel) in acc[i][0] and acc[i][1] of the same lane.
-__global__ __launch_bounds__(kThreads) void gateup_mma_kernel(
+template <int NK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mma_kernel(
     const uint16_t *__restrict__ x, int H, const uint16_t *__restrict__ Wg,
     const uint16_t *__restrict__ Wu, int I, const int32_t *__restrict__ plan, int E, int k1,
     const float *__restrict__ w, uint16_t *__restrict__ abf) {
@@ -299,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void gateup_mma_kernel(
   }
   f32x16_t acc[2][2];
   zero_acc(acc);
-  mma_k_loop<GM, GN>(T, ld, H, wm, wn, acc);
+  mma_k_any<NK, GM, GN>(T, ld, H, wm, wn, acc);
   const int c = c0 + wn * 32 + (lane_id() & 31);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -318,7 +384,8 @@ __global__ __launch_bounds__(kThreads) void gateup_mma_kernel(
 // Tile (M tile of expert u, 128 output rows h0..h0+127 of H):
 // z[asg, h] = a[asg, :] . Wd[e, h, :], stored as bf16 (the layer's output is
 // bf16; partials in bf16 halve the traffic of the slot combine).
-__global__ __launch_bounds__(kThreads) void down_mma_kernel(
+template <int NK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mma_kernel(
     const uint16_t *__restrict__ abf, int H, const uint16_t *__restrict__ Wd, int I,
     const int32_t *__restrict__ plan, int E, uint16_t *__restrict__ zbf) {
   __shared__ Tile<GM, GN> T;
@@ -345,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void down_mma_kernel(
     ld.brow[j] = Wd + ((int64_t)e * H + h0 + Loader<GM, GN>::row(j)) * I;
   f32x16_t acc[2][2];
   zero_acc(acc);
-  mma_k_loop<GM, GN>(T, ld, I, wm, wn, acc);
+  mma_k_any<NK, GM, GN>(T, ld, I, wm, wn, acc);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -506,15 +573,28 @@ hipError_t launch_gateup_mma(const uint16_t *x, int H, const uint16_t *Wg, const
                              int I, const int32_t *plan, int E, int64_t n, int k1, const float *w,
                              uint16_t *abf, hipStream_t s) {
   const unsigned grid = grouped_grid(max_mtiles(n, E) * (I / 64));
-  pf::gateup_mma_kernel<<<dim3(grid), dim3(pf::kThreads), 0, s>>>(x, H, Wg, Wu, I, plan, E, k1, w,
-                                                                  abf);
+#define GU(NK) pf::gateup_mma_kernel<NK><<<dim3(grid), dim3(pf::kThreads), 0, s>>>( \
+    x, H, Wg, Wu, I, plan, E, k1, w, abf)
+  switch (pf::unrolled_nk(H)) {
+    case 2048 / pf::BK: GU(2048 / pf::BK); break;
+    case 4096 / pf::BK: GU(4096 / pf::BK); break;
+    default: GU(0);
+  }
+#undef GU
   return hipGetLastError();
 }
 
 hipError_t launch_down_mma(const uint16_t *abf, int H, const uint16_t *Wd, int I,
                            const int32_t *plan, int E, int64_t n, uint16_t *zbf, hipStream_t s) {
   const unsigned grid = grouped_grid(max_mtiles(n, E) * (H / pf::GN));
-  pf::down_mma_kernel<<<dim3(grid), dim3(pf::kThreads), 0, s>>>(abf, H, Wd, I, plan, E, zbf);
+#define DN(NK) pf::down_mma_kernel<NK><<<dim3(grid), dim3(pf::kThreads), 0, s>>>( \
+    abf, H, Wd, I, plan, E, zbf)
+  switch (pf::unrolled_nk(I)) {
+    case 768 / pf::BK: DN(768 / pf::BK); break;
+    case 1024 / pf::BK: DN(1024 / pf::BK); break;
+    default: DN(0);
+  }
+#undef DN
   return hipGetLastError();
 }
 
