@@ -18,10 +18,7 @@
 //  combine_kernel: y[t,h] = sum of z[t,r,h] over the token's slots, in order.
 //
 // Batches of at most kIdsMax assignments skip the plan: every gate/up and
-// down block reads the batch's ids and finds its own expert and assignments,
-// and the down launch also does the combine (the block that completes a
-// block of output rows sums them), so such a batch runs as two launches
-// after the route.
+// down block reads the batch's ids and finds its own expert and assignments.
 #include <type_traits>
 
 #include "common.hpp"
@@ -694,9 +691,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= T * H) return;
   const int64_t t = i / H, h = i - t * H;
+  // eight slots' loads in flight at once, summed in slot order
+  constexpr int kU = 8;
+  const float *zt = zbuf + t * k1 * H + h;
+  const float sh = zs ? zs[i] : 0.0f;
   float s = 0.0f;
-  for (int r = 0; r < k1; ++r) s = s + zbuf[(t * k1 + r) * H + h];
-  if (zs) s = s + zs[i];
+  for (int r0 = 0; r0 < k1; r0 += kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = r0 + u < k1 ? zt[(int64_t)(r0 + u) * H] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (r0 + u < k1) s = s + v[u];
+  }
+  if (zs) s = s + sh;
   Elem<XT>::store1(y + i, s);
 }
 
