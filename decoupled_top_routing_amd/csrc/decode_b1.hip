@@ -12,33 +12,34 @@
 // deadlock whatever the occupancy):
 //   R   [0, n_r)          wave e computes logit e and publishes it as a
 //                         tagged word (sync.hpp);
-//   P   n_r               stages the E tagged logits, routes the token, sets
-//                         the activated experts' completion counters to
-//                         (tag, 0) and publishes (expert, weight) of the
-//                         activated experts, ascending by expert, in kRepP
-//                         copies;
+//   P   n_r               sets the activated experts' completion counters to
+//                         (tag, 0), stages the E tagged logits and routes the
+//                         token; it publishes the activated experts,
+//                         ascending by expert, in kRepP copies as soon as
+//                         the top-k1 set is known (one wave, E <= 256), then
+//                         their Eq. 2 weights once the top-k2 mass is
+//                         summed;
 //   GU  [.., +(k1+m)*n_cb) (expert u, block of channels): the first m*n_cb
 //                         blocks are the shared expert's, its Is = m*I
 //                         channels as m pieces u = k1..k1+m-1 of I channels
 //                         (each channel owns a gate row, an up row and a down
 //                         column, so the pieces add up to the whole); they
 //                         need no route and stream while it is computed.
-//                         A routed block waits for the two words of its u.
+//                         A routed block waits for the expert of its u.
 //                         Each streams the gate and up rows once, stores
-//                         a[u, c] = silu(g) * up * w_u (w_u: the Eq. 2
-//                         weight, or the shared gate factor) device-
-//                         coherently, then adds 1 to u's counter (a shared
-//                         block first waits for the route, which is
-//                         published after the counters are set); the block
-//                         that completes the count publishes "u complete" in
-//                         every copy;
+//                         a[u, c] = silu(g) * up (times the gate factor for
+//                         a shared piece) device-coherently, then adds 1 to
+//                         u's counter (a shared block first waits for the
+//                         route, which is published after the counters are
+//                         set); the block that completes the count
+//                         publishes "u complete" in every copy;
 //   D   [.., +n_d)        (block of four output rows): marks itself started,
-//                         waits for the route, issues the down rows of the
-//                         activated experts and shared pieces (they stream
-//                         while gate/up runs), waits until every one is
-//                         complete, stages a in LDS and writes
-//                         y[h] = sum_u Wd[e_u, h, :] . a[u, :] (+ the shared
-//                         pieces' Sd[h, piece] . a[u, :]).
+//                         waits for the activated experts, issues their down
+//                         rows and the shared pieces' (they stream while
+//                         gate/up runs), reads the Eq. 2 weights w_u, waits
+//                         until every slot is complete, stages a in LDS and
+//                         writes y[h] = sum_u w_u (Wd[e_u, h, :] . a[u, :])
+//                         (+ the shared pieces' Sd[h, piece] . a[u, :]).
 // The shared expert ("Channel Selection for Mixture-of-Experts Decoding Needs
 // No Calibration Data", appendix B: shared experts always run in full) is
 // added with the factor sigmoid(x . sg), or 1 without a gate vector sg.
@@ -78,8 +79,8 @@ struct Args {
   float *w_out;
   int32_t *sync;
   uint64_t *tl;       // E tagged logits
-  uint64_t *tp;       // kRepP copies of 3*k1 tagged words: (expert, weight) per
-                      // activated expert, then one "complete" word each
+  uint64_t *tp;       // kRepP copies of 3*k1 tagged words: the activated
+                      // experts, their weights, then one "complete" word each
   int64_t tp_rep;     // copy stride in words
   uint64_t *cnt;      // k1 + m + 1 counters (tag << 32 | count), kCntStride
                       // apart: blocks done per expert u, then experts complete
@@ -132,10 +133,12 @@ __device__ uint64_t await_lane(const uint64_t *p, int n, uint32_t tag, int32_t *
 
 // gate and up rows of CPW channels per wave (NCH 16-byte chunks per lane of
 // a row, all 2*CPW*NCH loads in flight before any arithmetic), dotted with x;
-// the activations are stored device-coherently.  Wg and Wu point at the
-// first of the I rows of expert (or shared piece) u.
-template <typename WT, typename XT, int NCH, int CPW>
-__device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, float wt, int c0) {
+// the activations, scaled by weight() (called once the dot products are
+// done), are stored device-coherently.  Wg and Wu point at the first of the
+// I rows of expert (or shared piece) u.
+template <typename WT, typename XT, int NCH, int CPW, typename WeightFn>
+__device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, int c0,
+                            WeightFn &&weight) {
   constexpr int NW = Elem<WT>::kPer16B;
   const int lane = lane_id();
   const XT *x = static_cast<const XT *>(a.x);
@@ -189,6 +192,7 @@ __device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, fl
       }
     }
   }
+  const float wt = weight();
   float av[CPW];
 #pragma unroll
   for (int ci = 0; ci < CPW; ++ci) av[ci] = silu(wave_sum_dpp(ag[ci])) * wave_sum_dpp(au[ci]) * wt;
@@ -217,8 +221,8 @@ __device__ void gateup_rows(const Args &a, int u, const WT *Wg, const WT *Wu, fl
 // One output row per wave: y[h] = sum over the activated experts, ascending,
 // of Wd[e_u, h, :] . a[u, :].
 template <typename WT, typename XT, int NCD>
-__device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, uint32_t tag,
-                          int d) {
+__device__ void down_rows(const Args &a, Lds &L, int *s_uniq, float *s_ws, uint32_t *s_new,
+                          uint32_t tag, int d) {
   constexpr int NW = Elem<WT>::kPer16B;
   constexpr int AB = kABytes<WT>;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
@@ -227,9 +231,9 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
   if (tid == 0) coh_st(a.started + d, (uint64_t)tag << 32);
   // the activated experts, ascending, then the shared pieces
   if (wv == 0) {
-    const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, 2 * a.k1, tag, err, a.spin_limit);
-    if ((lane & 1) == 0 && lane < 2 * a.k1)
-      s_uniq[lane >> 1] = min(max(__float_as_int(__uint_as_float((uint32_t)w)), 0), a.E - 1);
+    const uint64_t w = await_lane(a.tp + (d % kRepP) * a.tp_rep, a.k1, tag, err, a.spin_limit);
+    if (lane < a.k1)
+      s_uniq[lane] = min(max(__float_as_int(__uint_as_float((uint32_t)w)), 0), a.E - 1);
     if (lane < a.m) s_uniq[a.k1 + lane] = lane;
   }
   __syncthreads();
@@ -238,6 +242,17 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
   const WT *Sd = static_cast<const WT *>(a.Sd);
   const int nch = a.I / NW;
   const int U = a.k1 + a.m;
+  // the slots' Eq. 2 weights (1 for the shared pieces, whose factor is in
+  // their activations), read by wave 0 once its down rows are issued; the
+  // barriers of the loops below publish them to the block
+  auto await_weights = [&]() {
+    if (wv == 0) {
+      const uint64_t w =
+          await_lane(a.tp + (d % kRepP) * a.tp_rep + a.k1, a.k1, tag, err, a.spin_limit);
+      if (lane < a.k1) s_ws[lane] = __uint_as_float((uint32_t)w);
+      if (lane < a.m) s_ws[a.k1 + lane] = 1.0f;
+    }
+  };
   float acc = 0.0f;
   // Wd[e_s, h, :] . a[s, :] from the staged activations of slot s (one lane's share)
   auto dot_slot = [&](const uint4 (&dqs)[NCD], int s, float v) {
@@ -282,6 +297,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
         }
       }
     }
+    await_weights();
     float part[kPF];
 #pragma unroll
     for (int s = 0; s < kPF; ++s) part[s] = 0.0f;
@@ -326,7 +342,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
     }
 #pragma unroll
     for (int s = 0; s < kPF; ++s)
-      if (s < U) acc = acc + part[s];
+      if (s < U) acc = acc + s_ws[s] * part[s];
   }
   for (int ub = 0; U > kPF && ub < U; ub += kPF) {
     const int nu = min(kPF, U - ub);
@@ -345,6 +361,7 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
       }
     }
     if (ub == 0) {
+      await_weights();
       // every activated expert's and shared piece's activations are stored
       if (wv == 0) await_lane<4>(a.tp + (d % kRepP) * a.tp_rep + 2 * a.k1, U, tag, err, a.spin_limit);
       __syncthreads();
@@ -355,33 +372,9 @@ __device__ void down_rows(const Args &a, Lds &L, int *s_uniq, uint32_t *s_new, u
         static_cast<const char *>(a.abuf) + (int64_t)ub * a.I * AB);
     for (int i = tid; i < nw8; i += kThreads) L.a[i] = coh_ld(src + i);
     __syncthreads();
-    const char *sa = reinterpret_cast<const char *>(L.a);
 #pragma unroll
-    for (int s = 0; s < kPF; ++s) {
-      if (s < nu) {
-#pragma unroll
-        for (int j = 0; j < NCD; ++j) {
-          const int ch = j * kWave + lane;
-          if (ch < nch) {
-            if constexpr (sizeof(WT) == 2) {
-              const uint4 aq =
-                  *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB);
-              acc = dot2_bf16(dq[s][j].x, aq.x, acc);
-              acc = dot2_bf16(dq[s][j].y, aq.y, acc);
-              acc = dot2_bf16(dq[s][j].z, aq.z, acc);
-              acc = dot2_bf16(dq[s][j].w, aq.w, acc);
-            } else {
-              float dv[NW], av[NW];
-              Elem<WT>::widen(dq[s][j], dv);
-              Elem<float>::widen(
-                  *reinterpret_cast<const uint4 *>(sa + ((int64_t)s * a.I + ch * NW) * AB), av);
-#pragma unroll
-              for (int k = 0; k < NW; ++k) acc = __builtin_fmaf(dv[k], av[k], acc);
-            }
-          }
-        }
-      }
-    }
+    for (int s = 0; s < kPF; ++s)
+      if (s < nu) acc = acc + s_ws[ub + s] * dot_slot(dq[s], s, 0.0f);
     __syncthreads();
   }
   acc = wave_sum_dpp(acc);
@@ -392,6 +385,7 @@ template <typename WT, typename XT, int NCHR, int V, int NCH, int CPW, int NCD>
 __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
   __shared__ Lds L;
   __shared__ int s_uniq[kWave];
+  __shared__ float s_ws[kWave];
   __shared__ int s_e, s_last;
   __shared__ float s_wt;
   __shared__ float s_red[kWaves];
@@ -449,35 +443,58 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
   }
   if (b == a.n_r) {
     // ---- route.  The counters (k1 per-expert ones and the count of complete
-    // experts) are set to (tag, 0) first; the staging below waits for every
-    // earlier memory operation of the block, so they are in place before the
-    // route is published.
+    // experts) are set to (tag, 0) first, and each thread waits for its
+    // stores to complete (while the router runs), so they are in place
+    // before any route word is published.
     if (tid <= a.k1 + a.m) coh_st(a.cnt + tid * kCntStride, (uint64_t)tag << 32);
+    __builtin_amdgcn_s_waitcnt(0);
     stage_tagged<kMaxExperts / kSyncThreads>(L.r.sl, a.E, [&](int i) { return a.tl + i; }, tag,
                                              err, a.spin_limit);
-    route_into_lds<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S, a.router_bf16);
-    for (int r = tid; r < a.k1; r += kThreads) {
-      if (a.ids_out) a.ids_out[r] = L.r.s_ids[r];
-      if (a.w_out) a.w_out[r] = L.r.s_w[r];
-    }
-    if (tid < kWave && !a.withhold_route) {
-      const int n = a.k1;
-      __builtin_amdgcn_s_waitcnt(0);
-      // lane r holds slot r; u = its expert's place among the activated ones;
-      // lane L writes slot L % n into copy L / n, then the next copies
-      const int e = lane < n ? L.r.s_ids[lane] : 0x7FFFFFFF;
-      const int r = lane % n;
-      const int er = L.r.s_ids[r];
+    // publish the activated experts: the selected lanes (exactly k1), each
+    // at its place u among them in ascending expert order, in every copy
+    const bool publish = !a.withhold_route;
+    auto publish_experts = [&](bool sel, int idx) {
+      const uint64_t smask = __ballot(sel);
       int u = 0;
-      for (int j = 0; j < n; ++j) u += __builtin_amdgcn_readlane(e, j) < er;
-      const uint64_t we = tagged(tag, __int_as_float(er));
-      const uint64_t ww = tagged(tag, L.r.s_w[r]);
-      const int per = kWave / n;
-      if (lane < per * n) {
-        for (int c = lane / n; c < kRepP; c += per) {
-          coh_st(a.tp + c * a.tp_rep + 2 * u, we);
-          coh_st(a.tp + c * a.tp_rep + 2 * u + 1, ww);
-        }
+      for (uint64_t mm = smask; mm; mm &= mm - 1)
+        u += __builtin_amdgcn_readlane(idx, __builtin_ctzll(mm)) < idx;
+      if (sel && publish) {
+        const uint64_t we = tagged(tag, __int_as_float(idx));
+        for (int c = 0; c < kRepP; ++c) coh_st(a.tp + c * a.tp_rep + u, we);
+      }
+    };
+    bool early = false;
+    if constexpr (V * kWave <= kBlockThreads) {
+      // one wave: the activated set is published as soon as it is known,
+      // before the ranks and the mass that the weights need
+      if (tid < kWave)
+        route_token_wave_ex<V, true>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S,
+                                     a.router_bf16, publish_experts, &early);
+      __syncthreads();
+      if (L.r.S.n > kWave) {
+        const bool renorm = a.k2 < a.E;
+        block_rank(L.r.S, L.r.S.n, renorm ? a.k2 : a.k1, a.k1, renorm, a.router_bf16,
+                   L.r.s_ids, L.r.s_w);
+      }
+    } else {
+      route_token_block_large<V>(L.r.sl, a.E, a.k1, a.k2, L.r.s_ids, L.r.s_w, L.r.S,
+                                 a.router_bf16);
+    }
+    if (tid < kWave) {
+      // lane r < k1 holds rank r; u = its expert's place among the activated
+      const int n = a.k1;
+      const int er = lane < n ? L.r.s_ids[lane] : 0x7FFFFFFF;
+      const float wr = lane < n ? L.r.s_w[lane] : 0.0f;
+      if (!early) publish_experts(lane < n, er);
+      int u = 0;
+      for (int j = 0; j < n; ++j) u += __builtin_amdgcn_readlane(er, j) < er;
+      if (lane < n && publish) {
+        const uint64_t ww = tagged(tag, wr);
+        for (int c = 0; c < kRepP; ++c) coh_st(a.tp + c * a.tp_rep + n + u, ww);
+      }
+      if (lane < n) {
+        if (a.ids_out) a.ids_out[lane] = er;
+        if (a.w_out) a.w_out[lane] = wr;
       }
     }
     return;
@@ -510,24 +527,22 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
       ubase = static_cast<const WT *>(a.Su) + off;
     } else {
       if (wv == 0) {
-        const uint64_t w =
-            await_lane(a.tp + (item % kRepP) * a.tp_rep + 2 * u, 2, tag, err, a.spin_limit);
-        const uint64_t we = __shfl(w, 0), ww = __shfl(w, 1);
-        if (lane == 0) {
-          // a timed-out wait leaves any value here: keep the index in range
-          s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
-          s_wt = __uint_as_float((uint32_t)ww);
-        }
+        const uint64_t we = await_lane(a.tp + (item % kRepP) * a.tp_rep + u, 1, tag, err,
+                                       a.spin_limit);
+        // a timed-out wait leaves any value here: keep the index in range
+        if (lane == 0) s_e = min(max(__float_as_int(__uint_as_float((uint32_t)we)), 0), a.E - 1);
       }
       __syncthreads();
       const int64_t off = (int64_t)s_e * a.I * a.H;
       gbase = static_cast<const WT *>(a.Wg) + off;
       ubase = static_cast<const WT *>(a.Wu) + off;
     }
-    gateup_rows<WT, XT, NCH, CPW>(a, u, gbase, ubase, s_wt, (cb * kWaves + wv) * CPW);
+    // a routed expert's Eq. 2 weight is applied by the down blocks
+    gateup_rows<WT, XT, NCH, CPW>(a, u, gbase, ubase, (cb * kWaves + wv) * CPW,
+                                  [&]() { return shared ? s_wt : 1.0f; });
     // a shared block counts itself only once the route is published: the
     // route block sets the counters before it publishes
-    if (shared && wv == 0) await_lane(a.tp + (item % kRepP) * a.tp_rep, 2, tag, err, a.spin_limit);
+    if (shared && wv == 0) await_lane(a.tp + (item % kRepP) * a.tp_rep, 1, tag, err, a.spin_limit);
     // every activation store of the block is complete, then count the block
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -566,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     }
     return;
   }
-  down_rows<WT, XT, NCD>(a, L, s_uniq, &s_new, tag, b - a.n_r - 1 - a.n_gu);
+  down_rows<WT, XT, NCD>(a, L, s_uniq, s_ws, &s_new, tag, b - a.n_r - 1 - a.n_gu);
 }
 
 }  // namespace b1

@@ -257,21 +257,13 @@ __device__ inline void wave_plan(int e, int n, int E, int32_t *plan) {
   }
 }
 
-// One token (E <= 256) routed by one wave, with the arithmetic above: lane
-// L holds experts q * 64 + L in slot q < V (index order (q, L), so a
-// ballot's lower lanes are the lower indices); exact max; e =
-// exp_nonpos(l - max); S = the pairwise tree (each chunk q by the wave sum,
-// then the tree over the V chunk sums); p = e / S.  The selection is that of
-// route_token_block_large: the top kTauBits bits of the R-th largest key,
-// the candidates at or above them ranked against each other, the mass
-// summed in rank order.  With at most 64 candidates the wave ranks them
-// itself (one per lane) and ids and w (LDS, kMaxExperts entries) receive the
-// route in rank order, with no barrier (the wave's LDS accesses are ordered
-// by waiting for them); with more, the candidates stay in S.KL for
-// block_rank.  Returns the number of candidates (in every lane).
+// The keys of the experts held by one wave (E <= V * 64): lane L holds
+// experts q * 64 + L in slot q < V (index order (q, L), so a ballot's lower
+// lanes are the lower indices).  Exact max; e = exp_nonpos(l - max); S =
+// the pairwise tree (each chunk q by the wave sum, then the tree over the V
+// chunk sums); p = e / S; key = bits of p + 1, 0 for the padding.
 template <int V>
-__device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
-                                BlockRoute &S, bool wbf16 = false) {
+__device__ __forceinline__ void wave_keys(const float *l, int E, uint32_t (&key)[V]) {
 #pragma clang fp contract(off)
   const int lane = lane_id();
   float ex[V];
@@ -295,14 +287,19 @@ __device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *
 #pragma unroll
     for (int q = 0; q + step < V; q += 2 * step) cs[q] = cs[q] + cs[q + step];
   const float sum = cs[0];
-  uint32_t key[V];
 #pragma unroll
   for (int q = 0; q < V; ++q) {
     const int e = q * kWave + lane;
     key[q] = e < E ? __float_as_uint(ex[q] / sum) + 1u : 0u;
   }
-  const bool renorm = k2 < E;
-  const int R = renorm ? k2 : k1;
+}
+
+// The top kTauBits bits of the R-th largest of the wave's keys (one ballot
+// count per bit, from the top; keys are at most bits(1.0f) + 1 < 2^30).
+template <int V>
+__device__ __forceinline__ uint32_t wave_tau(const uint32_t (&key)[V], int R) {
+  // all V compares are issued before the first scalar popcount reads a
+  // result (interleaved, each popcount stalled the wave on its compare)
   auto count_ge = [&](uint32_t c) {
     uint64_t bal[V];
 #pragma unroll
@@ -318,6 +315,18 @@ __device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *
     const uint32_t c = tau | (1u << b);
     if (count_ge(c) >= R) tau = c;
   }
+  return tau;
+}
+
+// The candidates, every key >= tau (at least R of them when tau is the
+// prefix of the R-th largest, every one of the R largest among them),
+// packed with their index (key << 11 | 2047 - index, so that one unsigned
+// compare orders by (p descending, index ascending)) into S.KL in index
+// order; returns their number (in every lane).
+template <int V>
+__device__ __forceinline__ int wave_candidates(const uint32_t (&key)[V], uint32_t tau,
+                                               BlockRoute &S) {
+  const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1ull;
   int nc = 0;
 #pragma unroll
@@ -329,19 +338,77 @@ __device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *
           ((uint64_t)key[q] << 11) | (uint64_t)(2047 - (q * kWave + lane));
     nc += __popcll(cm);
   }
+  return nc;
+}
+
+// Rank of packed key K among the nc candidates in S.KL (LDS reads at one
+// address for the whole wave; measured faster than broadcasting the keys
+// from the lanes with readlane).
+__device__ __forceinline__ int wave_rank(const BlockRoute &S, uint64_t K, int nc) {
+  int r = 0;
+  for (int q = 0; q < nc; ++q) r += S.KL[q] > K ? 1 : 0;
+  return r;
+}
+
+// One token (E <= 256) routed by one wave, with the arithmetic above: the
+// keys (wave_keys), then the candidates at or above the top kTauBits bits of
+// the R-th largest key, ranked against each other, the mass summed in rank
+// order.  With at most 64 candidates the wave ranks them itself (one per
+// lane) and ids and w (LDS, kMaxExperts entries) receive the route in rank
+// order, with no barrier (the wave's LDS accesses are ordered by waiting for
+// them); with more, the candidates stay in S.KL for block_rank.  Returns the
+// number of candidates (in every lane).
+//
+// With EARLY, the activated set is found first, before the ranks that the
+// mass needs: the candidates of the k1-th key are ranked and top_set(sel,
+// index) is called in every lane of the wave, sel true in exactly the k1
+// lanes that hold an activated expert's index; it is not called (and false
+// is stored in *early_done) when those candidates are more than 64.
+template <int V, bool EARLY = false, typename TopSet>
+__device__ int route_token_wave_ex(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
+                                   BlockRoute &S, bool wbf16, TopSet &&top_set,
+                                   bool *early_done) {
+#pragma clang fp contract(off)
+  const int lane = lane_id();
+  uint32_t key[V];
+  wave_keys<V>(l, E, key);
+  const bool renorm = k2 < E;
+  const int R = renorm ? k2 : k1;
+  uint32_t tau = 0u;
+  int nc = -1;
+  if constexpr (EARLY) {
+    const uint32_t tau1 = wave_tau<V>(key, k1);
+    const int nc1 = wave_candidates<V>(key, tau1, S);
+    *early_done = nc1 <= kWave;
+    if (nc1 <= kWave) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t K = lane < nc1 ? S.KL[lane] : 0ull;
+      const int r = lane < nc1 ? wave_rank(S, K, nc1) : kWave;
+      top_set(r < k1, 2047 - (int)(K & 2047u));
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (R == k1) {
+      tau = tau1;
+      nc = nc1;
+    }
+  }
+  if (nc < 0) {
+    tau = wave_tau<V>(key, R);
+    nc = wave_candidates<V>(key, tau, S);
+  }
   if (lane == 0) S.n = nc;
   if (nc > kWave) return nc;  // ranked by the block
-  // lane i ranks candidate i against the others (LDS reads at one address
-  // for the whole wave)
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
+  // lane i ranks candidate i against the others
   if (lane < nc) {
-    const uint64_t Ki = S.KL[lane];
-    int r = 0;
-    for (int q = 0; q < nc; ++q) r += S.KL[q] > Ki ? 1 : 0;
+    const uint64_t K = S.KL[lane];
+    const int r = wave_rank(S, K, nc);
     if (r < R) {
-      w[r] = __uint_as_float((uint32_t)(Ki >> 11) - 1u);
-      ids[r] = 2047 - (int)(Ki & 2047u);
+      w[r] = __uint_as_float((uint32_t)(K >> 11) - 1u);
+      ids[r] = 2047 - (int)(K & 2047u);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -367,6 +434,13 @@ __device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *
     w[q] = wr;
   }
   return nc;
+}
+
+template <int V>
+__device__ int route_token_wave(const float *l, int E, int k1, int k2, int32_t *ids, float *w,
+                                BlockRoute &S, bool wbf16 = false) {
+  return route_token_wave_ex<V, false>(l, E, k1, k2, ids, w, S, wbf16, [](bool, int) {},
+                                       nullptr);
 }
 
 // Route one token into LDS (s_ids, s_w: rank order, kMaxExperts entries
