@@ -10,8 +10,11 @@
 // Workgroups, in block-index order (a block only waits for blocks of smaller
 // index, which the hardware dispatched before it, so the kernel cannot
 // deadlock whatever the occupancy):
-//   R   [0, n_r)          wave e computes logit e and publishes it as a
-//                         tagged word (sync.hpp);
+//   R   [0, n_r)          logit e, published as a tagged word (sync.hpp):
+//                         block e's four waves each take a quarter of the
+//                         router row when a lane holds at least four 16-byte
+//                         chunks of it (the loads spread over E compute
+//                         units), else wave e of the range takes the row;
 //   P   n_r               sets the activated experts' completion counters to
 //                         (tag, 0), stages the E tagged logits and routes the
 //                         token; it publishes the activated experts,
@@ -65,6 +68,10 @@ constexpr int kRepP = kB1RepP;    // copies of the published route
 constexpr int kPF = 8;            // activated experts whose down rows are in flight per wave
 constexpr int kCntStride = kB1CntStride;  // 64-bit words between two counters (128 B)
 constexpr int kLdsBytes = 24576;  // staged channel activations of one D block
+// waves that share one router row (NCHR 16-byte chunks of fp32 per lane):
+// a block per expert spreads the router's loads over E compute units
+template <int NCHR>
+constexpr int kRouterRowSplit = NCHR % kWaves == 0 ? kWaves : 1;
 
 struct Args {
   const void *x;
@@ -395,16 +402,20 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
   const uint32_t tag = call_tag(tag_epoch);
   int32_t *err = a.sync + kErrorWord;
   if (b < a.n_r) {
-    // ---- router: one expert per wave
-    const int e = b * kWaves + wv;
-    if (e >= a.E) return;
+    // ---- router: one expert per block, each wave a quarter of its row (a
+    // row of at least 4 chunks per lane), else one expert per wave
+    constexpr int RS = kRouterRowSplit<NCHR>;
+    constexpr int NCW = NCHR / RS;  // 16-byte (fp32) chunks per lane
+    const int e = RS > 1 ? b : b * kWaves + wv;
+    if (e >= a.E) return;  // uniform across the block when RS > 1
+    const int j0 = RS > 1 ? wv * NCW : 0;
     const XT *x = static_cast<const XT *>(a.x);
-    float wr[NCHR][4];
+    float wr[NCW][4];
     if (a.router_bf16) {
       const uint16_t *wrow = static_cast<const uint16_t *>(a.Wr) + (int64_t)e * a.H;
 #pragma unroll
-      for (int j = 0; j < NCHR; ++j) {
-        const uint2 q = *reinterpret_cast<const uint2 *>(wrow + (j * kWave + lane) * 4);
+      for (int j = 0; j < NCW; ++j) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(wrow + ((j0 + j) * kWave + lane) * 4);
         wr[j][0] = bf16_lo(q.x);
         wr[j][1] = bf16_hi(q.x);
         wr[j][2] = bf16_lo(q.y);
@@ -413,13 +424,13 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
     } else {
       const float *wrow = static_cast<const float *>(a.Wr) + (int64_t)e * a.H;
 #pragma unroll
-      for (int j = 0; j < NCHR; ++j)
-        Elem<float>::widen(ld16_stream(wrow + (j * kWave + lane) * 4), wr[j]);
+      for (int j = 0; j < NCW; ++j)
+        Elem<float>::widen(ld16_stream(wrow + ((j0 + j) * kWave + lane) * 4), wr[j]);
     }
     float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NCHR; ++j) {
-      const int h = (j * kWave + lane) * 4;
+    for (int j = 0; j < NCW; ++j) {
+      const int h = ((j0 + j) * kWave + lane) * 4;
       float xv[4];
       if constexpr (sizeof(XT) == 2) {
         const uint2 q = *reinterpret_cast<const uint2 *>(x + h);
@@ -433,7 +444,15 @@ __global__ __launch_bounds__(kThreads) void layer_kernel(Args a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(wr[j][k], xv[k], acc);
     }
-    float s = wave_sum_dpp(acc) + (a.br ? a.br[e] : 0.0f);
+    float s = wave_sum_dpp(acc);
+    if constexpr (RS > 1) {
+      static_assert(RS == 4 && kWaves == 4, "a row in four quarters");
+      if (lane == 0) s_red[wv] = s;
+      __syncthreads();
+      if (wv != 0) return;
+      s = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    }
+    s = s + (a.br ? a.br[e] : 0.0f);
     if (a.router_bf16) s = round_bf16(s);
     if (lane == 0) {
       coh_st(a.tl + e, tagged(tag, s));
@@ -622,6 +641,7 @@ static void launch_nch(b1::Args &a, int ncd, hipStream_t s) {
   constexpr int NCH = sizeof(WT) == 2 ? NCHR / 2 : NCHR;
   static_assert(NCH >= 1 && NCH <= 8, "gate/up chunks per lane out of range");
   constexpr int CPW = 8 / NCH;
+  a.n_r = b1::kRouterRowSplit<NCHR> > 1 ? a.E : (a.E + b1::kWaves - 1) / b1::kWaves;
   a.n_cb = (a.I + b1::kWaves * CPW - 1) / (b1::kWaves * CPW);
   a.n_gu = (a.k1 + a.m) * a.n_cb;
   const int grid = a.n_r + 1 + a.n_gu + a.n_d;

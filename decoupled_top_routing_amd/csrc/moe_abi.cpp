@@ -113,7 +113,7 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is
 
 // Workspace layout of the prefill path.
 struct PrefillLayout {
-  size_t logits, ids, w, plan, w3, part, abf, zbf, ids_s, plan_s, gs, abf_s, zbf_s, total;
+  size_t logits, ids, w, plan, w3, abf, zbf, ids_s, plan_s, gs, abf_s, zbf_s, total;
 };
 
 PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
@@ -130,8 +130,6 @@ PrefillLayout prefill_layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t
   o += round256(moe::prefill_plan_words((int64_t)n, E) * 4);
   L.w3 = o;
   o += round256((size_t)3 * E * H * 2);
-  L.part = o;
-  o += round256((size_t)3 * T * E * 4);
   L.abf = o;
   o += round256(n * (size_t)I * 2);
   L.zbf = o;
@@ -281,7 +279,6 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, boo
   int32_t *ids = reinterpret_cast<int32_t *>(ws + L.ids);
   float *w = reinterpret_cast<float *>(ws + L.w);
   int32_t *plan = reinterpret_cast<int32_t *>(ws + L.plan);
-  uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + L.w3);
   uint16_t *abf = reinterpret_cast<uint16_t *>(ws + L.abf);
   uint16_t *zbf = reinterpret_cast<uint16_t *>(ws + L.zbf);
   const int64_t n = T * k1;
@@ -290,10 +287,9 @@ int forward_prefill(const uint16_t *x, int64_t T, int32_t H, const void *Wr, boo
     RUN("router_mma", moe::launch_router_mma(x, T, H, static_cast<const uint16_t *>(Wr), E, 1,
                                              nullptr, logits, logits_out, s));
   } else {
+    uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + L.w3);
     RUN("split_router", moe::launch_split_router(static_cast<const float *>(Wr), E, H, w3, s));
-    float *part = reinterpret_cast<float *>(ws + L.part);
-    RUN("router_mma", moe::launch_router_mma(x, T, H, w3, E, 3, part, nullptr, nullptr, s));
-    RUN("router_sum", moe::launch_router_sum(part, T, E, br, logits, logits_out, s));
+    RUN("router_mma", moe::launch_router_mma(x, T, H, w3, E, 3, br, logits, logits_out, s));
   }
   RUN("route", moe::launch_route_plan(logits, T, E, k1, k2, ids, w, ids_out, w_out, nullptr,
                                       nullptr, router_bf16, s));

@@ -114,8 +114,8 @@ __device__ __forceinline__ void mma_slice(const Tile<BM, BN> &T, int buf, int wm
 
 // Full K loop, double buffered in LDS: the next slice's global loads are in
 // flight while the current slice is multiplied.  K is a multiple of BK.
-template <int BM, int BN>
-__device__ void mma_k_loop(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm, int wn,
+template <int BM, int BN, typename LD>
+__device__ void mma_k_loop(Tile<BM, BN> &T, LD &ld, int K, int wm, int wn,
                            f32x16_t (&acc)[BM / 64][BN / 64]) {
   const int nk = K / BK;
   ld.fetch(0);
@@ -140,21 +140,21 @@ __device__ void mma_k_loop(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm, i
 // flight whatever the ring).
 constexpr int kStages = 3;
 
-template <int BM, int BN, int NK>
-__device__ __forceinline__ void mma_k_loop_fixed(Tile<BM, BN> &T, Loader<BM, BN> &ld, int wm,
-                                                 int wn, f32x16_t (&acc)[BM / 64][BN / 64]) {
-  using Stage = typename Loader<BM, BN>::Stage;
+template <int BM, int BN, int NK, typename LD>
+__device__ __forceinline__ void mma_k_loop_fixed(Tile<BM, BN> &T, LD &ld, int wm, int wn,
+                                                 f32x16_t (&acc)[BM / 64][BN / 64]) {
+  using Stage = typename LD::Stage;
   Stage ring[kStages];
 #pragma unroll
   for (int q = 0; q < kStages; ++q)
     if (q < NK) ld.fetch(q * BK, ring[q]);
-  Loader<BM, BN>::store(T, 0, ring[0]);
+  LD::store(T, 0, ring[0]);
   if (kStages < NK) ld.fetch(kStages * BK, ring[0]);
   __syncthreads();
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     mma_slice<BM, BN>(T, kk & 1, wm, wn, acc);
-    if (kk + 1 < NK) Loader<BM, BN>::store(T, (kk + 1) & 1, ring[(kk + 1) % kStages]);
+    if (kk + 1 < NK) LD::store(T, (kk + 1) & 1, ring[(kk + 1) % kStages]);
     if (kk + 1 + kStages < NK) ld.fetch((kk + 1 + kStages) * BK, ring[(kk + 1) % kStages]);
     __syncthreads();
   }
@@ -163,9 +163,9 @@ __device__ __forceinline__ void mma_k_loop_fixed(Tile<BM, BN> &T, Loader<BM, BN>
 // K loop of the expert GEMMs: NK > 0 slices unrolled, NK = 0 the
 // double-buffered loop over any K (a kernel instantiation per NK keeps each
 // one's registers to itself).
-template <int NK, int BM, int BN>
-__device__ __forceinline__ void mma_k_any(Tile<BM, BN> &T, Loader<BM, BN> &ld, int K, int wm,
-                                          int wn, f32x16_t (&acc)[BM / 64][BN / 64]) {
+template <int NK, int BM, int BN, typename LD>
+__device__ __forceinline__ void mma_k_any(Tile<BM, BN> &T, LD &ld, int K, int wm, int wn,
+                                          f32x16_t (&acc)[BM / 64][BN / 64]) {
   if constexpr (NK > 0)
     mma_k_loop_fixed<BM, BN, NK>(T, ld, wm, wn, acc);
   else
@@ -449,79 +449,65 @@ __global__ void split_router_kernel(const float *__restrict__ Wr, int64_t n,
   w3[2 * n + i] = (uint16_t)b3;
 }
 
-// Tile (64 tokens, 64 experts) of one term: part[term, t, e] = x[t] . W_term[e]
-// (fp32 accumulation).  The three terms run as separate workgroups (three
-// times the parallelism) and router_sum_kernel adds them in a fixed order.
-// With one term (a bf16 router weight, the router method on a bf16 model)
-// the tile is the logits themselves, rounded to bf16.
-// Experts beyond E read a valid row and are not stored.
+// Tile (64 tokens, 64 experts) of the router logits, all NT terms in one
+// workgroup: B holds 64 * NT weight rows, placed so that wave (wm, wn)'s
+// NT column blocks are the NT terms of the same 32 experts; accumulator
+// acc[0][q] of a lane is then term q of the same (token, expert), and the
+// terms are added in the fixed order above in registers (plus br).  With
+// one term (a bf16 router weight, the router method on a bf16 model) the
+// tile is the logits themselves, rounded to bf16.  Experts beyond E read a
+// valid row and are not stored.
 constexpr int RM = 64, RN = 64;
 
+template <int NT, int NK>
 __global__ __launch_bounds__(kThreads) void router_mma_kernel(const uint16_t *__restrict__ x,
                                                               int64_t T, int H,
                                                               const uint16_t *__restrict__ w3,
-                                                              int E, int nterms,
-                                                              float *__restrict__ part,
+                                                              int E, const float *__restrict__ br,
                                                               float *__restrict__ logits,
                                                               float *__restrict__ logits2) {
-  __shared__ Tile<RM, RN> Tl;
+  static_assert(NT == 1 || NT == 3, "one bf16 term or the split fp32 weight");
+  constexpr int BN = RN * NT;
+  __shared__ Tile<RM, BN> Tl;
   const int n_nt = (E + RN - 1) / RN;
-  const int64_t n_tiles = ((T + RM - 1) / RM) * n_nt;
-  const int term = (int)(blockIdx.x / n_tiles);
-  const int64_t tile = blockIdx.x - term * n_tiles;
-  const int64_t mt = tile / n_nt;
-  const int nt = (int)(tile - mt * n_nt);
+  const int64_t mt = blockIdx.x / n_nt;
+  const int nt = (int)(blockIdx.x - mt * n_nt);
   const int tid = threadIdx.x, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int64_t t0 = mt * RM;
   const int e0 = nt * RN;
-  f32x16_t acc[1][1];
+  f32x16_t acc[1][NT];
   zero_acc(acc);
-  Loader<RM, RN> ld;
+  Loader<RM, BN> ld;
 #pragma unroll
-  for (int i = 0; i < Loader<RM, RN>::NA; ++i) {
-    const int64_t t = min<int64_t>(t0 + Loader<RM, RN>::row(i), T - 1);
+  for (int i = 0; i < Loader<RM, BN>::NA; ++i) {
+    const int64_t t = min<int64_t>(t0 + Loader<RM, BN>::row(i), T - 1);
     ld.arow[i] = x + t * H;
   }
 #pragma unroll
-  for (int j = 0; j < Loader<RM, RN>::NB; ++j) {
-    const int e = min(e0 + Loader<RM, RN>::row(j), E - 1);
+  for (int j = 0; j < Loader<RM, BN>::NB; ++j) {
+    // B row r: wave column half r / (32 NT), term (r % (32 NT)) / 32
+    const int r = Loader<RM, BN>::row(j);
+    const int term = (r % (32 * NT)) / 32;
+    const int e = min(e0 + (r / (32 * NT)) * 32 + (r & 31), E - 1);
     ld.brow[j] = w3 + (int64_t)term * E * H + (int64_t)e * H;
   }
-  mma_k_loop<RM, RN>(Tl, ld, H, wm, wn, acc);
+  mma_k_any<NK, RM, BN>(Tl, ld, H, wm, wn, acc);
   const int e = e0 + wn * 32 + (lane_id() & 31);
-  if (nterms == 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + acc_row<RM>(wm, 0, r);
-      if (t < T && e < E) {
-        const float l = round_bf16(acc[0][0][r]);
-        logits[t * E + e] = l;
-        if (logits2) logits2[t * E + e] = l;
-      }
-    }
-    return;
-  }
-  float *pt = part + (int64_t)term * T * E;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t t = t0 + acc_row<RM>(wm, 0, r);
-    if (t < T && e < E) pt[t * E + e] = acc[0][0][r];
+    if (t < T && e < E) {
+      float l;
+      if constexpr (NT == 1) {
+        l = round_bf16(acc[0][0][r]);
+      } else {
+        l = (acc[0][0][r] + acc[0][1][r]) + acc[0][2][r];
+        if (br) l = l + br[e];
+      }
+      logits[t * E + e] = l;
+      if (logits2) logits2[t * E + e] = l;
+    }
   }
-}
-
-// logits = (part0 + part1) + part2 (+ br)
-__global__ __launch_bounds__(256) void router_sum_kernel(const float *__restrict__ part,
-                                                         int64_t T, int E,
-                                                         const float *__restrict__ br,
-                                                         float *__restrict__ logits,
-                                                         float *__restrict__ logits2) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = T * E;
-  if (i >= n) return;
-  float v = (part[i] + part[n + i]) + part[2 * n + i];
-  if (br) v = v + br[i % E];
-  logits[i] = v;
-  if (logits2) logits2[i] = v;
 }
 
 }  // namespace pf
@@ -539,19 +525,22 @@ hipError_t launch_split_router(const float *Wr, int E, int H, uint16_t *w3, hipS
 }
 
 hipError_t launch_router_mma(const uint16_t *x, int64_t T, int H, const uint16_t *w3, int E,
-                             int nterms, float *part, float *logits, float *logits2,
+                             int nterms, const float *br, float *logits, float *logits2,
                              hipStream_t s) {
   const int64_t tiles = ((T + pf::RM - 1) / pf::RM) * ((E + pf::RN - 1) / pf::RN);
-  pf::router_mma_kernel<<<dim3((unsigned)(nterms * tiles)), dim3(pf::kThreads), 0, s>>>(
-      x, T, H, w3, E, nterms, part, logits, logits2);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_sum(const float *part, int64_t T, int E, const float *br, float *logits,
-                             float *logits2, hipStream_t s) {
-  const int64_t n = T * E;
-  pf::router_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(part, T, E, br,
-                                                                                logits, logits2);
+#define RT(NT, NK) pf::router_mma_kernel<NT, NK><<<dim3((unsigned)tiles), dim3(pf::kThreads), 0, s>>>( \
+    x, T, H, w3, E, br, logits, logits2)
+  const int nk = pf::unrolled_nk(H);
+  if (nterms == 1) {
+    if (nk == 2048 / pf::BK) RT(1, 2048 / pf::BK);
+    else if (nk == 4096 / pf::BK) RT(1, 4096 / pf::BK);
+    else RT(1, 0);
+  } else {
+    if (nk == 2048 / pf::BK) RT(3, 2048 / pf::BK);
+    else if (nk == 4096 / pf::BK) RT(3, 4096 / pf::BK);
+    else RT(3, 0);
+  }
+#undef RT
   return hipGetLastError();
 }
 
