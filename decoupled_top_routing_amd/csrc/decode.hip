@@ -275,10 +275,17 @@ __device__ __forceinline__ void gateup_tokens(const XT *__restrict__ x, int H, i
   }
 }
 
+// The workspace epoch (source of the call tags of the router + route launch
+// before this one, every block of which has ended) is advanced by block 0.
+__device__ __forceinline__ void advance_epoch(int32_t *epoch) {
+  if (epoch && blockIdx.x == 0 && threadIdx.x == 0) coh_st(epoch, coh_ld(epoch) + 1);
+}
+
 template <typename WT, typename XT, int NCH, int CPW>
 __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, int H,
                                                      GuGroup<WT> g0, GuGroup<WT> g1,
-                                                     unsigned n0) {
+                                                     unsigned n0, int32_t *epoch) {
+  advance_epoch(epoch);
   constexpr int NW = Elem<WT>::kPer16B;
   const bool second = blockIdx.x >= n0;
   const GuGroup<WT> G = second ? g1 : g0;
@@ -321,7 +328,8 @@ __global__ __launch_bounds__(256) void gateup_kernel(const XT *__restrict__ x, i
 template <typename WT, typename XT>
 __global__ __launch_bounds__(256) void gateup_any_kernel(const XT *__restrict__ x, int H,
                                                          GuGroup<WT> g0, GuGroup<WT> g1,
-                                                         unsigned n0) {
+                                                         unsigned n0, int32_t *epoch) {
+  advance_epoch(epoch);
   constexpr int NW = Elem<WT>::kPer16B;
   const bool second = blockIdx.x >= n0;
   const GuGroup<WT> G = second ? g1 : g0;
@@ -378,7 +386,7 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          const int32_t *plan, int E, int64_t n_assign, int k1, const float *w,
                          float *abuf, hipStream_t s, const WT *Sg, const WT *Su, int Is,
                          const int32_t *plan_s, const float *gs, float *abuf_s,
-                         const int32_t *ids) {
+                         const int32_t *ids, int32_t *epoch) {
   const int64_t umax = n_assign < E ? n_assign : E;
   const int nch = (H * (int)sizeof(WT)) % (16 * kWave) == 0 ? (int)(H * sizeof(WT) / 16 / kWave) : 0;
   if (ids && (n_assign > kIdsMax || !gateup_takes_ids<WT, XT>(H))) return hipErrorInvalidValue;
@@ -390,7 +398,7 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
     const unsigned n_r = (unsigned)(umax * ((I + kGuWaves * CPW - 1) / (kGuWaves * CPW)));
     const unsigned n_sh = Sg ? (unsigned)((Is + kGuWaves * CPW - 1) / (kGuWaves * CPW)) : 0u;
     gateup_kernel<WT, XT, NCH, CPW><<<dim3(n_r + n_sh), dim3(256), 0, s>>>(x, H, g0, gr,
-                                                                           Sg ? n_sh : n_r);
+                                                                           Sg ? n_sh : n_r, epoch);
   };
   using std::integral_constant;
   switch (nch) {
@@ -402,7 +410,7 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
       const unsigned n_r = (unsigned)(umax * ((I + kGuWaves - 1) / kGuWaves));
       const unsigned n_sh = Sg ? (unsigned)((Is + kGuWaves - 1) / kGuWaves) : 0u;
       gateup_any_kernel<WT, XT><<<dim3(n_r + n_sh), dim3(256), 0, s>>>(x, H, g0, gr,
-                                                                        Sg ? n_sh : n_r);
+                                                                        Sg ? n_sh : n_r, epoch);
     }
   }
   return hipGetLastError();
@@ -780,7 +788,8 @@ hipError_t launch_shared_prep(const XT *x, int64_t T, int H, const float *sgw, i
                                             const int32_t *, int, int64_t, int,           \
                                             const float *, float *, hipStream_t,          \
                                             const WT *, const WT *, int, const int32_t *, \
-                                            const float *, float *, const int32_t *);     \
+                                            const float *, float *, const int32_t *,      \
+                                            int32_t *);                                   \
   template hipError_t launch_down<WT>(const WT *, int, int, const int32_t *, int, int64_t,  \
                                       const float *, float *, hipStream_t, const WT *, int, \
                                       const int32_t *, const float *, float *,              \

@@ -138,23 +138,23 @@ hipError_t noalloc_scratch(void **ptr, size_t zero_prefix, hipStream_t s);
 
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
-// words of the sync region of the small-batch router + route launch: the
-// arrival count (zero between calls) and the sense of its barrier
-constexpr int kRouteArriveWord = 1056;
-constexpr int kRouteSenseWord = 1088;
-
 // Small batches: router and route in one launch (fp32 router weight,
-// router_route_supported(H), 2 <= T <= kRouteBatchMax).  sync is the
-// workspace's sync region; a route block's wait for the logits gives up
-// after spin_limit re-reads and sets the error word (withhold: every wait
-// gives up, a test hook).
+// router_route_supported(H), 2 <= T <= kRouteBatchMax).  The router blocks
+// publish the logits as tagged words in tl, a fixed region of
+// kRouteBatchTlBytes after the one-token layer's (token t's E logits at
+// word t * kMaxExperts); the call's tag comes from the epoch word of sync,
+// which the gate/up launch that follows advances (launch_gateup's epoch
+// argument).  A route block's wait for its token's logits gives up after
+// spin_limit re-reads and sets the error word (withhold: every wait gives
+// up, a test hook).
 constexpr int kRouteBatchMax = 64;
+constexpr size_t kRouteBatchTlBytes = (size_t)kRouteBatchMax * kMaxExperts * 8;
 bool router_route_batch_supported(int64_t T, int H);
 template <typename XT>
 hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const float *Wr,
                                      const float *br, int E, int k1, int k2, float *logits,
                                      float *logits2, int32_t *ids, float *w, int32_t *ids2,
-                                     float *w2, int32_t *sync, uint32_t spin_limit,
+                                     float *w2, int32_t *sync, uint64_t *tl, uint32_t spin_limit,
                                      bool withhold, hipStream_t s);
 // Batches of at most kIdsMax assignments (T*k1) need no plan: the gate/up
 // and down blocks find their work from the ids.
@@ -176,7 +176,7 @@ hipError_t launch_gateup(const XT *x, int H, const WT *Wg, const WT *Wu, int I,
                          float *abuf, hipStream_t s, const WT *Sg = nullptr,
                          const WT *Su = nullptr, int Is = 0, const int32_t *plan_s = nullptr,
                          const float *gs = nullptr, float *abuf_s = nullptr,
-                         const int32_t *ids = nullptr);
+                         const int32_t *ids = nullptr, int32_t *epoch = nullptr);
 
 template <typename WT>
 hipError_t launch_down(const WT *Wd, int H, int I, const int32_t *plan, int E, int64_t n_assign,

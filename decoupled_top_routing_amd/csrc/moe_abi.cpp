@@ -76,7 +76,8 @@ struct Layout {
 
 // Every workspace starts with the sync region, then the one-token kernel's
 // fixed tagged region; the per-call buffers follow.
-constexpr size_t kFixedBytes = moe::kSyncRegionBytes + moe::kB1RegionBytes;
+constexpr size_t kFixedBytes =
+    moe::kSyncRegionBytes + moe::kB1RegionBytes + moe::kRouteBatchTlBytes;
 
 Layout layout(int64_t T, int32_t H, int32_t E, int32_t I, int32_t k1, int32_t Is) {
   Layout L;
@@ -368,10 +369,11 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   const bool by_ids = T >= 2 && n_assign <= moe::kIdsMax && moe::gateup_takes_ids<WT, XT>(H) &&
                       moe::down_takes_ids<WT>(I, Sg ? sh.Is : 0);
   if (batch_route) {
-    RUN("router_route", moe::launch_router_route_batch<XT>(x, T, H, Wr32, br, E, k1, k2, logits,
-                                                           logits_out, ids, w, ids_out, w_out,
-                                                           sync, run.spin_limit,
-                                                           run.withhold_route, s));
+    RUN("router_route",
+        moe::launch_router_route_batch<XT>(
+            x, T, H, Wr32, br, E, k1, k2, logits, logits_out, ids, w, ids_out, w_out, sync,
+            reinterpret_cast<uint64_t *>(ws + moe::kSyncRegionBytes + moe::kB1RegionBytes),
+            run.spin_limit, run.withhold_route, s));
     if (!by_ids) RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));
   } else if (by_ids) {
     if (router_bf16) {
@@ -418,7 +420,8 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   }
   RUN("gateup", (moe::launch_gateup<WT, XT>(x, H, Wg, Wu, I, plan, E, n_assign, k1, w, abuf, s,
                                             Sg, Su, sh.Is, plan_s, gs, abuf_s,
-                                            by_ids ? ids : nullptr)));
+                                            by_ids ? ids : nullptr,
+                                            batch_route ? sync + moe::kEpochWord : nullptr)));
   if (ck.dn) {
     uint2 *kept_list = nullptr;
     float *part = nullptr;

@@ -150,14 +150,16 @@ __device__ __forceinline__ void load4(const XT *p, float (&v)[4]) {
 constexpr int kRowsTok = 16;
 
 // Block `bid` of the router: experts 4*(bid % n_eb) .. +3, tokens of group
-// bid / n_eb.  COH stores the logits device-coherently (read back by other
-// workgroups of the same kernel).
-template <typename XT, int NCHR, bool COH>
+// bid / n_eb.  With tl, each logit is also published as a tagged word
+// tl[t * kMaxExperts + e] (read by other workgroups of the same kernel).
+template <typename XT, int NCHR>
 __device__ __forceinline__ void router_rows(const XT *__restrict__ x, int64_t T, int H,
                                             const float *__restrict__ Wr,
                                             const float *__restrict__ br, int E,
                                             float *__restrict__ logits,
-                                            float *__restrict__ logits2, int bid) {
+                                            float *__restrict__ logits2, int bid,
+                                            uint64_t *__restrict__ tl = nullptr,
+                                            uint32_t tag = 0u) {
   const int n_eb = (E + 3) / 4;
   const int tg = bid / n_eb;
   const int e = (bid - tg * n_eb) * 4 + (threadIdx.x >> 6);
@@ -188,10 +190,8 @@ __device__ __forceinline__ void router_rows(const XT *__restrict__ x, int64_t T,
       const float sum = wave_sum_dpp(acc[q]) + b;
       const int64_t t = t0 + q;
       if (lane == 0 && t < t_end) {
-        if (COH)
-          coh_st(logits + t * E + e, sum);
-        else
-          logits[t * E + e] = sum;
+        if (tl) coh_st(tl + t * kMaxExperts + e, tagged(tag, sum));
+        logits[t * E + e] = sum;
         if (logits2) logits2[t * E + e] = sum;
       }
     }
@@ -204,71 +204,47 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__
                                                           const float *__restrict__ br, int E,
                                                           float *__restrict__ logits,
                                                           float *__restrict__ logits2) {
-  router_rows<XT, NCHR, false>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x);
+  router_rows<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x);
 }
 
-// Small batches (2 <= T <= kRouteBatchMax): router and route in one launch.
-// The first n_router blocks compute the logits (as router_rows_kernel) and
-// store them device-coherently; every block then reads the sense word and
-// takes an arrival ticket.  The last arrival resets the count and flips the
-// sense; the T arrivals before it route one token each once they see the
-// sense flipped, the last arrival routes the last token.  (A sense-reversing
-// barrier: the count is zero between calls without a second ticket.)  At
-// most T - 1 blocks wait and the grid's other blocks never do, so the
-// waiters cannot keep the others from running; the wait is bounded and sets
-// the error word when it gives up.  `withhold` (a test hook) keeps the
-// sense from flipping, so every waiter gives up; the route is still valid
-// for any logits it reads (ids in range), the outputs are unspecified.
+// Small batches (2 <= T <= kRouteBatchMax): router and route in one launch,
+// with the one-token layer's hand-over (sync.hpp) instead of a barrier: the
+// first n_router blocks compute the logits and publish each as a tagged word
+// of the call (tl); the last T blocks of the grid each stage one token's E
+// tagged words (one round trip, then re-reads of the missing ones) and route
+// it.  Only those T <= 64 blocks ever wait and every other block runs to its
+// end, so the waiters cannot keep the blocks they wait for from running; the
+// wait is bounded and sets the error word when it gives up.  No counter or word of
+// the sync region changes, so nothing has to return to zero; the epoch that
+// makes the tag is advanced by the gate/up launch that follows.  `withhold`
+// (a test hook) makes the route blocks wait for a tag no word carries, so
+// every wait gives up; they route the finite values they read (this call's
+// or an earlier call's logits, or zero), so the ids stay in range; the
+// outputs are unspecified.
 template <typename XT, int NCHR, int V>
 __global__ __launch_bounds__(256) void router_route_batch_kernel(
     const XT *__restrict__ x, int T, int H, const float *__restrict__ Wr,
     const float *__restrict__ br, int E, int k1, int k2, float *__restrict__ logits,
     float *__restrict__ logits2, int32_t *__restrict__ ids, float *__restrict__ w,
     int32_t *__restrict__ ids2, float *__restrict__ w2, int32_t *__restrict__ sync,
-    uint32_t spin_limit, bool withhold, int n_router) {
+    uint64_t *__restrict__ tl, uint32_t spin_limit, bool withhold, int n_router) {
   __shared__ float sl[kMaxExperts];
   __shared__ int32_t s_ids[kMaxExperts];
   __shared__ float s_w[kMaxExperts];
   __shared__ BlockRoute S;
-  __shared__ int s_tok;
-  const int tid = threadIdx.x;
+  const uint32_t tag = call_tag((uint32_t)coh_ld(sync + kEpochWord));
   if ((int)blockIdx.x < n_router)
-    router_rows<XT, NCHR, true>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x);
-  int32_t *arrive = sync + kRouteArriveWord;
-  int32_t *sense = sync + kRouteSenseWord;
-  const int G = (int)gridDim.x;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    // the sense is read (waited for) before the arrival: it can only flip
-    // at the last arrival
-    const int s0 = coh_ld(sense);
-    __builtin_amdgcn_s_waitcnt(0);
-    const int old = atomic_inc(arrive);
-    const int tok = old - (G - T);
-    if (old == G - 1) {
-      coh_st(arrive, 0);
-      if (!withhold) coh_st(sense, s0 ^ 1);
-    } else if (tok >= 0) {
-      uint32_t n = 0;
-      while (coh_ld(sense) == s0) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++n > spin_limit) {
-          coh_st(sync + kErrorWord, 1);
-          break;
-        }
-      }
-    }
-    s_tok = tok;
-  }
-  __syncthreads();
-  const int t = s_tok;
+    router_rows<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+  const int t = (int)blockIdx.x - ((int)gridDim.x - T);
   if (t < 0) return;
-  for (int i = tid; i < E; i += kBlockThreads) sl[i] = coh_ld(logits + (int64_t)t * E + i);
-  __syncthreads();
+  // 2: not a call tag (their low bit is set) and not the zero fill
+  const uint32_t want = withhold ? 2u : tag;
+  const uint64_t *trow = tl + (int64_t)t * kMaxExperts;
+  stage_tagged<kMaxExperts / kSyncThreads>(sl, E, [&](int i) { return trow + i; }, want,
+                                           sync + kErrorWord, spin_limit);
   route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S);
   const int64_t o = (int64_t)t * k1;
-  for (int r = tid; r < k1; r += kBlockThreads) {
+  for (int r = (int)threadIdx.x; r < k1; r += kBlockThreads) {
     ids[o + r] = s_ids[r];
     w[o + r] = s_w[r];
     if (ids2) ids2[o + r] = s_ids[r];
@@ -283,13 +259,13 @@ bool router_route_batch_supported(int64_t T, int H) {
 template <typename XT, int NCHR>
 static void launch_rrb_v(const XT *x, int T, int H, const float *Wr, const float *br, int E,
                          int k1, int k2, float *logits, float *logits2, int32_t *ids, float *w,
-                         int32_t *ids2, float *w2, int32_t *sync, uint32_t spin_limit,
-                         bool withhold, hipStream_t s) {
+                         int32_t *ids2, float *w2, int32_t *sync, uint64_t *tl,
+                         uint32_t spin_limit, bool withhold, hipStream_t s) {
   const int n_router = ((E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok);
   const dim3 grid((unsigned)max(n_router, T)), block(256);
 #define RRB(V)                                                                               \
   router_route_batch_kernel<XT, NCHR, V><<<grid, block, 0, s>>>(                            \
-      x, T, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, \
+      x, T, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, \
       n_router)
   if (E <= 64) RRB(1);
   else if (E <= 128) RRB(2);
@@ -303,16 +279,16 @@ template <typename XT>
 hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const float *Wr,
                                      const float *br, int E, int k1, int k2, float *logits,
                                      float *logits2, int32_t *ids, float *w, int32_t *ids2,
-                                     float *w2, int32_t *sync, uint32_t spin_limit,
+                                     float *w2, int32_t *sync, uint64_t *tl, uint32_t spin_limit,
                                      bool withhold, hipStream_t s) {
   if (!router_route_batch_supported(T, H)) return hipErrorInvalidValue;
   const int t = (int)T;
   switch (H / (4 * kWave)) {
-    case 1: launch_rrb_v<XT, 1>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, s); break;
-    case 2: launch_rrb_v<XT, 2>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, s); break;
-    case 4: launch_rrb_v<XT, 4>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, s); break;
-    case 8: launch_rrb_v<XT, 8>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, s); break;
-    default: launch_rrb_v<XT, 16>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, spin_limit, withhold, s); break;
+    case 1: launch_rrb_v<XT, 1>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
+    case 2: launch_rrb_v<XT, 2>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
+    case 4: launch_rrb_v<XT, 4>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
+    case 8: launch_rrb_v<XT, 8>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
+    default: launch_rrb_v<XT, 16>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
   }
   return hipGetLastError();
 }
@@ -320,13 +296,13 @@ hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const float 
 template hipError_t launch_router_route_batch<float>(const float *, int64_t, int, const float *,
                                                      const float *, int, int, int, float *,
                                                      float *, int32_t *, float *, int32_t *,
-                                                     float *, int32_t *, uint32_t, bool,
-                                                     hipStream_t);
+                                                     float *, int32_t *, uint64_t *, uint32_t,
+                                                     bool, hipStream_t);
 template hipError_t launch_router_route_batch<bf16_t>(const bf16_t *, int64_t, int,
                                                       const float *, const float *, int, int, int,
                                                       float *, float *, int32_t *, float *,
-                                                      int32_t *, float *, int32_t *, uint32_t,
-                                                      bool, hipStream_t);
+                                                      int32_t *, float *, int32_t *, uint64_t *,
+                                                      uint32_t, bool, hipStream_t);
 
 // bf16 router (the router method on a bf16 model): logits[t, e] =
 // bf16(sum_h x[t, h] Wr[e, h]) with bf16 x and Wr, the products exact and the

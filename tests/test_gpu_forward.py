@@ -59,12 +59,15 @@ def test_a3b_decode_each_path(a3b, k1, k2, flags, T):
 
 def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
     """One workspace serves calls of different shapes and paths in a row; the
-    synchronisation words must be back at zero after every call."""
+    synchronisation words must be back at zero after every call, and each of
+    these calls (every one hands values over as tagged words) advances the
+    epoch that makes the call tags by exactly one."""
     L, Lh = a3b
     tL, tLh = tiny
     g, tg = to_dev(L), to_dev(tL)
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
     ref = {}
+    epoch = 0
     for rep in range(3):
         for name, (lay, T, k1, k2, fl) in {
                 "a": (g, 1, 4, 16, 0), "b": (tg, 8, 2, 4, 0), "c": (g, 8, 8, 8, 0),
@@ -73,11 +76,10 @@ def test_a3b_workspace_reuse_across_shapes(a3b, tiny):
                             br=lay["br"], flags=fl, workspace=ws)
             torch.cuda.synchronize()
             words = ws[:16384].view(torch.int32).cpu().clone()
-            # word 0 is the workspace's epoch and word 1088 the sense of the
-            # small-batch route barrier (it flips every call, 0 or 1); every
-            # counter and the error word must be back at zero
-            assert int(words[1088]) in (0, 1), name
-            words[1088] = 0
+            # word 0 is the workspace's epoch; every counter and the error
+            # word must be back at zero
+            assert int(words[0]) == epoch + 1, name
+            epoch = int(words[0])
             assert int(words[1:].abs().sum()) == 0, f"sync words left set ({name})"
             yb = y.float().cpu()
             if rep == 0:
