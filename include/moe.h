@@ -156,12 +156,14 @@ size_t moe_forward_workspace(int64_t T, int32_t H, int32_t E, int32_t I,
  *          256-byte aligned, ZERO-FILLED before its first use.  It carries
  *          state from call to call, so one zero fill at allocation lasts for
  *          its lifetime, whatever the shapes of later calls: an epoch word
- *          that advances on every one-token call (the source of the tags of
- *          its hand-over words, which sit at fixed places of a region of
- *          their own, so a stale word cannot carry the current tag until 2^31
- *          calls have passed), the error word read by moe_workspace_status,
- *          and counters that return to zero after every call.  Calls that
- *          run concurrently need separate workspaces.
+ *          that advances on every call that hands values over as tagged
+ *          words (one-token calls and the 2-64-token router + route; the
+ *          epoch is the source of the tags, and the words sit at fixed
+ *          places of regions of their own, so a stale word cannot carry the
+ *          current tag until 2^31 calls have passed), the error word read by
+ *          moe_workspace_status, and counters that return to zero after
+ *          every call.  Calls that run concurrently need separate
+ *          workspaces.
  *   flags: 0 or one MOE_FLAG_FORCE_* value, optionally with
  *          MOE_FLAG_ROUTER_BF16.
  *
