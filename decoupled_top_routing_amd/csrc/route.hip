@@ -198,6 +198,65 @@ __device__ __forceinline__ void router_rows(const XT *__restrict__ x, int64_t T,
   }
 }
 
+// Block `bid` of the small-batch router when a lane holds at least four
+// 16-byte chunks of a router row: expert bid % E, tokens of group bid / E;
+// each wave takes a quarter of the row, the four partial dot products of
+// each token are added in a fixed order, and the logits are published as
+// tagged words tl[t * kMaxExperts + e].  A block per expert spreads the
+// router's loads over E compute units (four experts per block left most of
+// them idle).
+template <typename XT, int NCHR>
+__device__ __forceinline__ void router_rows_split(const XT *__restrict__ x, int64_t T, int H,
+                                                  const float *__restrict__ Wr,
+                                                  const float *__restrict__ br, int E,
+                                                  float *__restrict__ logits,
+                                                  float *__restrict__ logits2, int bid,
+                                                  uint64_t *__restrict__ tl, uint32_t tag) {
+  constexpr int NCW = NCHR / 4;
+  static_assert(NCHR % 4 == 0, "a row in four quarters");
+  __shared__ float part[4][kRowsTok];
+  const int tg = bid / E;
+  const int e = bid - tg * E;
+  const int lane = lane_id(), wq = threadIdx.x >> 6;
+  const int j0 = wq * NCW;
+  const float *wrow = Wr + (int64_t)e * H;
+  float wv[NCW][4];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j)
+    Elem<float>::widen(ld16_stream(wrow + ((j0 + j) * kWave + lane) * 4), wv[j]);
+  const int64_t t_begin = (int64_t)tg * kRowsTok;
+  const int64_t t_end = min<int64_t>(T, t_begin + kRowsTok);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 4) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t t = min<int64_t>(t0 + q, t_end - 1);
+      const XT *xr = x + t * H;
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) {
+        float xv[4];
+        load4(xr + ((j0 + j) * kWave + lane) * 4, xv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[q] = __builtin_fmaf(wv[j][k], xv[k], acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sum = wave_sum_dpp(acc[q]);
+      if (lane == 0 && t0 + q < t_end) part[wq][t0 + q - t_begin] = sum;
+    }
+  }
+  __syncthreads();
+  const int i = (int)threadIdx.x;
+  if (i < t_end - t_begin) {
+    const int64_t t = t_begin + i;
+    const float sum = ((part[0][i] + part[1][i]) + (part[2][i] + part[3][i])) + (br ? br[e] : 0.0f);
+    coh_st(tl + t * kMaxExperts + e, tagged(tag, sum));
+    logits[t * E + e] = sum;
+    if (logits2) logits2[t * E + e] = sum;
+  }
+}
+
 template <typename XT, int NCHR>
 __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__ x, int64_t T,
                                                           int H, const float *__restrict__ Wr,
@@ -233,8 +292,12 @@ __global__ __launch_bounds__(256) void router_route_batch_kernel(
   __shared__ float s_w[kMaxExperts];
   __shared__ BlockRoute S;
   const uint32_t tag = call_tag((uint32_t)coh_ld(sync + kEpochWord));
-  if ((int)blockIdx.x < n_router)
-    router_rows<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+  if ((int)blockIdx.x < n_router) {
+    if constexpr (NCHR % 4 == 0)
+      router_rows_split<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+    else
+      router_rows<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+  }
   const int t = (int)blockIdx.x - ((int)gridDim.x - T);
   if (t < 0) return;
   // 2: not a call tag (their low bit is set) and not the zero fill
@@ -261,7 +324,8 @@ static void launch_rrb_v(const XT *x, int T, int H, const float *Wr, const float
                          int k1, int k2, float *logits, float *logits2, int32_t *ids, float *w,
                          int32_t *ids2, float *w2, int32_t *sync, uint64_t *tl,
                          uint32_t spin_limit, bool withhold, hipStream_t s) {
-  const int n_router = ((E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok);
+  const int n_router =
+      (NCHR % 4 == 0 ? E : (E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok);
   const dim3 grid((unsigned)max(n_router, T)), block(256);
 #define RRB(V)                                                                               \
   router_route_batch_kernel<XT, NCHR, V><<<grid, block, 0, s>>>(                            \
