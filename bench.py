@@ -11,8 +11,10 @@ replayed; HIP events on the capture stream time the replays.  The other cells
 at 1 and 64 tokens) are reported in "cells".
 
 The timed region of the headline is exactly --steps layer calls (whole ring
-replays, then one replay of a graph of the remaining calls); the spread is
-reported from at least 10 ring replays timed one by one.
+replays, then one replay of a graph of the remaining calls), queued behind a
+short GPU spin so that it holds the calls back to back and not the host's
+submission of the first graph; the spread is reported from at least 10 ring
+replays timed one by one the same way.
 
 The roofline object is for the headline's dominant kernel: every launch of
 one call is bracketed with HIP events (moe_profile_launch) in an eager pass,
@@ -37,6 +39,9 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# a GPU spin (torch.cuda._sleep, clock cycles) queued ahead of each timed
+# region: a few hundred microseconds, far longer than a graph's submission
+GPU_SPIN_CYCLES = 1_000_000
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
 RING = 32
 PATH_FLAGS = {"auto": 0, "g": 2, "p": 4}
@@ -247,6 +252,10 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        # the GPU spins before the start event while the host queues the
+        # replays behind it, so the timed region holds the layer calls back
+        # to back and not the host's submission of the first graph
+        torch.cuda._sleep(GPU_SPIN_CYCLES)
         start.record(stream)
         for _ in range(n_full):
             g.replay()
@@ -259,6 +268,7 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
         for _ in range(max(min_replays, min(20, n_full), 1)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(GPU_SPIN_CYCLES)
             e0.record(stream)
             g.replay()
             e1.record(stream)
