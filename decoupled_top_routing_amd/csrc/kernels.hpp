@@ -138,8 +138,10 @@ hipError_t noalloc_scratch(void **ptr, size_t zero_prefix, hipStream_t s);
 
 // word of the sync region used as the route kernel's ticket
 constexpr int kRouteTicketWord = 1024;
-// Small batches: router and route in one launch (fp32 router weight,
-// router_route_supported(H), 2 <= T <= kRouteBatchMax).  The router blocks
+// Small batches: router and route in one launch (router_route_supported(H),
+// 2 <= T <= kRouteBatchMax; a bf16 router weight (wr_bf16, bf16 x) when H is
+// a multiple of 1024: logits rounded to bf16, no bias, weights rounded to
+// bf16).  The router blocks
 // publish the logits as tagged words in tl, a fixed region of
 // kRouteBatchTlBytes after the one-token layer's (token t's E logits at
 // word t * kMaxExperts); the call's tag comes from the epoch word of sync,
@@ -149,9 +151,9 @@ constexpr int kRouteTicketWord = 1024;
 // up, a test hook).
 constexpr int kRouteBatchMax = 64;
 constexpr size_t kRouteBatchTlBytes = (size_t)kRouteBatchMax * kMaxExperts * 8;
-bool router_route_batch_supported(int64_t T, int H);
+bool router_route_batch_supported(int64_t T, int H, bool wr_bf16);
 template <typename XT>
-hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const float *Wr,
+hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const void *Wr, bool wr_bf16,
                                      const float *br, int E, int k1, int k2, float *logits,
                                      float *logits2, int32_t *ids, float *w, int32_t *ids2,
                                      float *w2, int32_t *sync, uint64_t *tl, uint32_t spin_limit,

@@ -349,8 +349,8 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
            *Sd = static_cast<const WT *>(sh.Sd);
   // the launches with a bounded wait inside: the one-token kernel and the
   // small-batch router + route
-  const bool batch_route = path != Path::Single && !router_bf16 &&
-                           moe::router_route_batch_supported(T, H);
+  const bool batch_route = path != Path::Single && (!router_bf16 || sizeof(XT) == 2) &&
+                           moe::router_route_batch_supported(T, H, router_bf16);
   if ((path == Path::Single || batch_route) && g_withhold_calls > 0) {
     --g_withhold_calls;
     run.withhold_route = true;
@@ -371,7 +371,7 @@ int forward_typed(const XT *x, int64_t T, int32_t H, const void *Wr, bool router
   if (batch_route) {
     RUN("router_route",
         moe::launch_router_route_batch<XT>(
-            x, T, H, Wr32, br, E, k1, k2, logits, logits_out, ids, w, ids_out, w_out, sync,
+            x, T, H, Wr, router_bf16, br, E, k1, k2, logits, logits_out, ids, w, ids_out, w_out, sync,
             reinterpret_cast<uint64_t *>(ws + moe::kSyncRegionBytes + moe::kB1RegionBytes),
             run.spin_limit, run.withhold_route, s));
     if (!by_ids) RUN("plan", moe::launch_plan(ids, n_assign, E, plan, s));

@@ -205,9 +205,11 @@ __device__ __forceinline__ void router_rows(const XT *__restrict__ x, int64_t T,
 // tagged words tl[t * kMaxExperts + e].  A block per expert spreads the
 // router's loads over E compute units (four experts per block left most of
 // them idle).
-template <typename XT, int NCHR>
+// With WB the router weight is bf16 (the router method on a bf16 model): the
+// products are exact in fp32, the sum is rounded once to bf16, no bias.
+template <typename XT, int NCHR, bool WB>
 __device__ __forceinline__ void router_rows_split(const XT *__restrict__ x, int64_t T, int H,
-                                                  const float *__restrict__ Wr,
+                                                  const void *__restrict__ Wr,
                                                   const float *__restrict__ br, int E,
                                                   float *__restrict__ logits,
                                                   float *__restrict__ logits2, int bid,
@@ -219,11 +221,23 @@ __device__ __forceinline__ void router_rows_split(const XT *__restrict__ x, int6
   const int e = bid - tg * E;
   const int lane = lane_id(), wq = threadIdx.x >> 6;
   const int j0 = wq * NCW;
-  const float *wrow = Wr + (int64_t)e * H;
   float wv[NCW][4];
+  if constexpr (WB) {
+    const uint16_t *wrow = static_cast<const uint16_t *>(Wr) + (int64_t)e * H;
 #pragma unroll
-  for (int j = 0; j < NCW; ++j)
-    Elem<float>::widen(ld16_stream(wrow + ((j0 + j) * kWave + lane) * 4), wv[j]);
+    for (int j = 0; j < NCW; ++j) {
+      const uint2 q = *reinterpret_cast<const uint2 *>(wrow + ((j0 + j) * kWave + lane) * 4);
+      wv[j][0] = bf16_lo(q.x);
+      wv[j][1] = bf16_hi(q.x);
+      wv[j][2] = bf16_lo(q.y);
+      wv[j][3] = bf16_hi(q.y);
+    }
+  } else {
+    const float *wrow = static_cast<const float *>(Wr) + (int64_t)e * H;
+#pragma unroll
+    for (int j = 0; j < NCW; ++j)
+      Elem<float>::widen(ld16_stream(wrow + ((j0 + j) * kWave + lane) * 4), wv[j]);
+  }
   const int64_t t_begin = (int64_t)tg * kRowsTok;
   const int64_t t_end = min<int64_t>(T, t_begin + kRowsTok);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 4) {
@@ -250,7 +264,11 @@ __device__ __forceinline__ void router_rows_split(const XT *__restrict__ x, int6
   const int i = (int)threadIdx.x;
   if (i < t_end - t_begin) {
     const int64_t t = t_begin + i;
-    const float sum = ((part[0][i] + part[1][i]) + (part[2][i] + part[3][i])) + (br ? br[e] : 0.0f);
+    float sum = (part[0][i] + part[1][i]) + (part[2][i] + part[3][i]);
+    if constexpr (WB)
+      sum = round_bf16(sum);
+    else
+      sum = sum + (br ? br[e] : 0.0f);
     coh_st(tl + t * kMaxExperts + e, tagged(tag, sum));
     logits[t * E + e] = sum;
     if (logits2) logits2[t * E + e] = sum;
@@ -280,9 +298,9 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const XT *__restrict__
 // every wait gives up; they route the finite values they read (this call's
 // or an earlier call's logits, or zero), so the ids stay in range; the
 // outputs are unspecified.
-template <typename XT, int NCHR, int V>
+template <typename XT, int NCHR, int V, bool WB>
 __global__ __launch_bounds__(256) void router_route_batch_kernel(
-    const XT *__restrict__ x, int T, int H, const float *__restrict__ Wr,
+    const XT *__restrict__ x, int T, int H, const void *__restrict__ Wr,
     const float *__restrict__ br, int E, int k1, int k2, float *__restrict__ logits,
     float *__restrict__ logits2, int32_t *__restrict__ ids, float *__restrict__ w,
     int32_t *__restrict__ ids2, float *__restrict__ w2, int32_t *__restrict__ sync,
@@ -294,9 +312,10 @@ __global__ __launch_bounds__(256) void router_route_batch_kernel(
   const uint32_t tag = call_tag((uint32_t)coh_ld(sync + kEpochWord));
   if ((int)blockIdx.x < n_router) {
     if constexpr (NCHR % 4 == 0)
-      router_rows_split<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
-    else
-      router_rows<XT, NCHR>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+      router_rows_split<XT, NCHR, WB>(x, T, H, Wr, br, E, logits, logits2, blockIdx.x, tl, tag);
+    else if constexpr (!WB)
+      router_rows<XT, NCHR>(x, T, H, static_cast<const float *>(Wr), br, E, logits, logits2,
+                            blockIdx.x, tl, tag);
   }
   const int t = (int)blockIdx.x - ((int)gridDim.x - T);
   if (t < 0) return;
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(256) void router_route_batch_kernel(
   const uint64_t *trow = tl + (int64_t)t * kMaxExperts;
   stage_tagged<kMaxExperts / kSyncThreads>(sl, E, [&](int i) { return trow + i; }, want,
                                            sync + kErrorWord, spin_limit);
-  route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S);
+  route_into_lds<V>(sl, E, k1, k2, s_ids, s_w, S, WB);
   const int64_t o = (int64_t)t * k1;
   for (int r = (int)threadIdx.x; r < k1; r += kBlockThreads) {
     ids[o + r] = s_ids[r];
@@ -315,12 +334,14 @@ __global__ __launch_bounds__(256) void router_route_batch_kernel(
   }
 }
 
-bool router_route_batch_supported(int64_t T, int H) {
-  return T >= 2 && T <= kRouteBatchMax && router_route_supported(H);
+bool router_route_batch_supported(int64_t T, int H, bool wr_bf16) {
+  // the bf16 router weight only with a row in four quarters (H % 1024 == 0)
+  return T >= 2 && T <= kRouteBatchMax && router_route_supported(H) &&
+         (!wr_bf16 || (H / (4 * kWave)) % 4 == 0);
 }
 
-template <typename XT, int NCHR>
-static void launch_rrb_v(const XT *x, int T, int H, const float *Wr, const float *br, int E,
+template <typename XT, int NCHR, bool WB>
+static void launch_rrb_v(const XT *x, int T, int H, const void *Wr, const float *br, int E,
                          int k1, int k2, float *logits, float *logits2, int32_t *ids, float *w,
                          int32_t *ids2, float *w2, int32_t *sync, uint64_t *tl,
                          uint32_t spin_limit, bool withhold, hipStream_t s) {
@@ -328,7 +349,7 @@ static void launch_rrb_v(const XT *x, int T, int H, const float *Wr, const float
       (NCHR % 4 == 0 ? E : (E + 3) / 4) * ((T + kRowsTok - 1) / kRowsTok);
   const dim3 grid((unsigned)max(n_router, T)), block(256);
 #define RRB(V)                                                                               \
-  router_route_batch_kernel<XT, NCHR, V><<<grid, block, 0, s>>>(                            \
+  router_route_batch_kernel<XT, NCHR, V, WB><<<grid, block, 0, s>>>(                        \
       x, T, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, \
       n_router)
   if (E <= 64) RRB(1);
@@ -340,31 +361,46 @@ static void launch_rrb_v(const XT *x, int T, int H, const float *Wr, const float
 }
 
 template <typename XT>
-hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const float *Wr,
+hipError_t launch_router_route_batch(const XT *x, int64_t T, int H, const void *Wr, bool wr_bf16,
                                      const float *br, int E, int k1, int k2, float *logits,
                                      float *logits2, int32_t *ids, float *w, int32_t *ids2,
                                      float *w2, int32_t *sync, uint64_t *tl, uint32_t spin_limit,
                                      bool withhold, hipStream_t s) {
-  if (!router_route_batch_supported(T, H)) return hipErrorInvalidValue;
+  if (!router_route_batch_supported(T, H, wr_bf16)) return hipErrorInvalidValue;
   const int t = (int)T;
-  switch (H / (4 * kWave)) {
-    case 1: launch_rrb_v<XT, 1>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
-    case 2: launch_rrb_v<XT, 2>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
-    case 4: launch_rrb_v<XT, 4>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
-    case 8: launch_rrb_v<XT, 8>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
-    default: launch_rrb_v<XT, 16>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, ids2, w2, sync, tl, spin_limit, withhold, s); break;
+#define GO(N, WB) launch_rrb_v<XT, N, WB>(x, t, H, Wr, br, E, k1, k2, logits, logits2, ids, w, \
+                                          ids2, w2, sync, tl, spin_limit, withhold, s)
+  if (wr_bf16) {
+    if constexpr (sizeof(XT) == 2) {
+      switch (H / (4 * kWave)) {
+        case 4: GO(4, true); break;
+        case 8: GO(8, true); break;
+        default: GO(16, true); break;
+      }
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    switch (H / (4 * kWave)) {
+      case 1: GO(1, false); break;
+      case 2: GO(2, false); break;
+      case 4: GO(4, false); break;
+      case 8: GO(8, false); break;
+      default: GO(16, false); break;
+    }
   }
+#undef GO
   return hipGetLastError();
 }
 
-template hipError_t launch_router_route_batch<float>(const float *, int64_t, int, const float *,
-                                                     const float *, int, int, int, float *,
+template hipError_t launch_router_route_batch<float>(const float *, int64_t, int, const void *,
+                                                     bool, const float *, int, int, int, float *,
                                                      float *, int32_t *, float *, int32_t *,
                                                      float *, int32_t *, uint64_t *, uint32_t,
                                                      bool, hipStream_t);
 template hipError_t launch_router_route_batch<bf16_t>(const bf16_t *, int64_t, int,
-                                                      const float *, const float *, int, int, int,
-                                                      float *, float *, int32_t *, float *,
+                                                      const void *, bool, const float *, int, int,
+                                                      int, float *, float *, int32_t *, float *,
                                                       int32_t *, float *, int32_t *, uint64_t *,
                                                       uint32_t, bool, hipStream_t);
 

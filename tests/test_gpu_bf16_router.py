@@ -156,6 +156,8 @@ SMALL = replace(synth.TINY, dtype="bf16", rms_norm_x=True, router_var_times_H=4.
     (40, 3, 7, 264, 72, 5, 0),
     (300, 6, 12, 512, 64, 1, 0),      # E > 256: the one-launch kernel's wave route
     (300, 6, 12, 512, 64, 8, 0),      # E > 256 on the grouped path
+    (300, 6, 12, 1024, 64, 8, 0),     # the small-batch router + route launch, E > 256
+    (64, 4, 16, 2048, 128, 40, 0),    # the same launch with three groups of tokens
     (1, 1, 1, 256, 64, 3, 0),         # one expert: p = 1, w = 1
     (33, 5, 9, 1024, 192, 257, moe.FORCE_PREFILL),  # E not a multiple of the router tile
 ])
