@@ -11,10 +11,10 @@ replayed; HIP events on the capture stream time the replays.  The other cells
 at 1 and 64 tokens) are reported in "cells".
 
 The timed region of the headline is exactly --steps layer calls (whole ring
-replays, then one replay of a graph of the remaining calls), queued behind a
-short GPU spin so that it holds the calls back to back and not the host's
-submission of the first graph; the spread is reported from at least 10 ring
-replays timed one by one the same way.
+replays, then the remaining calls launched one by one), queued behind a short
+GPU spin so that it holds the calls back to back and not the host's
+submission of them; the spread is reported from at least 10 ring replays
+timed one by one the same way.
 
 The roofline object is for the headline's dominant kernel: every launch of
 one call is bracketed with HIP events (moe_profile_launch) in an eager pass,
@@ -40,8 +40,8 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # a GPU spin (torch.cuda._sleep, clock cycles) queued ahead of each timed
-# region: a few hundred microseconds, far longer than a graph's submission
-GPU_SPIN_CYCLES = 1_000_000
+# region: about 2 ms, longer than the host takes to queue a ring of calls
+GPU_SPIN_CYCLES = 5_000_000
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
 RING = 32
 PATH_FLAGS = {"auto": 0, "g": 2, "p": 4}
@@ -241,15 +241,8 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             one_pass()
-        g_rem = None
-        if rem:
-            g_rem = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_rem, stream=stream):
-                one_pass(rem)
         for _ in range(max(1, -(-warmup // L))):
             g.replay()
-        if g_rem is not None:
-            g_rem.replay()  # a graph's first launch carries its upload
         torch.cuda.synchronize()
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
@@ -263,8 +256,11 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
         start.record(stream)
         for _ in range(n_full):
             g.replay()
-        if g_rem is not None:
-            g_rem.replay()
+        # the remaining calls are launched one by one: each replay of a graph
+        # carries about 10 us of its own on the device (measured: 24.2 us per
+        # call with one call per graph, 14.7 with 32), which a region of fewer
+        # calls than the ring would otherwise hold once
+        one_pass(rem)
         stop.record(stream)
         stop.synchronize()
         total_ms = start.elapsed_time(stop)
@@ -281,7 +277,7 @@ def time_cell(moe, torch, cfg, layers, T, k1, k2, path, steps, warmup, min_repla
         torch.cuda.synchronize()
         for a, b in zip(y_eager, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
-    del g, g_rem
+    del g
     us = total_ms * 1e3 / steps
     U = unique_experts(ids_list)
     bias = layers[0]["br"] is not None
@@ -592,11 +588,12 @@ def main():
                                hlayers[0]["Wr"].element_size(), shared_bytes(hcfg, hlayers[0]))
     eager_us = dom_us
     if len(launches) == 1:
-        # the call is this one launch: the timed region (graph-replayed ring,
-        # HIP events on the launch stream) gives its average duration without
-        # the dispatch cost of an eager launch inside the event pair
+        # the call is this one launch: the timed region (calls queued back to
+        # back behind a GPU spin, HIP events on the launch stream) gives its
+        # average duration without the dispatch cost of an eager launch
+        # inside an event pair
         dom_us = head["us_per_layer"]
-        timing = "timed region: graph-replayed ring, one launch per layer call"
+        timing = "timed region: layer calls queued back to back, one launch per call"
     else:
         timing = "HIP events around the launch in an eager pass over the ring"
     print(f"# launches {launches}; dominant {dom['kernel']}: {dom_us:.2f} us per launch "
@@ -656,8 +653,8 @@ def main():
         "data": "synthetic: seeded Gaussian layers generated on the device",
         "config": {
             "workload": f"decode batch {hT}, H={hcfg.H} E={hcfg.E} I={hcfg.I} bf16 experts, "
-                        f"k1:k2={hk1}:{hk2}, cold ring of {len(hlayers)} layers replayed from "
-                        f"one HIP graph",
+                        f"k1:k2={hk1}:{hk2}, cold ring of {len(hlayers)} layers (whole-ring "
+                        f"HIP graph replays, the rest of the steps launched one by one)",
             "global_batch": hT,
         },
         "roofline": roofline,
