@@ -362,10 +362,10 @@ int moe_workspace_status(void *workspace, void *stream);
 /*
  * moe_debug_withhold_route -- test hook for the status above.  The next
  * `calls` calls on the calling thread that run a launch with such a wait
- * (the one-token kernel, or the router + route launch of 2..64 tokens with
- * an fp32 router weight) withhold their hand-over: the one-token kernel does
- * not publish its route, and the router + route launch never releases the
- * blocks that wait for every token's logits.  Every such wait gives up
+ * (the one-token kernel, or the router + route launch of 2..64 tokens) withhold
+ * their hand-over: the one-token kernel does not publish its route, and the
+ * route blocks of the router + route launch wait for a tag that no logit
+ * carries.  Every such wait gives up
  * after `spin_limit` re-reads (>= 1); the kernels still run to the end,
  * reading only in-range expert rows, and the outputs are unspecified.
  * calls = 0 disarms.
