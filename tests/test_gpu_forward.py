@@ -134,6 +134,7 @@ def test_zero_tokens(a3b):
     (16, 2, 4, 256, 64, 65),   # the smallest batch past it
     (512, 10, 20, 512, 136, 40),  # many unique experts, down rows of 34 chunks
     (33, 5, 9, 1024, 64, 13),  # router rows of 4 chunks per lane
+    (1024, 3, 9, 1024, 64, 20),  # a router block per expert for the most experts, two token groups
 ])
 def test_edge_shapes_fp32(E, k1, k2, H, I, T):
     from dataclasses import replace
@@ -149,6 +150,8 @@ def test_edge_shapes_fp32(E, k1, k2, H, I, T):
     (33, 5, 9, 512, 72, "f32"),       # E and I not multiples of the tiles
     (1024, 4, 16, 512, 64, "bf16"),   # bf16, the most experts
     (128, 8, 8, 2048, 768, "bf16"),   # a full-size expert at 8:8
+    (1024, 4, 16, 1024, 64, "f32"),   # a router block per expert (rows of 4 chunks per lane), the most experts
+    (256, 6, 24, 4096, 128, "bf16"),  # router rows of 16 chunks per lane, a quarter per wave
 ])
 def test_one_launch_limits(E, k1, k2, H, I, dtype):
     """One token on the single-launch kernel at the edges of the shapes it takes."""
